@@ -1,0 +1,158 @@
+"""Pins of the oracle's summaries and block scores to facts fixed by the pages
+and by mathematics (not to the oracle's own formulas).
+
+Summaries: OasisKV signal-papers reader text, paragraph on ranking
+non-resident blocks; paperpeel v2 text, §4.1 (two summary rows per block,
+1/16 of the KV cache at B = 16).  Scores: paperpeel v2 text, §3.1 equation
+s_b(alpha), alpha = 1.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")))
+
+
+def _f(x):
+    return -np.inf if x == "-inf" else float(x)
+
+
+def test_summaries_hand_example():
+    ex = GOLD["summaries"]
+    keys = np.array(ex["keys"], dtype=np.float64)[None, None]  # [1][1][6][3]
+    s = oracle.build_summaries(keys, ex["block_size"], seq_len=[ex["seq_len"]])
+    np.testing.assert_array_equal(s[0, 0, :2, 0], np.array(ex["expected_min"]))
+    np.testing.assert_array_equal(s[0, 0, :2, 1], np.array(ex["expected_max"]))
+    # the partial block (token 4) is not summarised
+    np.testing.assert_array_equal(s[0, 0, 2], 0.0)
+
+
+@pytest.mark.parametrize("B", [1, 2, 4, 16])
+def test_summaries_bound_and_attained(B):
+    rng = np.random.default_rng(7 + B)
+    R, H, nb, D = 2, 3, 9, 8
+    keys = rng.standard_normal((R, H, nb * B, D))
+    s = oracle.build_summaries(keys, B)
+    blocks = keys.reshape(R, H, nb, B, D)
+    mn, mx = s[:, :, :, 0], s[:, :, :, 1]
+    # every key lies inside [min, max] coordinate-wise ...
+    assert np.all(blocks >= mn[:, :, :, None, :])
+    assert np.all(blocks <= mx[:, :, :, None, :])
+    # ... and both bounds are attained by some key of the block (tightness)
+    assert np.all(np.any(blocks == mn[:, :, :, None, :], axis=3))
+    assert np.all(np.any(blocks == mx[:, :, :, None, :], axis=3))
+    if B == 1:
+        np.testing.assert_array_equal(mn, blocks[:, :, :, 0])
+        np.testing.assert_array_equal(mx, blocks[:, :, :, 0])
+
+
+def test_summaries_size_is_one_sixteenth_of_kv():
+    # v2 §4.1: two summary rows per 16-token block = 1/16 of the K+V cache.
+    R, H, B, nb, D = 1, 2, 16, 4, 8
+    keys = np.zeros((R, H, nb * B, D))
+    s = oracle.build_summaries(keys, B)
+    kv_elems = 2 * keys.size
+    assert s.size * 16 == kv_elems
+
+
+def test_summaries_range_and_seq_len():
+    rng = np.random.default_rng(3)
+    R, H, B, nb, D = 2, 1, 4, 6, 4
+    keys = rng.standard_normal((R, H, nb * B, D))
+    full = oracle.build_summaries(keys, B)
+    seq = np.array([9, 24], dtype=np.int32)  # request 0: 2 full blocks + 1 token
+    part = oracle.build_summaries(keys, B, seq_len=seq, blk_begin=1, blk_end=5)
+    # request 0: only block 1 is both in range and full
+    np.testing.assert_array_equal(part[0, :, 1], full[0, :, 1])
+    assert np.all(part[0, :, [0, 2, 3, 4, 5]] == 0)
+    np.testing.assert_array_equal(part[1, :, 1:5], full[1, :, 1:5])
+    assert np.all(part[1, :, [0, 5]] == 0)
+
+
+def test_scores_hand_example():
+    ex = GOLD["scores"]
+    keys = np.array(GOLD["summaries"]["keys"], dtype=np.float64)[None, None]
+    s = oracle.build_summaries(keys, 2, seq_len=[5])
+    q = np.array(ex["q"], dtype=np.float64)[None, None]  # [1][1][2][3]
+    sc = oracle.block_scores(q, s, n_blk=[ex["n_blk"]])
+    np.testing.assert_array_equal(sc[0, 0, 0], np.array([_f(x) for x in ex["expected"]]))
+
+
+def _center_radius_form(q, summ, G):
+    """The paper's written form: sum_h (q_h . c_b + |q_h| . r_b), c = (max+min)/2,
+    r = (max-min)/2 (paperpeel v2 §3.1, alpha = 1)."""
+    R, nq, Hq, D = q.shape
+    H = Hq // G
+    c = 0.5 * (summ[:, :, :, 1] + summ[:, :, :, 0])
+    rad = 0.5 * (summ[:, :, :, 1] - summ[:, :, :, 0])
+    qg = q.reshape(R, nq, H, G, D)
+    return (np.einsum("rjhgd,rhbd->rjhb", qg, c) + np.einsum("rjhgd,rhbd->rjhb", np.abs(qg), rad))
+
+
+@pytest.mark.parametrize("G,B", [(1, 4), (2, 16), (4, 8), (16, 2)])
+def test_scores_equal_center_radius_form(G, B):
+    rng = np.random.default_rng(100 + G * B)
+    R, H, nb, D, nq = 2, 2, 7, 16, 2
+    keys = rng.standard_normal((R, H, nb * B, D))
+    q = rng.standard_normal((R, nq, H * G, D))
+    summ = oracle.build_summaries(keys, B)
+    got = oracle.block_scores(q, summ)
+    ref = _center_radius_form(q, summ, G)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("G,B", [(1, 16), (4, 16), (16, 4)])
+def test_scores_upper_bound_brute_force(G, B):
+    rng = np.random.default_rng(200 + G)
+    R, H, nb, D, nq = 2, 2, 11, 8, 2
+    keys = rng.standard_normal((R, H, nb * B, D))
+    q = rng.standard_normal((R, nq, H * G, D))
+    summ = oracle.build_summaries(keys, B)
+    sc = oracle.block_scores(q, summ)
+    qsum = q.reshape(R, nq, H, G, D).sum(axis=3)           # sum of the group's queries
+    dots = np.einsum("rjhd,rhld->rjhl", qsum, keys)         # every key
+    best = dots.reshape(R, nq, H, nb, B).max(axis=-1)
+    assert np.all(sc >= best - 1e-12 * (1 + np.abs(best)))
+
+
+def test_scores_tight_for_single_key_blocks_and_constant_blocks():
+    rng = np.random.default_rng(5)
+    R, H, G, D, nq = 1, 2, 4, 8, 2
+    q = rng.standard_normal((R, nq, H * G, D))
+    qsum = q.reshape(R, nq, H, G, D).sum(axis=3)
+    # B = 1: the bound is the exact dot product
+    keys = rng.standard_normal((R, H, 5, D))
+    sc = oracle.block_scores(q, oracle.build_summaries(keys, 1))
+    np.testing.assert_allclose(sc, np.einsum("rjhd,rhld->rjhl", qsum, keys), rtol=1e-12, atol=1e-12)
+    # every key of a block identical: the bound is that key's dot product
+    k1 = rng.standard_normal((R, H, 3, D))
+    keys = np.repeat(k1, 4, axis=2)
+    sc = oracle.block_scores(q, oracle.build_summaries(keys, 4))
+    np.testing.assert_allclose(sc, np.einsum("rjhd,rhld->rjhl", qsum, k1), rtol=1e-12, atol=1e-12)
+
+
+def test_scores_group_mapping_is_contiguous():
+    # query head h reads KV head h // G: zeroing KV head 1's group zeroes only its scores.
+    rng = np.random.default_rng(9)
+    R, H, G, D, B, nb = 1, 2, 3, 4, 2, 3
+    keys = rng.standard_normal((R, H, nb * B, D))
+    q = rng.standard_normal((R, 1, H * G, D))
+    q[:, :, G:2 * G] = 0.0
+    sc = oracle.block_scores(q, oracle.build_summaries(keys, B))
+    assert np.all(sc[0, 0, 1] == 0.0)
+    assert np.all(sc[0, 0, 0] != 0.0)
+
+
+def test_scores_past_n_blk_are_minus_inf():
+    rng = np.random.default_rng(11)
+    keys = rng.standard_normal((2, 1, 40, 4))
+    summ = oracle.build_summaries(keys, 4)
+    q = rng.standard_normal((2, 2, 1, 4))
+    sc = oracle.block_scores(q, summ, n_blk=[3, 10])
+    assert np.all(np.isneginf(sc[0, :, :, 3:]))
+    assert np.all(np.isfinite(sc[0, :, :, :3]))
+    assert np.all(np.isfinite(sc[1]))

@@ -1,0 +1,246 @@
+/*
+ * oasis.h -- C ABI of liboasis.so, the MI355X (gfx950) hot path of lookahead
+ * sparse-KV decode attention.
+ *
+ * Per layer and decode step the path (1) keeps Quest-style min/max key
+ * summaries per logical block, (2) scans them with the stacked normal and
+ * draft queries to bound every block's attention score per KV head, (3) takes
+ * a per-head top-K, (4) diffs the prediction against the resident set into a
+ * capped least-recently-selected transfer plan, (5) copies planned tiles from
+ * pinned host memory into HBM, and (6) runs paged GQA decode attention of both
+ * stacked queries over the resident tiles in one call.
+ *
+ * Sources (web pages about "OasisKV: Scaling In-Decode KV Cache Beyond HBM
+ * with Lookahead Sparse Prefetching"):
+ *   [v2]     the paperpeel.com text of the paper (arXiv v2, numbered sections)
+ *   [reader] the signal-papers reader text (earlier version, no headings;
+ *            cited by paragraph topic)
+ *   [metal]  the metallab.ai summary page (figure captions)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
+ *    The library allocates nothing, keeps no state between calls and never
+ *    synchronises: every call validates its host-side arguments, enqueues its
+ *    kernels on `stream` and returns.  Calls are thread-safe.
+ *  - All arrays are dense and row-major in the layouts given below.
+ *  - dtype (oasis_shape.dtype) applies to q, keys, values, summaries and out.
+ *    Scores, lse and all accumulation are fp32.
+ *  - Device-side preconditions are NOT checked and violating them is undefined
+ *    behaviour: tile / block ids within range, distinct ids in one table row,
+ *    finite inputs, buffers at least as large as stated.
+ *  - Notation: R batch, n_q stacked query rows (1 or 2; row 0 = normal query
+ *    of step t, row 1 = draft query of step t+1), Hq query heads, H KV heads,
+ *    G = Hq / H (query head h reads KV head h / G), D head dim, B block size,
+ *    K top-K = resident slots per KV head, unit = one (request r, KV head g)
+ *    pair with index u = r*H + g.
+ *  - Tiles: a K tile holds the B keys of one block of one KV head, token-major
+ *    [B][D].  A V tile holds the same block's values DIM-major [D][B] (value
+ *    of token i, dim d at d*B + i).  Tile ids are 64-bit element offsets / (B*D).
+ */
+#ifndef OASIS_H
+#define OASIS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OASIS_OK 0
+#define OASIS_EINVAL (-1)       /* null required pointer, bad size or index argument */
+#define OASIS_EUNSUPPORTED (-2) /* dtype / head_dim / block size / group size not built */
+#define OASIS_EWORKSPACE (-3)   /* workspace missing or smaller than the query says */
+#define OASIS_EHIP (-4)         /* a kernel launch failed (hipGetLastError) */
+
+typedef enum { OASIS_F32 = 0, OASIS_BF16 = 1 } oasis_dtype;
+
+typedef struct oasis_shape {
+    int32_t batch;      /* R >= 1 */
+    int32_t n_q;        /* stacked query rows, 1 or 2 */
+    int32_t n_q_heads;  /* Hq >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads; /* H >= 1 */
+    int32_t head_dim;   /* D: 64 or 128 */
+    int32_t block_size; /* B: power of two, 1..64 (16 in every measured workload) */
+    int32_t dtype;      /* oasis_dtype */
+} oasis_shape;
+
+/* Human-readable text of a status code.  Never NULL; static storage. */
+const char* oasis_status_string(int status);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int oasis_version(void);
+
+/*
+ * Build per-block key summaries.
+ * Defines: for every unit u and full block b (b < floor(L_r / B)) in
+ * [blk_begin, blk_end), summaries[u][b][0][d] = min over the block's B keys of
+ * key[d] and summaries[u][b][1][d] = max (coordinate-wise; exact, no rounding).
+ * [reader] paragraph on ranking non-resident blocks (coordinate-wise min and
+ * max of the keys of each logical block); [metal] Fig. 7 caption (per-block
+ * min/max pooling); [v2] §4.1 (two summary rows per 16-token block, 1/16 of
+ * the KV cache).
+ *   s          shape; uses batch, n_kv_heads, head_dim, block_size, dtype
+ *   keys       [R][H][n_blk_max][B][D] (dtype): the full key store of the layer
+ *   n_blk_max  blocks per unit in `keys` and `summaries`
+ *   seq_len    [R] int32 context lengths, or NULL = n_blk_max*B for every
+ *              request; each must be in [0, n_blk_max*B]
+ *   blk_begin, blk_end  block range to (re)build; clipped to [0, full blocks);
+ *              an incremental update after a block completes passes [b, b+1)
+ *   summaries  [R][H][n_blk_max][2][D] (dtype) output; entries outside the
+ *              range and the trailing partial block are not written
+ * Errors: EINVAL (null pointer, sizes <= 0, blk_begin > blk_end),
+ *         EUNSUPPORTED (dtype, D, B), EHIP.
+ */
+int oasis_build_summaries(const oasis_shape* s, const void* keys, int32_t n_blk_max,
+                          const int32_t* seq_len, int32_t blk_begin, int32_t blk_end,
+                          void* summaries, hipStream_t stream);
+
+/*
+ * Workspace bytes oasis_score_topk needs (0 if none).  Returns 0 also for an
+ * invalid shape; oasis_score_topk then reports the error.
+ */
+size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k);
+
+/*
+ * Score every full block with every stacked query row and keep the top-K per
+ * (request, row, KV head).
+ * Score: s[r][j][g][b] = sum over the query heads h of group g and over d of
+ *   max(q[r][j][h][d] * max_b[d], q[r][j][h][d] * min_b[d])
+ * which is [v2] §3.1 equation s_b(alpha) at alpha = 1 (c = (max+min)/2,
+ * r = (max-min)/2), i.e. an upper bound of sum_h q_h . k for every key k of
+ * the block.  Computed in fp32 as P_g . max_b + N_g . min_b with
+ * P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0), so the scan cost does not
+ * grow with the group size.  No 1/sqrt(D) factor.
+ * Top-K: the min(K, n_r) full blocks with the largest fp32 score, ranked by
+ * (score descending, block ascending); positions past n_r hold block -1 and
+ * score -inf.  [v2] §3.3.1 (prediction ranks the compressed keys into the
+ * per-head set); [reader] paragraph on ranking all logical blocks
+ * independently for every KV head.
+ *   q           [R][n_q][Hq][D] (dtype)
+ *   summaries   [R][H][n_blk_max][2][D] (dtype)
+ *   n_blk       [R] int32 full-block counts (0..n_blk_max), or NULL = n_blk_max
+ *   top_k       K, 1..1024
+ *   topk_idx    [R][n_q][H][K] int32 output
+ *   topk_score  [R][n_q][H][K] fp32 output, or NULL
+ *   scores      [R][n_q][H][n_blk_max] fp32 output of every block score
+ *               (-inf past n_r), or NULL (then the workspace holds them)
+ *   workspace   device buffer of at least oasis_score_topk_workspace() bytes
+ * Limits: n_blk_max <= 32768.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int oasis_score_topk(const oasis_shape* s, const void* q, const void* summaries,
+                     int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
+                     int32_t* topk_idx, float* topk_score, float* scores,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Capped least-recently-selected selection and transfer plan, per unit:
+ *   P       = the ranked blocks of top-K row `pred_row` (entries >= 0)
+ *   seeding = some slot is empty (block -1) on entry; then no cap applies
+ *   hit     : a slot whose block is in P gets stamp `step`
+ *   missing = P's blocks that are not resident, in P's rank order
+ *   victims = slots whose block is not in P (empty slots included), ordered
+ *             by (stamp ascending, slot ascending)
+ *   n       = min(|missing|, |victims|, seeding ? unbounded : cap)
+ *   pair i < n: plan_src[i] = missing[i], plan_dst[i] = victims[i],
+ *             plan_evicted[i] = the slot's old block; the slot then holds
+ *             missing[i] with stamp `step`.  Entries i >= n are -1.
+ * Every other slot keeps its block and stamp.  [reader] paragraphs on the
+ * capped eviction policy and on partial transfer at admission; [v2] §3.3.2
+ * (at most f_HBM*K admissions per head per step once the first working set
+ * is seeded; exactly K resident blocks per head).
+ *   topk_idx         [R][n_q][H][K] int32 (distinct entries per row; -1 pad)
+ *   slot_block_in    [R][H][K] int32 resident block per slot (-1 = empty)
+ *   slot_stamp_in    [R][H][K] int32 last step the slot's block was selected
+ *   slot_block_out, slot_stamp_out  [R][H][K] outputs; may alias the inputs
+ *   plan_count       [R][H] int32 output
+ *   plan_src, plan_dst [R][H][K] int32 outputs
+ *   plan_evicted     [R][H][K] int32 output or NULL
+ * Integer-only and deterministic; no atomics.
+ * Errors: EINVAL (pred_row outside [0, n_q), cap < 0, K outside 1..1024,
+ *         null pointers), EHIP.
+ */
+int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t pred_row,
+                      int32_t top_k, const int32_t* topk_idx, const int32_t* slot_block_in,
+                      const int32_t* slot_stamp_in, int32_t* slot_block_out,
+                      int32_t* slot_stamp_out, int32_t step, int32_t cap,
+                      int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
+                      int32_t* plan_evicted, hipStream_t stream);
+
+/*
+ * Gather planned block-head tiles into the resident store: for every unit u
+ * and i < plan_count[u], copy K tile src_k[u][plan_src[u][i]] to
+ * res_k[u][plan_dst[u][i]] and the same for V (B*D*elem bytes each, layout
+ * preserved).  [v2] §3.2.1 (a gather kernel on the GPU reads the selected
+ * per-head entries from pinned host memory over PCIe and writes them into
+ * HBM) and §4.1 Implementation.  Run it on a background stream ordered after
+ * the attention that last read the destination slots.
+ *   src_k, src_v  [R][H][n_blk_max] tiles; device memory or pinned host
+ *                 memory the GPU can address (hipHostMalloc / pinned torch)
+ *   res_k, res_v  [R][H][top_k] tiles in device memory
+ *   plan_*        as written by oasis_select_plan (device memory)
+ * Errors: EINVAL, EUNSUPPORTED, EHIP.
+ */
+int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const void* src_v,
+                      int32_t n_blk_max, void* res_k, void* res_v, int32_t top_k,
+                      const int32_t* plan_count, const int32_t* plan_src,
+                      const int32_t* plan_dst, hipStream_t stream);
+
+/* Workspace bytes oasis_sparse_attn needs for this shape (0 for an invalid shape). */
+size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel);
+
+/*
+ * Paged GQA decode attention of all stacked query rows over each unit's
+ * selected tiles plus its active local block, in one call.
+ * Tokens of unit u: the B tokens of tile u*unit_stride + tile_table[u][s] for
+ * every s < n_sel with entry >= 0, plus the first tail_len[r] tokens of tile
+ * u*unit_stride + tail_tile[u] when both arrays are given and the entry >= 0.
+ *   z_i = scale * q[r][j][h] . k_i   (g = h / G)
+ *   out[r][j][h] = sum_i exp(z_i - m) v_i / sum_i exp(z_i - m),  m = max z
+ *   lse[r][j][h] = m + log(sum_i exp(z_i - m))
+ * A unit with no tokens gets out = 0 and lse = -inf.  Both rows attend the
+ * same tile set.  [v2] §3.1 and Fig. 6 (one attention call over one resident
+ * working set returns the outputs of the normal and the draft query) and
+ * §4.1 (each head also attends its active local block: K + 1 blocks).
+ *   q           [R][n_q][Hq][D] (dtype)
+ *   k_tiles     tile store, K tiles [B][D];  v_tiles  V tiles [D][B]
+ *   tile_table  [R][H][n_sel] int32 unit-local tile indices, -1 = skip
+ *   unit_stride tiles per unit in the store: K for a resident set of K slots
+ *               per head, n_blk_max when the full cache is the store
+ *   tail_tile   [R][H] int32 unit-local tile index of the active block, or NULL
+ *   tail_len    [R] int32 valid tokens of the active block (0..B), or NULL
+ *   scale       softmax scale; <= 0 means 1/sqrt(D)
+ *   out         [R][n_q][Hq][D] (dtype); bf16 rounds to nearest even
+ *   lse         [R][n_q][Hq] fp32, or NULL
+ *   workspace   at least oasis_sparse_attn_workspace() bytes
+ * Limits: n_q * G <= 32.
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int oasis_sparse_attn(const oasis_shape* s, const void* q, const void* k_tiles,
+                      const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
+                      int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len,
+                      float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * oasis_sparse_attn with an explicit choice of split kernel, for measuring one
+ * against the other: impl 0 = automatic (MFMA for bf16 with B a multiple of
+ * 16, VALU otherwise), 1 = VALU kernel (any dtype and B), 2 = MFMA kernel
+ * (EUNSUPPORTED unless bf16 and B % 16 == 0).  Results of 1 and 2 agree
+ * within the bf16 tolerance; the MFMA kernel rounds softmax weights to bf16.
+ */
+int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const void* k_tiles,
+                           const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
+                           int64_t unit_stride, const int32_t* tail_tile,
+                           const int32_t* tail_len, float scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, int32_t impl,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OASIS_H */

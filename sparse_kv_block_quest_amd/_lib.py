@@ -1,0 +1,105 @@
+"""ctypes loader of liboasis.so (the C ABI declared in include/oasis.h).
+
+The HIP library is the only implementation of the path: if it is not built,
+loading fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboasis.so")
+
+OASIS_OK = 0
+OASIS_EINVAL = -1
+OASIS_EUNSUPPORTED = -2
+OASIS_EWORKSPACE = -3
+OASIS_EHIP = -4
+
+OASIS_F32 = 0
+OASIS_BF16 = 1
+
+IMPL_AUTO = 0
+IMPL_VALU = 1
+IMPL_MFMA = 2
+
+# Every symbol include/oasis.h declares.
+EXPORTS = (
+    "oasis_status_string",
+    "oasis_version",
+    "oasis_build_summaries",
+    "oasis_score_topk_workspace",
+    "oasis_score_topk",
+    "oasis_select_plan",
+    "oasis_copy_blocks",
+    "oasis_sparse_attn_workspace",
+    "oasis_sparse_attn",
+    "oasis_sparse_attn_impl",
+)
+
+
+class OasisShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("n_q", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class OasisError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: status {status} ({text})")
+        self.status = status
+
+
+_lib = None
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+_shp = ctypes.POINTER(OasisShape)
+
+
+def load() -> ctypes.CDLL:
+    """Load liboasis.so and declare its signatures.  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "(hipcc --offload-arch=gfx950).  There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.oasis_status_string.argtypes = [ctypes.c_int]
+    lib.oasis_status_string.restype = ctypes.c_char_p
+    lib.oasis_version.argtypes = []
+    lib.oasis_version.restype = ctypes.c_int
+    lib.oasis_build_summaries.argtypes = [_shp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]
+    lib.oasis_score_topk_workspace.argtypes = [_shp, _i32, _i32]
+    lib.oasis_score_topk_workspace.restype = _sz
+    lib.oasis_score_topk.argtypes = [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.oasis_select_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                      _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+    lib.oasis_copy_blocks.argtypes = [_shp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+    lib.oasis_sparse_attn_workspace.argtypes = [_shp, _i32]
+    lib.oasis_sparse_attn_workspace.restype = _sz
+    lib.oasis_sparse_attn.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp,
+                                      ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
+    lib.oasis_sparse_attn_impl.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp,
+                                           _vp, ctypes.c_float, _vp, _vp, _vp, _sz, _i32, _vp]
+    for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan",
+                 "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def check(fn: str, status: int) -> None:
+    if status != OASIS_OK:
+        text = load().oasis_status_string(status).decode()
+        raise OasisError(fn, status, text)

@@ -1,0 +1,124 @@
+// Internal helpers shared by the gfx950 kernels of liboasis.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "oasis.h"
+
+namespace oasis {
+
+// ---------------------------------------------------------------- elements
+template <int DT>
+struct Elem;
+template <>
+struct Elem<OASIS_F32> {
+    static constexpr int bytes = 4;
+};
+template <>
+struct Elem<OASIS_BF16> {
+    static constexpr int bytes = 2;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Widen the 16 bytes of `v` into 16/bytes floats (exact).
+template <int DT>
+__device__ __forceinline__ void unpack16(const uint4& v, float* out) {
+    if constexpr (DT == OASIS_F32) {
+        out[0] = __uint_as_float(v.x);
+        out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z);
+        out[3] = __uint_as_float(v.w);
+    } else {
+        out[0] = bf16_lo(v.x);
+        out[1] = bf16_hi(v.x);
+        out[2] = bf16_lo(v.y);
+        out[3] = bf16_hi(v.y);
+        out[4] = bf16_lo(v.z);
+        out[5] = bf16_hi(v.z);
+        out[6] = bf16_lo(v.w);
+        out[7] = bf16_hi(v.w);
+    }
+}
+
+// Narrow 16/bytes floats that are exactly representable back into 16 bytes.
+template <int DT>
+__device__ __forceinline__ uint4 pack16_exact(const float* in) {
+    uint4 v;
+    if constexpr (DT == OASIS_F32) {
+        v.x = __float_as_uint(in[0]);
+        v.y = __float_as_uint(in[1]);
+        v.z = __float_as_uint(in[2]);
+        v.w = __float_as_uint(in[3]);
+    } else {
+        v.x = (__float_as_uint(in[0]) >> 16) | (__float_as_uint(in[1]) & 0xffff0000u);
+        v.y = (__float_as_uint(in[2]) >> 16) | (__float_as_uint(in[3]) & 0xffff0000u);
+        v.z = (__float_as_uint(in[4]) >> 16) | (__float_as_uint(in[5]) & 0xffff0000u);
+        v.w = (__float_as_uint(in[6]) >> 16) | (__float_as_uint(in[7]) & 0xffff0000u);
+    }
+    return v;
+}
+
+// Load one element as float.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* base, size_t i) {
+    if constexpr (DT == OASIS_F32) {
+        return reinterpret_cast<const float*>(base)[i];
+    } else {
+        return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(base)[i]) << 16);
+    }
+}
+
+// Store one float as an element (bf16: round to nearest even).
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, size_t i, float f) {
+    if constexpr (DT == OASIS_F32) {
+        reinterpret_cast<float*>(base)[i] = f;
+    } else {
+        reinterpret_cast<uint16_t*>(base)[i] = uint16_t(f32_to_bf16_bits(f));
+    }
+}
+
+// Order-preserving map of fp32 onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ host checks
+inline bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Shape fields every kernel family relies on.  Returns an oasis status.
+inline int check_shape(const oasis_shape* s) {
+    if (!s) return OASIS_EINVAL;
+    if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
+        s->block_size <= 0)
+        return OASIS_EINVAL;
+    if (s->n_q != 1 && s->n_q != 2) return OASIS_EINVAL;
+    if (s->n_q_heads % s->n_kv_heads != 0) return OASIS_EINVAL;
+    if (s->dtype != OASIS_F32 && s->dtype != OASIS_BF16) return OASIS_EUNSUPPORTED;
+    if (s->head_dim != 64 && s->head_dim != 128) return OASIS_EUNSUPPORTED;
+    if (!is_pow2(s->block_size) || s->block_size > 64) return OASIS_EUNSUPPORTED;
+    return OASIS_OK;
+}
+
+inline int launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? OASIS_OK : OASIS_EHIP;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace oasis

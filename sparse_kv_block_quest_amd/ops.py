@@ -1,0 +1,212 @@
+"""Torch-tensor front end of liboasis.so: argument marshalling only.
+
+Every function checks shapes, dtypes and devices of its tensors, hands their
+device pointers to the matching ``oasis_*`` entry point of the C ABI together
+with torch's current HIP stream, and returns.  No step of the path is computed
+here; workspaces are plain torch allocations.  Layouts and semantics are the
+ones documented in include/oasis.h.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import IMPL_AUTO, IMPL_MFMA, IMPL_VALU, OasisShape, check  # noqa: F401
+
+_DTYPES = {torch.float32: _lib.OASIS_F32, torch.bfloat16: _lib.OASIS_BF16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host_or_dev_ptr(t: torch.Tensor):
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if not t.is_cuda and not t.is_pinned():
+        raise ValueError("source store must be device memory or pinned host memory")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape(R, n_q, Hq, H, D, B, dtype) -> OasisShape:
+    return OasisShape(int(R), int(n_q), int(Hq), int(H), int(D), int(B), int(dtype))
+
+
+def build_summaries(keys: torch.Tensor, block_size: int, seq_len: torch.Tensor | None = None,
+                    blk_begin: int = 0, blk_end: int | None = None,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """keys [R][H][L_max][D] -> summaries [R][H][L_max/B][2][D] (0 = min, 1 = max)."""
+    lib = _lib.load()
+    if keys.dim() == 5:
+        keys = keys.flatten(2, 3)
+    R, H, Lmax, D = keys.shape
+    B = int(block_size)
+    if Lmax % B:
+        raise ValueError("L_max must be a multiple of block_size")
+    nb = Lmax // B
+    if out is None:
+        out = torch.zeros((R, H, nb, 2, D), dtype=keys.dtype, device=keys.device)
+    if out.shape != (R, H, nb, 2, D) or out.dtype != keys.dtype:
+        raise ValueError("summaries buffer has the wrong shape or dtype")
+    if seq_len is not None:
+        _i32(seq_len, "seq_len")
+    shp = _shape(R, 1, H, H, D, B, _dt(keys))
+    end = nb if blk_end is None else int(blk_end)
+    check("oasis_build_summaries",
+          lib.oasis_build_summaries(ctypes.byref(shp), _ptr(keys), nb, _ptr(seq_len),
+                                    int(blk_begin), end, _ptr(out), _stream(stream)))
+    return out
+
+
+def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
+               n_blk: torch.Tensor | None = None, want_scores: bool = False,
+               stream=None, out=None):
+    """q [R][n_q][Hq][D], summaries [R][H][n_blk_max][2][D].
+
+    Returns (topk_idx int32, topk_score fp32, scores fp32 or None), top-K tensors
+    shaped [R][n_q][H][top_k], scores [R][n_q][H][n_blk_max].  ``out`` may pass
+    preallocated (topk_idx, topk_score, scores, workspace).
+    """
+    lib = _lib.load()
+    R, n_q, Hq, D = q.shape
+    R2, H, nb, two, D2 = summaries.shape
+    if R2 != R or two != 2 or D2 != D or summaries.dtype != q.dtype:
+        raise ValueError("summaries do not match q")
+    shp = _shape(R, n_q, Hq, H, D, 1, _dt(q))
+    dev = q.device
+    if out is not None:
+        idx, val, sc, ws = out
+    else:
+        idx = torch.empty((R, n_q, H, top_k), dtype=torch.int32, device=dev)
+        val = torch.empty((R, n_q, H, top_k), dtype=torch.float32, device=dev)
+        sc = torch.empty((R, n_q, H, nb), dtype=torch.float32, device=dev) if want_scores else None
+        wsb = lib.oasis_score_topk_workspace(ctypes.byref(shp), nb, int(top_k))
+        ws = torch.empty(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+    if n_blk is not None:
+        _i32(n_blk, "n_blk")
+    check("oasis_score_topk",
+          lib.oasis_score_topk(ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk),
+                               int(top_k), _ptr(idx), _ptr(val), _ptr(sc), _ptr(ws),
+                               ws.numel(), _stream(stream)))
+    return idx, val, sc
+
+
+def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: torch.Tensor,
+                step: int, cap: int, pred_row: int = 1, slot_block_out=None,
+                slot_stamp_out=None, plan=None, want_evicted: bool = True, stream=None):
+    """Capped least-recently-selected plan.  Slot tables are updated in place
+    unless *_out tensors are given.  Returns dict of plan tensors."""
+    lib = _lib.load()
+    R, n_q, H, K = topk_idx.shape
+    for t, n in ((topk_idx, "topk_idx"), (slot_block, "slot_block"), (slot_stamp, "slot_stamp")):
+        _i32(t, n)
+    if slot_block.shape != (R, H, K) or slot_stamp.shape != (R, H, K):
+        raise ValueError("slot tables must be [R][H][K]")
+    bo = slot_block if slot_block_out is None else slot_block_out
+    so = slot_stamp if slot_stamp_out is None else slot_stamp_out
+    dev = topk_idx.device
+    if plan is None:
+        plan = {
+            "plan_count": torch.empty((R, H), dtype=torch.int32, device=dev),
+            "plan_src": torch.empty((R, H, K), dtype=torch.int32, device=dev),
+            "plan_dst": torch.empty((R, H, K), dtype=torch.int32, device=dev),
+            "plan_evicted": (torch.empty((R, H, K), dtype=torch.int32, device=dev)
+                             if want_evicted else None),
+        }
+    check("oasis_select_plan",
+          lib.oasis_select_plan(R, H, n_q, int(pred_row), K, _ptr(topk_idx), _ptr(slot_block),
+                                _ptr(slot_stamp), _ptr(bo), _ptr(so), int(step), int(cap),
+                                _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
+                                _ptr(plan["plan_dst"]), _ptr(plan.get("plan_evicted")),
+                                _stream(stream)))
+    return plan
+
+
+def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
+                res_v: torch.Tensor, plan: dict, block_size: int, stream=None) -> None:
+    """src_* [R][H][n_blk_max][tile] (device or pinned host), res_* [R][H][K][tile] (device),
+    where a tile is B*D elements (K tiles [B][D], V tiles [D][B])."""
+    lib = _lib.load()
+    R, H, nb = src_k.shape[:3]
+    K = res_k.shape[2]
+    tile = src_k[0, 0, 0].numel()
+    B = int(block_size)
+    D = tile // B
+    if src_v.shape != src_k.shape or res_v.shape != res_k.shape or res_k.shape[:2] != (R, H):
+        raise ValueError("store shapes do not match")
+    if res_k[0, 0, 0].numel() != tile or res_k.dtype != src_k.dtype:
+        raise ValueError("tile size or dtype mismatch")
+    shp = _shape(R, 1, H, H, D, B, _dt(src_k))
+    check("oasis_copy_blocks",
+          lib.oasis_copy_blocks(ctypes.byref(shp), _host_or_dev_ptr(src_k), _host_or_dev_ptr(src_v),
+                                nb, _ptr(res_k), _ptr(res_v), K, _ptr(plan["plan_count"]),
+                                _ptr(plan["plan_src"]), _ptr(plan["plan_dst"]), _stream(stream)))
+
+
+def sparse_attn_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_sel: int,
+                                dtype: torch.dtype) -> int:
+    R, n_q, Hq, D = q_shape
+    shp = _shape(R, n_q, Hq, n_kv_heads, D, block_size, _DTYPES[dtype])
+    return int(_lib.load().oasis_sparse_attn_workspace(ctypes.byref(shp), int(n_sel)))
+
+
+def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
+                tile_table: torch.Tensor, unit_stride: int, block_size: int,
+                tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
+                scale: float = 0.0, want_lse: bool = True, impl: int = IMPL_AUTO,
+                out=None, lse=None, workspace=None, stream=None):
+    """q [R][n_q][Hq][D]; k_tiles [..][B][D]; v_tiles [..][D][B] (dim-major);
+    tile_table [R][H][n_sel] unit-local indices (-1 = skip).  Returns (out, lse)."""
+    lib = _lib.load()
+    R, n_q, Hq, D = q.shape
+    R2, H, n_sel = tile_table.shape
+    _i32(tile_table, "tile_table")
+    if R2 != R:
+        raise ValueError("tile_table batch mismatch")
+    if k_tiles.dtype != q.dtype or v_tiles.dtype != q.dtype:
+        raise ValueError("q, k_tiles and v_tiles must share a dtype")
+    B = int(block_size)
+    shp = _shape(R, n_q, Hq, H, D, B, _dt(q))
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((R, n_q, Hq), dtype=torch.float32, device=dev)
+    if workspace is None:
+        wsb = lib.oasis_sparse_attn_workspace(ctypes.byref(shp), n_sel)
+        workspace = torch.empty(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+    for t, n in ((tail_tile, "tail_tile"), (tail_len, "tail_len")):
+        if t is not None:
+            _i32(t, n)
+    check("oasis_sparse_attn_impl",
+          lib.oasis_sparse_attn_impl(ctypes.byref(shp), _ptr(q), _ptr(k_tiles), _ptr(v_tiles),
+                                     _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile),
+                                     _ptr(tail_len), float(scale), _ptr(out),
+                                     _ptr(lse if want_lse else None), _ptr(workspace),
+                                     workspace.numel(), int(impl), _stream(stream)))
+    return out, (lse if want_lse else None)

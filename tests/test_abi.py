@@ -1,0 +1,111 @@
+"""The C ABI: every symbol include/oasis.h declares is exported by liboasis.so,
+and host-side argument checks reject bad calls before any kernel is launched
+(these calls never touch a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_kv_block_quest_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "oasis.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oasis_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("liboasis.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert len(names) >= 10
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 99):
+        assert lib.oasis_status_string(code)
+    assert lib.oasis_version() >= 100
+
+
+def _shape(**kw):
+    d = dict(batch=1, n_q=2, n_q_heads=4, n_kv_heads=2, head_dim=128, block_size=16, dtype=1)
+    d.update(kw)
+    return _lib.OasisShape(**d)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), _lib.OASIS_EINVAL),
+    (dict(n_q=3), _lib.OASIS_EINVAL),
+    (dict(n_q_heads=5), _lib.OASIS_EINVAL),
+    (dict(dtype=7), _lib.OASIS_EUNSUPPORTED),
+    (dict(head_dim=96), _lib.OASIS_EUNSUPPORTED),
+    (dict(block_size=12), _lib.OASIS_EUNSUPPORTED),
+    (dict(block_size=128), _lib.OASIS_EUNSUPPORTED),
+])
+def test_shape_validation(lib, kw, code):
+    s = _shape(**kw)
+    assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 0, 4, FAKE, None) == code
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 2, FAKE, None, FAKE, None, 0,
+                                None) == code
+    assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
+                                 FAKE, None, FAKE, 1 << 20, None) == code
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4, 2) == 0
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 2) == 0
+
+
+def test_argument_validation(lib):
+    s = _shape()
+    E = _lib.OASIS_EINVAL
+    assert lib.oasis_build_summaries(None, FAKE, 4, None, 0, 4, FAKE, None) == E
+    assert lib.oasis_build_summaries(ctypes.byref(s), None, 4, None, 0, 4, FAKE, None) == E
+    assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 3, 2, FAKE, None) == E
+    assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 2, 2, FAKE, None) == 0  # empty
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 0, FAKE, None, FAKE, None, 0,
+                                None) == E
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 1025, FAKE, None, FAKE, None,
+                                0, None) == E
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 40000, None, 8, FAKE, None, FAKE,
+                                None, 0, None) == _lib.OASIS_EUNSUPPORTED
+    # scores NULL and no workspace
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 2, FAKE, None, None, None, 0,
+                                None) == _lib.OASIS_EWORKSPACE
+    # plan: pred_row out of range, negative cap, K too large
+    args = [FAKE] * 5
+    assert lib.oasis_select_plan(1, 2, 2, 2, 8, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 8, *args, 0, -1, FAKE, FAKE, FAKE, None, None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 2048, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 8, None, *args[1:], 0, 1, FAKE, FAKE, FAKE, None,
+                                 None) == E
+    # attention: workspace too small, group too large, MFMA forced on fp32
+    assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
+                                 FAKE, None, FAKE, 0, None) == _lib.OASIS_EWORKSPACE
+    big = _shape(n_q_heads=34, n_kv_heads=1)
+    assert lib.oasis_sparse_attn(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
+                                 FAKE, None, FAKE, 1 << 30, None) == _lib.OASIS_EUNSUPPORTED
+    f32 = _shape(dtype=0)
+    assert lib.oasis_sparse_attn_impl(ctypes.byref(f32), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None,
+                                      0.0, FAKE, None, FAKE, 1 << 30, 2, None) == \
+        _lib.OASIS_EUNSUPPORTED
+    assert lib.oasis_copy_blocks(ctypes.byref(s), None, FAKE, 4, FAKE, FAKE, 8, FAKE, FAKE, FAKE,
+                                 None) == E
+
+
+def test_workspace_queries(lib):
+    s = _shape(batch=32, n_q_heads=32, n_kv_heads=8)
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 2048, 128) >= 32 * 2 * 8 * 2048 * 4
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 128) > 0

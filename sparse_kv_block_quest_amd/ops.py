@@ -157,10 +157,12 @@ def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
     tile = src_k[0, 0, 0].numel()
     B = int(block_size)
     D = tile // B
-    if src_v.shape != src_k.shape or res_v.shape != res_k.shape or res_k.shape[:2] != (R, H):
+    if src_v.shape[:3] != src_k.shape[:3] or res_v.shape[:3] != res_k.shape[:3] or \
+            res_k.shape[:2] != (R, H):
         raise ValueError("store shapes do not match")
-    if res_k[0, 0, 0].numel() != tile or res_k.dtype != src_k.dtype:
-        raise ValueError("tile size or dtype mismatch")
+    for t in (src_v, res_k, res_v):
+        if t[0, 0, 0].numel() != tile or t.dtype != src_k.dtype:
+            raise ValueError("tile size or dtype mismatch")
     shp = _shape(R, 1, H, H, D, B, _dt(src_k))
     check("oasis_copy_blocks",
           lib.oasis_copy_blocks(ctypes.byref(shp), _host_or_dev_ptr(src_k), _host_or_dev_ptr(src_v),

@@ -48,6 +48,11 @@ def parse_args(argv=None):
     p.add_argument("--batch", type=int, default=None, help="override the workload's batch")
     p.add_argument("--layers", type=int, default=None, help="override the number of layers")
     p.add_argument("--impl", choices=("auto", "valu", "mfma"), default="auto")
+    p.add_argument("--path", choices=("fused", "unfused"), default="fused",
+                   help="fused: one oasis_lookahead_step launch per layer-step; unfused: "
+                        "oasis_sparse_attn + oasis_score_topk + oasis_select_plan")
+    p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
+    p.add_argument("--attn-splits", type=int, default=0, help="fused path: 0 = automatic")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
     p.add_argument("--seed", type=int, default=None)
@@ -62,6 +67,10 @@ def algo_bytes(wl, e):
     attn = K * 2 * B * D * e + 2 * nq * G * D * e + nq * G * 4   # tiles, q, out, lse
     plan = K * 4 * 2 + K * 4 * 2 + K * 4 * 3 + 4                 # top-K row, slots r/w, plan
     return {"scan_topk": scan, "attn": attn, "plan": plan}
+
+
+def per_ls_alg(units, ab):
+    return units * sum(ab.values())
 
 
 def kernel_source_hash():
@@ -138,14 +147,15 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     qseq = query_sequence(wl, dev, n_layers, T, torch, synth)
 
     R, H, K, nq = wl.R, wl.H, wl.K, wl.n_q
-    # Preallocated outputs, workspaces and per-layer resident state.
+    # Preallocated outputs, workspaces and per-layer resident state (slot
+    # tables double-buffered: step t reads buffer t % 2 and plans into the other).
     idx = torch.empty((R, nq, H, K), dtype=torch.int32, device=dev)
     val = torch.empty((R, nq, H, K), dtype=torch.float32, device=dev)
     lib = _lib.load()
     shp = ops._shape(R, nq, wl.Hq, H, wl.D, 1, ops._dt(qseq))
-    ws_sc = torch.empty(int(lib.oasis_score_topk_workspace(ctypes.byref(shp), wl.n_blk, K)), dtype=torch.uint8,
-                        device=dev)
-    ws_at = torch.empty(max(1, ops.sparse_attn_workspace_bytes((R, nq, wl.Hq, wl.D), H, wl.B, K,
+    ws_sc = torch.zeros(int(lib.oasis_score_topk_workspace(ctypes.byref(shp), wl.n_blk, K)),
+                        dtype=torch.uint8, device=dev)
+    ws_at = torch.zeros(max(1, ops.sparse_attn_workspace_bytes((R, nq, wl.Hq, wl.D), H, wl.B, K,
                                                                wl.dtype)),
                         dtype=torch.uint8, device=dev)
     out = torch.empty((R, nq, wl.Hq, wl.D), dtype=wl.dtype, device=dev)
@@ -153,70 +163,107 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     plan = {k: torch.empty((R, H, K) if k != "plan_count" else (R, H), dtype=torch.int32,
                            device=dev) for k in ("plan_count", "plan_src", "plan_dst")}
     plan["plan_evicted"] = None
-    blk = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(n_layers)]
-    stamp = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(n_layers)]
+    blk = [[torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+           for _ in range(n_layers)]
+    stamp = [[torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+             for _ in range(n_layers)]
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
 
     # Seeding: the first working set comes from the first normal query (row 0).
     for l in range(n_layers):
         ops.score_topk(qseq[0, l], layers[l]["summ"], K, out=(idx, val, None, ws_sc))
-        ops.select_plan(idx, blk[l], stamp[l], 0, wl.cap, pred_row=0, plan=plan)
+        ops.select_plan(idx, blk[l][0], stamp[l][0], 0, wl.cap, pred_row=0, plan=plan)
     torch.cuda.synchronize()
+
+    fused = args.path == "fused"
+    calls = None
+    if fused:
+        opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
+        bufs = {}
+        calls = [[ops.prepare_lookahead_step(
+            qseq[0, l], layers[l]["summ"], K, blk[l][p], stamp[l][p], blk[l][1 - p],
+            stamp[l][1 - p], 0, wl.cap, layers[l]["keys"], layers[l]["vt"], blk[l][p], wl.n_blk,
+            wl.B, pred_row=1, want_evicted=False, opts=opts, bufs=bufs) for p in range(2)]
+            for l in range(n_layers)]
 
     ev_attn, ev_scan, ev_plan = [], [], []
 
     def layer_step(t, l, timed):
+        """One layer-step; `timed` (unfused breakdown pass only) brackets each
+        entry point with events.  The main timed region records no events
+        between launches: they add a gap of ~10 us per marker on this stack."""
         q = qseq[t, l]
         L = layers[l]
+        p = t % 2
+        if fused:
+            return calls[l][p](t + 1, q)["plan_count"]
         if timed:
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             s1, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a0.record()
-        ops.sparse_attn(q, L["keys"], L["vt"], blk[l], wl.n_blk, wl.B, impl=impl, out=out,
+        ops.sparse_attn(q, L["keys"], L["vt"], blk[l][p], wl.n_blk, wl.B, impl=impl, out=out,
                         lse=lse, workspace=ws_at)
         if timed:
             a1.record()
         ops.score_topk(q, L["summ"], K, out=(idx, val, None, ws_sc))
         if timed:
             s1.record()
-        ops.select_plan(idx, blk[l], stamp[l], t + 1, wl.cap, pred_row=1, plan=plan)
+        ops.select_plan(idx, blk[l][p], stamp[l][p], t + 1, wl.cap, pred_row=1,
+                        slot_block_out=blk[l][1 - p], slot_stamp_out=stamp[l][1 - p], plan=plan)
         if timed:
             p1.record()
             ev_attn.append((a0, a1))
             ev_scan.append((a1, s1))
             ev_plan.append((s1, p1))
+        return plan["plan_count"]
 
     for t in range(args.warmup):
         for l in range(n_layers):
             layer_step(t, l, False)
     torch.cuda.synchronize()
-    admitted.zero_()
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for t in range(args.warmup, args.warmup + args.steps):
         for l in range(n_layers):
-            layer_step(t, l, True)
+            layer_step(t, l, False)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
+    if not fused:
+        # Per-entry-point split of a layer-step, from a replay of the timed
+        # steps (the slot tables advance; the workload is the same).
+        for t in range(args.warmup, args.warmup + args.steps):
+            for l in range(n_layers):
+                layer_step(t, l, True)
+        torch.cuda.synchronize()
     # Churn, counted outside the timed region on the one spare step of queries.
     t = args.warmup + args.steps
     for l in range(n_layers):
-        layer_step(t, l, False)
-        admitted.add_(plan["plan_count"].sum())
+        admitted.add_(layer_step(t, l, False).sum())
     torch.cuda.synchronize()
+    cur = (t + 1) % 2  # buffer holding the newest resident set
+    launches = 1
+    if fused:
+        # A fused layer-step is one launch unless units are split (then the
+        # library adds a merge launch and needs a workspace).
+        launches = 1 if calls[0][0].res is not None and bufs["workspace"].numel() <= 1 else 2
 
     def avg_us(evs):
         return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
     res = {
-        "total_ms": total_ms, "wall_s": wall,
-        "attn_us": avg_us(ev_attn), "scan_topk_us": avg_us(ev_scan), "plan_us": avg_us(ev_plan),
+        "total_ms": total_ms, "wall_s": wall, "fused": fused,
+        "step_us": total_ms * 1000.0 / (args.steps * n_layers) if fused else None,
+        "launches": launches,
+        "attn_us": avg_us(ev_attn) if not fused else None,
+        "scan_topk_us": avg_us(ev_scan) if not fused else None,
+        "plan_us": avg_us(ev_plan) if not fused else None,
         "summ_ms": summ_ms,
         "admitted_per_head_step": float(admitted.item()) / (n_layers * R * H),
-        "layers": layers, "qseq": qseq, "blk": blk, "stamp": stamp,
+        "layers": layers, "qseq": qseq,
+        "blk_at_t": blk[0][cur], "stamp_at_t": stamp[0][cur],
     }
     return res
 
@@ -309,14 +356,20 @@ def main(argv=None):
     per_ls = units * sum(ab.values())
     attn_bytes = units * ab["attn"]
     scan_bytes = units * ab["scan_topk"]
-    kern = {
-        "oasis_sparse_attn": {"us": g["attn_us"], "algo_bytes": attn_bytes},
-        "oasis_score_topk": {"us": g["scan_topk_us"], "algo_bytes": scan_bytes},
-        "oasis_select_plan": {"us": g["plan_us"], "algo_bytes": units * ab["plan"]},
-    }
+    if g["fused"]:
+        kern = {"oasis_lookahead_step": {"us": g["step_us"], "algo_bytes": per_ls_alg(units, ab),
+                                         "launches": g["launches"]}}
+    else:
+        kern = {
+            "oasis_sparse_attn": {"us": g["attn_us"], "algo_bytes": attn_bytes},
+            "oasis_score_topk": {"us": g["scan_topk_us"], "algo_bytes": scan_bytes},
+            "oasis_select_plan": {"us": g["plan_us"], "algo_bytes": units * ab["plan"]},
+        }
     for k in kern.values():
         k["GBps"] = k["algo_bytes"] / (k["us"] * 1e-6) / 1e9
         k["frac"] = k["GBps"] / PEAK_HBM_GBS
+    # The fused step's duration is the timed region / launches (no markers
+    # between launches); the unfused split comes from the breakdown replay.
     dom = max(kern, key=lambda k: kern[k]["us"])
     achieved = kern[dom]["GBps"]
     src_hash = kernel_source_hash()
@@ -324,11 +377,8 @@ def main(argv=None):
 
     cpu = None
     if args.cpu_seconds > 0:
-        # resident state at the first timed step is re-derived by replaying the
-        # seeding + warmup plans would cost GPU time; the state after the run is
-        # an equally valid working set of this workload.
-        g["blk_at_t"] = g["blk"][0]
-        g["stamp_at_t"] = g["stamp"][0]
+        # The oracle runs on layer 0's newest resident set (after the churn
+        # step): a working set this workload reaches, on the GPU's own data.
         cpu = run_cpu_baseline(args, wl, g, torch, synth)
 
     summ_bytes = units * (wl.n_blk * wl.B * wl.D * e + wl.n_blk * 2 * wl.D * e)
@@ -349,7 +399,7 @@ def main(argv=None):
                                f"{wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}",
                    "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
                    "budget_tokens": wl.K * wl.B, "layers": wl.layers, "cap": wl.cap,
-                   "stacked_queries": wl.n_q, "impl": args.impl},
+                   "stacked_queries": wl.n_q, "impl": args.impl, "path": args.path},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

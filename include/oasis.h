@@ -100,8 +100,15 @@ int oasis_build_summaries(const oasis_shape* s, const void* keys, int32_t n_blk_
                           void* summaries, hipStream_t stream);
 
 /*
- * Workspace bytes oasis_score_topk needs (0 if none).  Returns 0 also for an
- * invalid shape; oasis_score_topk then reports the error.
+ * Workspaces.  When a unit's work is split over several workgroups (small
+ * batches, long contexts), the partial results (block scores, attention
+ * partials) go through a caller-owned scratch buffer and a second, small
+ * launch merges them.  The *_workspace() queries give its size for a shape;
+ * 0 means none is needed (or the shape is invalid, which the call reports).
+ * The content need not be initialised.  One workspace serves one call at a
+ * time: calls that may overlap in time (other streams) need their own.
+ *
+ * Workspace bytes oasis_score_topk needs.
  */
 size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k);
 
@@ -129,6 +136,7 @@ size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32
  *   scores      [R][n_q][H][n_blk_max] fp32 output of every block score
  *               (-inf past n_r), or NULL (then the workspace holds them)
  *   workspace   device buffer of at least oasis_score_topk_workspace() bytes
+ *               (NULL when that is 0; see Workspaces above)
  * Limits: n_blk_max <= 32768.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
  */
@@ -190,7 +198,7 @@ int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const void* src_v
                       const int32_t* plan_count, const int32_t* plan_src,
                       const int32_t* plan_dst, hipStream_t stream);
 
-/* Workspace bytes oasis_sparse_attn needs for this shape (0 for an invalid shape). */
+/* Workspace bytes oasis_sparse_attn needs for this shape (see Workspaces above). */
 size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel);
 
 /*
@@ -216,7 +224,7 @@ size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel);
  *   scale       softmax scale; <= 0 means 1/sqrt(D)
  *   out         [R][n_q][Hq][D] (dtype); bf16 rounds to nearest even
  *   lse         [R][n_q][Hq] fp32, or NULL
- *   workspace   at least oasis_sparse_attn_workspace() bytes
+ *   workspace   at least oasis_sparse_attn_workspace() bytes (NULL if 0)
  * Limits: n_q * G <= 32.
  * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
  */
@@ -239,6 +247,58 @@ int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const void* k_ti
                            const int32_t* tail_len, float scale, void* out, float* lse,
                            void* workspace, size_t workspace_bytes, int32_t impl,
                            hipStream_t stream);
+
+/* Tuning of oasis_lookahead_step; a NULL pointer or zero fields mean automatic. */
+typedef struct oasis_step_opts {
+    int32_t scan_chunks; /* workgroups that share one unit's summary scan (0 = auto) */
+    int32_t attn_splits; /* workgroups that share one unit's attention (0 = auto) */
+    int32_t attn_impl;   /* 0 automatic, 1 VALU, 2 MFMA (as oasis_sparse_attn_impl) */
+} oasis_step_opts;
+
+/* Workspace bytes of oasis_lookahead_step (see Workspaces above). */
+size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k,
+                                      int32_t n_sel, const oasis_step_opts* opts);
+
+/*
+ * One layer of one decode step, in a single launch when every unit fits one
+ * scan and one attention workgroup (at least 256 units): the attention of both
+ * stacked query rows over the current resident working set, and, from the same
+ * queries, the summary scan, the per-KV-head top-K of every row and the capped
+ * least-recently-selected plan that makes the next step's working set.
+ * [v2] §3.1 and Fig. 6 (the normal and draft queries share one attention call
+ * over the resident set; the draft query ranks the summaries to predict the
+ * next per-head set) and §3.3.1 (prediction and selection of step t+1 run
+ * while step t decodes); the two halves have no data dependence within a step.
+ *
+ * Results equal, bit for bit on the integer outputs,
+ *   oasis_sparse_attn(q, k_tiles, v_tiles, tile_table, n_sel, unit_stride,
+ *                     tail_tile, tail_len, scale, out, lse)
+ *   oasis_score_topk(q, summaries, n_blk_max, n_blk, top_k,
+ *                    topk_idx, topk_score, scores)
+ *   oasis_select_plan(R, H, n_q, pred_row, top_k, topk_idx, slot_block_in,
+ *                     slot_stamp_in, slot_block_out, slot_stamp_out, step,
+ *                     cap, plan_count, plan_src, plan_dst, plan_evicted)
+ * run in that order (arguments as documented there; the resident set holds
+ * K = top_k slots per KV head).  In the full-cache layout (unit_stride =
+ * n_blk_max) the caller passes slot_block_in as tile_table; the plan's outputs
+ * must then go to other buffers (double-buffer the slot tables), because the
+ * attention still reads the old table while the plan writes the new one:
+ * slot_block_out / slot_stamp_out overlapping tile_table is EINVAL.
+ *   opts       tuning, or NULL
+ *   workspace  at least oasis_lookahead_step_workspace() bytes (NULL if 0)
+ * Errors: EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP.
+ */
+int oasis_lookahead_step(const oasis_shape* s, const void* q, const void* summaries,
+                         int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
+                         int32_t* topk_idx, float* topk_score, float* scores,
+                         const int32_t* slot_block_in, const int32_t* slot_stamp_in,
+                         int32_t* slot_block_out, int32_t* slot_stamp_out, int32_t step,
+                         int32_t cap, int32_t pred_row, int32_t* plan_count, int32_t* plan_src,
+                         int32_t* plan_dst, int32_t* plan_evicted, const void* k_tiles,
+                         const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
+                         int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len,
+                         float scale, void* out, float* lse, const oasis_step_opts* opts,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -36,6 +36,8 @@ EXPORTS = (
     "oasis_sparse_attn_workspace",
     "oasis_sparse_attn",
     "oasis_sparse_attn_impl",
+    "oasis_lookahead_step_workspace",
+    "oasis_lookahead_step",
 )
 
 
@@ -48,6 +50,14 @@ class OasisShape(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+    ]
+
+
+class OasisStepOpts(ctypes.Structure):
+    _fields_ = [
+        ("scan_chunks", ctypes.c_int32),
+        ("attn_splits", ctypes.c_int32),
+        ("attn_impl", ctypes.c_int32),
     ]
 
 
@@ -92,8 +102,17 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
     lib.oasis_sparse_attn_impl.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp,
                                            _vp, ctypes.c_float, _vp, _vp, _vp, _sz, _i32, _vp]
+    _opts = ctypes.POINTER(OasisStepOpts)
+    lib.oasis_lookahead_step_workspace.argtypes = [_shp, _i32, _i32, _i32, _opts]
+    lib.oasis_lookahead_step_workspace.restype = _sz
+    lib.oasis_lookahead_step.argtypes = (
+        [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp,          # q .. scores
+         _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,  # slots .. plan
+         _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
+         _opts, _vp, _sz, _vp])
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan",
-                 "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl"):
+                 "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl",
+                 "oasis_lookahead_step"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -1,0 +1,1265 @@
+// Device code of the per-layer lookahead step, shared by the fused step kernel
+// and by the standalone score/top-K and attention entry points.
+//
+// Sources (web pages about "OasisKV: Scaling In-Decode KV Cache Beyond HBM with
+// Lookahead Sparse Prefetching"):
+//  - summary scan: paperpeel v2 text, §3.1, equation s_b(alpha) at alpha = 1,
+//    summed over the query heads that share one KV head (selection is per KV
+//    head: signal-papers reader text, paragraph on ranking non-resident
+//    blocks);
+//  - top-K: v2 §3.3.1 (the prediction stage ranks the compressed keys into the
+//    per-head block set);
+//  - plan: reader text, paragraphs on the capped eviction policy and on
+//    partial transfer at admission; v2 §3.3.2 (cap applies once the first
+//    working set is seeded; exactly K blocks stay resident per head);
+//  - attention: v2 §3.1 and Fig. 6 (one attention call over one resident
+//    working set returns the outputs of both stacked queries), §4.1 (each head
+//    also attends its active local block).
+//
+// Work decomposition.  A unit is one (request r, KV head g) pair, u = r*H + g.
+// A launch is a 1-D grid of 256-thread workgroups.  Consecutive workgroup ids
+// go round robin over the 8 XCDs, so id w runs on XCD w % 8; every item of
+// unit u gets an id on XCD u % 8, which keeps a unit's partial results in one
+// L2.  Per XCD, scan items come first.
+//  - scan item (u, c): scores of blocks [c*chunk, (c+1)*chunk) for every
+//    stacked row.  When one item covers the whole unit (NC = 1) its scores
+//    stay in LDS and the same workgroup selects the top-K of every row and, in
+//    the fused step, builds the plan.  Otherwise the scores go to global
+//    memory and a second, small launch (finish_kernel) selects and plans.
+//  - attention item (u, s): online softmax over split s of the unit's tile
+//    table (the last split also takes the active block).  With one split the
+//    item writes the outputs; with S > 1 it writes a partial (max, sum, acc)
+//    that finish_kernel merges in split order.
+// Workgroups of one launch never exchange data: on this multi-XCD part every
+// device-scope release writes back a whole L2, which costs more than a second
+// launch, so the kernel boundary is the only synchronisation.
+#pragma once
+
+#include "oasis_internal.h"
+
+namespace oasis {
+
+typedef short bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kNT = 256;        // threads of every step workgroup
+constexpr int kMaxTopK = 1024;  // largest K (resident slots per KV head)
+constexpr int kMaxRows = 32;    // n_q * G rows one attention item handles
+constexpr int kScanUnroll = 8;  // block passes in flight per scan thread
+constexpr int kTopkKPT = 16;    // top-K keys per thread held in registers
+constexpr int kMaxSplitEntries = 1024;  // tile-table entries of one attention item
+constexpr size_t kScoreLdsMax = 65536;  // scores of a whole unit kept in LDS up to this size
+
+enum { kAttnNone = 0, kAttnMfma = 1, kAttnValu = 2 };
+
+struct StepArgs {
+    // shape
+    int R, NQ, Hq, H, G, NR, D, B, U;
+    const uint8_t* q;  // [R][NQ][Hq][D]
+    // scan + top-K
+    const uint8_t* summ;  // [R][H][n_blk_max][2][D]
+    int n_blk_max;
+    const int32_t* n_blk;  // [R] or null
+    int K;
+    int32_t* topk_idx;   // [R][NQ][H][K]
+    float* topk_score;   // [R][NQ][H][K] or null
+    float* scores;       // [R][NQ][H][n_blk_max] global scores, or null (NC = 1 only)
+    int NC, chunk;       // scan items per unit, blocks per item
+    int scores_lds;      // NC = 1 and the unit's scores fit in LDS
+    // plan
+    int do_plan, pred_row, step, cap;
+    const int32_t* slot_blk_in;
+    const int32_t* slot_stamp_in;
+    int32_t* slot_blk_out;
+    int32_t* slot_stamp_out;
+    int32_t* plan_count;
+    int32_t* plan_src;
+    int32_t* plan_dst;
+    int32_t* plan_evicted;
+    // attention
+    const uint8_t* kt;  // K tiles [.][B][D]
+    const uint8_t* vt;  // V tiles [.][D][B]
+    const int32_t* table;  // [U][n_sel]
+    int n_sel;
+    long long unit_stride;
+    const int32_t* tail_tile;  // [U] or null
+    const int32_t* tail_len;   // [R] or null
+    float scale_log2;
+    void* out;   // [R][NQ][Hq][D]
+    float* lse;  // [R][NQ][Hq] or null
+    int S, per_split;
+    float* part_ml;   // [U][S][NR][2]
+    float* part_acc;  // [U][S][NR][D]
+    // roles enabled in this launch: items per unit (0 = role off)
+    int scan_items, attn_items;
+};
+
+// ------------------------------------------------------------ utilities
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for the
+// wave's outstanding global stores, which under a full HBM read stream cost
+// microseconds; the select / plan code exchanges data through LDS only and
+// leaves its global stores in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exclusive prefix sums over the workgroup of N values per thread.
+template <int N>
+__device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&excl)[N],
+                                           uint32_t (&total)[N], uint32_t* buf /*[4][N]*/) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t inc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) inc[i] = v[i];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const uint32_t t = __shfl_up(inc[i], off, 64);
+            if (lane >= off) inc[i] += t;
+        }
+    }
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) buf[w * N + i] = inc[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        uint32_t base = 0, tot = 0;
+#pragma unroll
+        for (int ww = 0; ww < kNT / 64; ++ww) {
+            const uint32_t x = buf[ww * N + i];
+            base += ww < w ? x : 0u;
+            tot += x;
+        }
+        excl[i] = inc[i] - v[i] + base;
+        total[i] = tot;
+    }
+    lds_barrier();
+}
+
+// ------------------------------------------------------------ LDS carving
+struct LdsCursor {
+    unsigned char* p;
+    template <typename T>
+    __device__ __forceinline__ T* take(size_t n) {
+        T* r = reinterpret_cast<T*>(p);
+        p += (n * sizeof(T) + 15) & ~size_t(15);
+        return r;
+    }
+};
+
+__host__ __device__ inline int pad4(int k) { return (k + 3) & ~3; }
+
+// LDS bytes of a scan item (P/N rows, top-K, plan, and the unit's scores when
+// they stay in LDS), mirrored by the carving in scan_item / finish_kernel.
+__host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_scores) {
+    auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+    const size_t kp = (size_t)pad4(K);
+    size_t b = a16(NQ * 2 * D * 4);                                     // pn
+    b += a16(NQ * 512 * 4) + a16(4 * 2 * 4) + a16(16 * 4);             // hist, scan, sh
+    b += a16(NQ * kp * 4) * 2 + a16(kp * 4);                            // sel key/idx, P
+    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 4 + a16(64);     // plan
+    b += a16((size_t)n_scores * 4);                                     // scores
+    return b;
+}
+
+// ============================================================ summary scan
+// Scores of blocks [c*chunk, (c+1)*chunk) of unit u for all NQ rows, written to
+// dst (row j at dst + j*drs; LDS or global) and, if dst2 is set, also to dst2.
+// LPR lanes share one block: lane cl owns the 16-byte chunk cl of the min row
+// and of the max row.  The loop is software-pipelined: the next UNR blocks of
+// every lane group are in flight while the current ones are reduced.
+template <int DT, int D, int NQ>
+__device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, float* pn, float* dst,
+                                            size_t drs, float* dst2, size_t drs2) {
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int VEC = 16 / EB;
+    constexpr int LPR = D / VEC;     // lanes per summary row
+    constexpr int BPP = kNT / LPR;   // blocks per workgroup pass
+    constexpr int UNR = kScanUnroll;
+    const int tid = threadIdx.x;
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    // P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0) over the group's heads.
+    for (int idx = tid; idx < NQ * D; idx += kNT) {
+        const int j = idx / D, d = idx - (idx / D) * D;
+        float p = 0.f, n = 0.f;
+        for (int h = 0; h < a.G; ++h) {
+            const float x =
+                load_elem<DT>(a.q, (((size_t)r * NQ + j) * a.Hq + (size_t)g * a.G + h) * D + d);
+            p += x > 0.f ? x : 0.f;
+            n += x < 0.f ? x : 0.f;
+        }
+        pn[(j * 2) * D + d] = p;
+        pn[(j * 2 + 1) * D + d] = n;
+    }
+    lds_barrier();
+    const int cl = tid % LPR, lb = tid / LPR;
+    float P[NQ][VEC], N[NQ][VEC];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            P[j][e] = pn[(j * 2) * D + cl * VEC + e];
+            N[j][e] = pn[(j * 2 + 1) * D + cl * VEC + e];
+        }
+    const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
+    const int b_begin = c * a.chunk;
+    const int b_end = min(b_begin + a.chunk, a.n_blk_max);
+    const int v_end = min(b_end, n_r);
+    const uint4* base = reinterpret_cast<const uint4*>(a.summ) + (size_t)u * a.n_blk_max * 2 * LPR + cl;
+    auto load = [&](int b0, uint4 (&mn)[UNR], uint4 (&mx)[UNR]) {
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            const int b = b0 + k * BPP + lb;
+            if (b < v_end) {
+                mn[k] = base[(size_t)b * 2 * LPR];
+                mx[k] = base[(size_t)b * 2 * LPR + LPR];
+            } else {
+                mn[k] = make_uint4(0, 0, 0, 0);
+                mx[k] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+    uint4 mn[UNR], mx[UNR];
+    load(b_begin, mn, mx);
+    for (int b0 = b_begin; b0 < b_end; b0 += BPP * UNR) {
+        uint4 mn2[UNR], mx2[UNR];
+        if (b0 + BPP * UNR < b_end) load(b0 + BPP * UNR, mn2, mx2);
+        float acc[UNR][NQ];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            float lo[VEC], hi[VEC];
+            unpack16<DT>(mn[k], lo);
+            unpack16<DT>(mx[k], hi);
+#pragma unroll
+            for (int j = 0; j < NQ; ++j) {
+                float sacc = 0.f;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    sacc = fmaf(P[j][e], hi[e], sacc);
+                    sacc = fmaf(N[j][e], lo[e], sacc);
+                }
+                acc[k][j] = sacc;
+            }
+        }
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1)
+#pragma unroll
+            for (int k = 0; k < UNR; ++k)
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) acc[k][j] += __shfl_xor(acc[k][j], off, 64);
+        if (cl == 0) {
+#pragma unroll
+            for (int k = 0; k < UNR; ++k) {
+                const int b = b0 + k * BPP + lb;
+                if (b < b_end) {
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j) {
+                        const float v = b < v_end ? acc[k][j] : -__builtin_inff();
+                        dst[j * drs + b] = v;
+                        if (dst2) dst2[j * drs2 + b] = v;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) {
+            mn[k] = mn2[k];
+            mx[k] = mx2[k];
+        }
+    }
+}
+
+// ============================================================ top-K
+struct TopkLds {
+    int* hist;          // [NQ][2][256] (double-buffered)
+    uint32_t* scanbuf;  // [4][2]
+    int* sh;            // [NQ][4]
+    uint32_t* sel_key;  // [NQ][Kp4]
+    int* sel_idx;       // [NQ][Kp4]
+    int* P;             // [Kp4] ranked blocks of the plan's row (-1 pad)
+};
+
+// Ranked top-K of NQ score rows (row j at sc + j*rs, n valid entries each; LDS
+// or global): the min(K, n) largest by (score desc, block asc).  The rows are
+// selected concurrently, each by its own group of kNT/NQ threads (whole
+// waves) holding up to kTopkKPT consecutive keys each in registers.  Radix
+// select on order-preserving uint32 keys: the bits every key of a row shares
+// are found first (min / max), then each pass resolves the next 8 bits below
+// them through a 256-bin LDS histogram (two buffers, so a pass needs two
+// barriers), until the threshold key's bin holds exactly the keys still to
+// take.  The threshold ties are compacted in block order and the survivors
+// ranked by counting.  Integer work only, so the result is exact for the fp32
+// scores given.
+template <int NQ>
+__device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oidx, float* oscore,
+                          size_t ors, int pred_row, const TopkLds& L) {
+    constexpr int TPR = kNT / NQ;  // threads per row
+    constexpr int WPR = TPR / 64;  // waves per row
+    constexpr int KPT = kTopkKPT;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = tid / TPR, t = tid - (tid / TPR) * TPR;  // row, thread within row
+    const int wr = wv - j * WPR;                           // wave within the row group
+    const int Kp = min(K, n);
+    const int K4 = pad4(K);
+    const float* row = sc + j * rs;
+    int32_t* orow = oidx + j * ors;
+    float* srow = oscore ? oscore + j * ors : nullptr;
+    for (int a = Kp + t; a < K; a += TPR) {
+        orow[a] = -1;
+        if (srow) srow[a] = -__builtin_inff();
+    }
+    if (j == pred_row)
+        for (int a = Kp + t; a < K4; a += TPR) L.P[a] = -1;
+    if (Kp <= 0) {
+        lds_barrier();
+        return;
+    }
+    const int per = (n + TPR - 1) / TPR;
+    const int i0 = min(t * per, n), i1 = min(i0 + per, n);
+    uint32_t key[KPT];
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) key[e] = (i0 + e < i1) ? float_key(row[i0 + e]) : 0u;
+    // Visit this thread's keys in block order.
+#define OASIS_FOR_KEYS(BODY)                                                      \
+    {                                                                             \
+        _Pragma("unroll") for (int e_ = 0; e_ < KPT; ++e_) {                      \
+            if (i0 + e_ < i1) {                                                   \
+                const uint32_t kk = key[e_];                                      \
+                const int ii = i0 + e_;                                           \
+                BODY                                                              \
+            }                                                                     \
+        }                                                                         \
+        for (int ii = i0 + KPT; ii < i1; ++ii) {                                  \
+            const uint32_t kk = float_key(row[ii]);                               \
+            BODY                                                                  \
+        }                                                                         \
+    }
+
+    // Bits shared by every key of a row: min and max over the row group.
+    uint32_t lo = 0xffffffffu, hi = 0u;
+    OASIS_FOR_KEYS({
+        (void)ii;
+        lo = kk < lo ? kk : lo;
+        hi = kk > hi ? kk : hi;
+    })
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = __shfl_xor(lo, off, 64), y = __shfl_xor(hi, off, 64);
+        lo = x < lo ? x : lo;
+        hi = y > hi ? y : hi;
+    }
+    if (lane == 0) {
+        L.scanbuf[wv * 2] = lo;
+        L.scanbuf[wv * 2 + 1] = hi;
+    }
+    for (int i = tid; i < NQ * 256; i += kNT) L.hist[(i >> 8) * 512 + (i & 255)] = 0;
+    lds_barrier();
+    // Every thread derives the starting state of every row (to know when all
+    // rows are done) and keeps the full state of its own row.
+    bool done_all[NQ];
+    uint32_t prefix = 0, mask = 0;
+    int hb = 0;
+#pragma unroll
+    for (int jj = 0; jj < NQ; ++jj) {
+        uint32_t l2 = 0xffffffffu, h2 = 0u;
+#pragma unroll
+        for (int w = jj * WPR; w < (jj + 1) * WPR; ++w) {
+            const uint32_t x = L.scanbuf[w * 2], y = L.scanbuf[w * 2 + 1];
+            l2 = x < l2 ? x : l2;
+            h2 = y > h2 ? y : h2;
+        }
+        const int b = l2 == h2 ? 0 : 32 - __clz(l2 ^ h2);  // low bits not shared
+        done_all[jj] = b == 0;
+        if (jj == j) {
+            hb = b;
+            mask = b >= 32 ? 0u : (0xffffffffu << b);
+            prefix = h2 & mask;
+        }
+    }
+    int remaining = Kp;
+    bool done = hb == 0;
+    int buf = 0;
+    for (;;) {
+        bool all = true;
+#pragma unroll
+        for (int jj = 0; jj < NQ; ++jj) all = all && done_all[jj];
+        if (all) break;
+        int* hist = L.hist + j * 512 + buf * 256;
+        const int w8 = hb < 8 ? hb : 8;
+        const int shift = hb - w8;
+        const uint32_t dm = (1u << w8) - 1u;
+        if (!done) {
+            OASIS_FOR_KEYS({
+                (void)ii;
+                if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & dm], 1);
+            })
+        }
+        lds_barrier();
+        if (!done && wr == 0) {
+            // Lane l holds digits 255-4l .. 252-4l, so a prefix over lanes is a
+            // suffix (largest digits first) over digits.
+            int c[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[e] = hist[255 - (4 * lane + e)];
+            const int local = c[0] + c[1] + c[2] + c[3];
+            int inc = local;
+            for (int off = 1; off < 64; off <<= 1) {
+                const int x = __shfl_up(inc, off, 64);
+                if (lane >= off) inc += x;
+            }
+            int before = inc - local;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (before < remaining && before + c[e] >= remaining) {
+                    const int rem2 = remaining - before;
+                    L.sh[j * 4 + 0] = 255 - (4 * lane + e);
+                    L.sh[j * 4 + 1] = before;
+                    L.sh[j * 4 + 3] = (c[e] == rem2 || shift == 0) ? 1 : 0;
+                }
+                before += c[e];
+            }
+        }
+        // The other buffer is cleared for the next pass meanwhile.
+        for (int i = tid; i < NQ * 256; i += kNT)
+            L.hist[(i >> 8) * 512 + (buf ^ 1) * 256 + (i & 255)] = 0;
+        lds_barrier();
+        if (!done) {
+            prefix |= uint32_t(L.sh[j * 4 + 0]) << shift;
+            mask |= dm << shift;
+            hb = shift;
+            remaining -= L.sh[j * 4 + 1];
+            done = L.sh[j * 4 + 3] != 0;
+        }
+#pragma unroll
+        for (int jj = 0; jj < NQ; ++jj)
+            if (!done_all[jj]) done_all[jj] = L.sh[jj * 4 + 3] != 0;
+        buf ^= 1;
+    }
+    // Take every key above the threshold prefix and the first `remaining`
+    // keys equal to it, in block order: exclusive counts within the row group.
+    uint32_t gt = 0, eq = 0;
+    OASIS_FOR_KEYS({
+        (void)ii;
+        const uint32_t mk = kk & mask;
+        gt += mk > prefix;
+        eq += mk == prefix;
+    })
+    uint32_t ig = gt, ie = eq;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = __shfl_up(ig, off, 64), y = __shfl_up(ie, off, 64);
+        if (lane >= off) {
+            ig += x;
+            ie += y;
+        }
+    }
+    if (lane == 63) {
+        L.scanbuf[wv * 2] = ig;
+        L.scanbuf[wv * 2 + 1] = ie;
+    }
+    lds_barrier();
+    for (int w = j * WPR; w < wv; ++w) {
+        ig += L.scanbuf[w * 2];
+        ie += L.scanbuf[w * 2 + 1];
+    }
+    int pos = int(ig - gt) + min(int(ie - eq), remaining);
+    int eqb = int(ie - eq);
+    uint32_t* skey = L.sel_key + j * K4;
+    int* sidx = L.sel_idx + j * K4;
+    OASIS_FOR_KEYS({
+        const uint32_t mk = kk & mask;
+        bool take = mk > prefix;
+        if (mk == prefix) {
+            take = eqb < remaining;
+            ++eqb;
+        }
+        if (take) {
+            skey[pos] = kk;
+            sidx[pos] = ii;
+            ++pos;
+        }
+    })
+#undef OASIS_FOR_KEYS
+    for (int a = Kp + t; a < K4; a += TPR) {
+        skey[a] = 0u;
+        sidx[a] = -1;
+    }
+    lds_barrier();
+    // Counting rank under (key desc, position asc); survivors sit in block order.
+    const uint4* kv = reinterpret_cast<const uint4*>(skey);
+    for (int a = t; a < Kp; a += TPR) {
+        const uint32_t ka = skey[a];
+        int rank = 0;
+#pragma unroll 8
+        for (int b4 = 0; b4 < K4 / 4; ++b4) {
+            const uint4 x = kv[b4];
+            const int b = b4 * 4;
+            rank += (x.x > ka) + ((x.x == ka) & (b + 0 < a));
+            rank += (x.y > ka) + ((x.y == ka) & (b + 1 < a));
+            rank += (x.z > ka) + ((x.z == ka) & (b + 2 < a));
+            rank += (x.w > ka) + ((x.w == ka) & (b + 3 < a));
+        }
+        const int bi = sidx[a];
+        orow[rank] = bi;
+        if (srow) srow[rank] = key_float(ka);
+        if (j == pred_row) L.P[rank] = bi;
+    }
+    lds_barrier();
+}
+
+// ============================================================ plan
+struct PlanLds {
+    int* blk;      // [K4]
+    int* stamp;    // [K4]
+    int* hit;      // [K4]
+    int* miss;     // [K4]
+    long long* ekey;  // [K4]
+    int* missing_of_rank;  // [K4]
+    int* victim_of_rank;   // [K4]
+    int* new_blk;          // [K4]
+    int* new_stamp;        // [K4]
+    uint32_t* scanbuf;     // [4][2]
+};
+
+__device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
+    PlanLds L;
+    L.blk = cur.take<int>(K4);
+    L.stamp = cur.take<int>(K4);
+    L.hit = cur.take<int>(K4);
+    L.miss = cur.take<int>(K4);
+    L.ekey = cur.take<long long>(K4);
+    L.missing_of_rank = cur.take<int>(K4);
+    L.victim_of_rank = cur.take<int>(K4);
+    L.new_blk = cur.take<int>(K4);
+    L.new_stamp = cur.take<int>(K4);
+    L.scanbuf = cur.take<uint32_t>(16);
+    return L;
+}
+
+// Stage one unit's slot tables in LDS (no barrier: plan_unit's callers pass
+// at least one before plan_unit reads them).  Issued early, so the loads
+// overlap other work.
+__device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* stamp_in, int K,
+                                          const PlanLds& L) {
+    const int K4 = pad4(K);
+    for (int s = threadIdx.x; s < K4; s += kNT) {
+        L.blk[s] = s < K ? blk_in[s] : -1;
+        L.stamp[s] = s < K ? stamp_in[s] : 0;
+    }
+}
+
+// Capped least-recently-selected plan of one unit from the ranked predicted
+// list P (LDS, -1 padded) and the staged slot tables.  The outputs may alias
+// the slot tables the stage was loaded from.
+__device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_out, int step,
+                          int cap, int32_t* cnt_out, int32_t* src_out, int32_t* dst_out,
+                          int32_t* ev_out, const PlanLds& L) {
+    const int tid = threadIdx.x;
+    const int K4 = pad4(K);
+    int empty = 0;
+    for (int s = tid; s < K; s += kNT) empty |= L.blk[s] == -1;
+    const bool wave_empty = __ballot(empty) != 0;
+    if ((tid & 63) == 0) L.scanbuf[8 + (tid >> 6)] = wave_empty;
+    lds_barrier();
+    const int seeding = (L.scanbuf[8] | L.scanbuf[9] | L.scanbuf[10] | L.scanbuf[11]) != 0;
+    // Membership both ways: slot s is a hit if its block is predicted; rank i
+    // is missing if its block is not resident.  Items [0, K) are slots,
+    // [K, 2K) predicted ranks.
+    const int4* P4 = reinterpret_cast<const int4*>(P);
+    const int4* B4 = reinterpret_cast<const int4*>(L.blk);
+    for (int it = tid; it < 2 * K; it += kNT) {
+        const bool slot = it < K;
+        const int idx = slot ? it : it - K;
+        const int v = slot ? L.blk[idx] : P[idx];
+        const int4* other = slot ? P4 : B4;
+        int found = 0;
+        if (v >= 0) {
+#pragma unroll 8
+            for (int i = 0; i < K4 / 4; ++i) {
+                const int4 x = other[i];
+                found |= (x.x == v) | (x.y == v) | (x.z == v) | (x.w == v);
+            }
+        }
+        if (slot)
+            L.hit[idx] = found;
+        else
+            L.miss[idx] = v >= 0 && !found;
+    }
+    lds_barrier();
+    // Missing blocks in rank order, victims counted.
+    uint32_t n_missing = 0, n_hits = 0;
+    for (int base = 0; base < K; base += kNT) {
+        const int i = base + tid;
+        uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
+        uint32_t ex[2], tot[2];
+        block_scan<2>(v, ex, tot, L.scanbuf);
+        if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
+        n_missing += tot[0];
+        n_hits += tot[1];
+    }
+    for (int s = tid; s < K4; s += kNT)
+        L.ekey[s] = (s < K && !L.hit[s])
+                        ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
+                        : 0x7fffffffffffffffLL;
+    lds_barrier();
+    // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
+    for (int s = tid; s < K; s += kNT) {
+        if (!L.hit[s]) {
+            const long long e = L.ekey[s];
+            int r = 0;
+            const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
+#pragma unroll 8
+            for (int i = 0; i < K4 / 2; ++i) {
+                const longlong2 x = E2[i];
+                r += (x.x < e) + (x.y < e);
+            }
+            L.victim_of_rank[r] = s;
+        }
+        L.new_blk[s] = L.blk[s];
+        L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+    }
+    lds_barrier();
+    const int n_victims = K - (int)n_hits;
+    int n = min((int)n_missing, n_victims);
+    if (!seeding) n = min(n, cap);
+    for (int i = tid; i < K; i += kNT) {
+        if (i < n) {
+            const int dst = L.victim_of_rank[i];
+            const int src = L.missing_of_rank[i];
+            src_out[i] = src;
+            dst_out[i] = dst;
+            if (ev_out) ev_out[i] = L.blk[dst];
+            L.new_blk[dst] = src;
+            L.new_stamp[dst] = step;
+        } else {
+            src_out[i] = -1;
+            dst_out[i] = -1;
+            if (ev_out) ev_out[i] = -1;
+        }
+    }
+    lds_barrier();
+    for (int s = tid; s < K; s += kNT) {
+        blk_out[s] = L.new_blk[s];
+        stamp_out[s] = L.new_stamp[s];
+    }
+    if (tid == 0) *cnt_out = n;
+}
+
+__device__ __forceinline__ TopkLds carve_topk(LdsCursor& cur, int NQ, int K4) {
+    TopkLds T;
+    T.hist = cur.take<int>(NQ * 512);
+    T.scanbuf = cur.take<uint32_t>(4 * 2);
+    T.sh = cur.take<int>(16);
+    T.sel_key = cur.take<uint32_t>((size_t)NQ * K4);
+    T.sel_idx = cur.take<int>((size_t)NQ * K4);
+    T.P = cur.take<int>(K4);
+    return T;
+}
+
+// Top-K of every row of unit u from `sc` (row stride rs), then, in the fused
+// step, the plan of the unit from row pred_row.
+template <int NQ>
+__device__ void select_unit(const StepArgs& a, int u, const float* sc, size_t rs,
+                            const TopkLds& T, const PlanLds& Pl) {
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
+    const size_t ors = (size_t)a.H * a.K;
+    const size_t ob = ((size_t)r * NQ * a.H + g) * a.K;
+    topk_rows<NQ>(sc, rs, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
+                  ors, a.do_plan ? a.pred_row : -1, T);
+    if (!a.do_plan) return;
+    const size_t so = (size_t)u * a.K;
+    plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
+              a.plan_count + u, a.plan_src + so, a.plan_dst + so,
+              a.plan_evicted ? a.plan_evicted + so : nullptr, Pl);
+}
+
+// ============================================================ scan item
+template <int DT, int D, int NQ>
+__device__ void scan_item(const StepArgs& a, int u, int c, unsigned char* lds) {
+    LdsCursor cur{lds};
+    float* pn = cur.take<float>(NQ * 2 * D);
+    const int K4 = pad4(a.K);
+    const TopkLds T = carve_topk(cur, NQ, K4);
+    const PlanLds Pl = carve_plan(cur, K4);
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    float* gsc = a.scores ? a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max : nullptr;
+    const size_t grs = (size_t)a.H * a.n_blk_max;
+    if (a.NC > 1) {  // one chunk of a split unit: scores to global, selection later
+        scan_blocks<DT, D, NQ>(a, u, c, pn, gsc, grs, nullptr, 0);
+        return;
+    }
+    if (a.do_plan) plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
+    if (a.scores_lds) {
+        float* lsc = cur.take<float>((size_t)NQ * a.n_blk_max);
+        scan_blocks<DT, D, NQ>(a, u, 0, pn, lsc, a.n_blk_max, gsc, grs);
+        lds_barrier();
+        select_unit<NQ>(a, u, lsc, a.n_blk_max, T, Pl);
+    } else {
+        scan_blocks<DT, D, NQ>(a, u, 0, pn, gsc, grs, nullptr, 0);
+        __syncthreads();
+        select_unit<NQ>(a, u, gsc, grs, T, Pl);
+    }
+}
+
+// ============================================================ attention
+// Split of one unit: table entries [e0, e1); the last split also owns the
+// active block (tail_len tokens of tile tail_tile).
+struct SplitRange {
+    int e0, e1, tail_tile, tail_len;
+};
+
+__device__ __forceinline__ SplitRange split_range(const StepArgs& a, int u, int sp) {
+    SplitRange s;
+    s.e0 = min(sp * a.per_split, a.n_sel);
+    s.e1 = min(s.e0 + a.per_split, a.n_sel);
+    s.tail_tile = -1;
+    s.tail_len = 0;
+    if (sp == a.S - 1 && a.tail_tile && a.tail_len) {
+        const int r = u / a.H;
+        const int tt = a.tail_tile[u];
+        const int tl = min(a.tail_len[r], a.B);
+        if (tt >= 0 && tl > 0) {
+            s.tail_tile = tt;
+            s.tail_len = tl;
+        }
+    }
+    return s;
+}
+
+// LDS of an attention item: table slice + final (m, l, acc) of the item, plus
+// the kernel-specific staging below.
+__host__ __device__ inline size_t attn_lds_bytes(int att, int NR, int D, int per_split) {
+    auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+    size_t b = a16((size_t)per_split * 4) + a16(NR * 4) * 2 + a16((size_t)NR * D * 4);
+    if (att == kAttnMfma) {
+        b += a16(3 * NR * 4) * 2 + a16((size_t)3 * NR * D * 4);
+    } else {
+        b += a16((size_t)kMaxRows * D * 4) + a16(16 * (D + 1) * 4) + a16((size_t)D * 17 * 4) +
+             a16(kMaxRows * 16 * 4) + a16(kMaxRows * 4) * 3;
+    }
+    return b;
+}
+
+struct AttnFin {
+    float* m;    // [NR] running max, log2 domain
+    float* l;    // [NR] sum of exp2(z - m)
+    float* acc;  // [NR][D] unnormalised output
+};
+
+// MFMA split (bf16, B % 16 == 0).  Per 16-token sub-tile:
+//   S^T[16 tok][16 rows] = K_sub[16][D] * Q^T  (v_mfma_f32_16x16x32_bf16; K rows
+//   go straight from HBM into the A operand, q stays in registers),
+//   O^T[D][rows] += V^T * P^T                  (v_mfma_f32_16x16x16_bf16; the A
+//   operand is 4 consecutive tokens of one dim, contiguous in a [D][B] V tile).
+// The 4 waves take sub-tiles round robin and prefetch their next sub-tile
+// into registers while the current one is computed.  P is rounded to bf16.
+template <int D, int NRG>
+__device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
+                               const int* tbl) {
+    constexpr int KB = D / 32;
+    constexpr int DB = D / 16;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int NR = a.NR, B = a.B;
+    float* lm = cur.take<float>(3 * NR);
+    float* ll = cur.take<float>(3 * NR);
+    float* la = cur.take<float>((size_t)3 * NR * D);
+
+    bf16x8_t qv[NRG][KB];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+        const int row = rg * 16 + l16;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qv[rg][kb] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        if (row < NR) {
+            const int j = row / a.G, hh = row - (row / a.G) * a.G;
+            const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(
+                a.q + ((((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh) * D) * 2);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) qv[rg][kb] = qp[kb * 4 + lg];
+        }
+    }
+    float m[NRG], lsum[NRG];
+    f32x4_t acc[NRG][DB];
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+        m[rg] = -__builtin_inff();
+        lsum[rg] = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const SplitRange sr = split_range(a, u, sp);
+    const int spe = B / 16;
+    const int n_entry_sub = (sr.e1 - sr.e0) * spe;
+    const int n_sub = n_entry_sub + (sr.tail_len + 15) / 16;
+    const size_t tile_elems = (size_t)B * D;
+
+    auto fetch = [&](int st, bf16x8_t (&kv)[KB], bf16x4_t (&vv)[DB]) -> int {
+        int tile, sub, ntok;
+        if (st < n_entry_sub) {
+            tile = tbl[st / spe];
+            sub = st - (st / spe) * spe;
+            ntok = 16;
+            if (tile < 0) return 0;
+        } else {
+            tile = sr.tail_tile;
+            sub = st - n_entry_sub;
+            ntok = min(16, sr.tail_len - sub * 16);
+        }
+        const size_t t64 = (size_t)((long long)u * a.unit_stride + tile);
+        const uint8_t* kbase = a.kt + (t64 * tile_elems + (size_t)sub * 16 * D) * 2;
+        const uint8_t* vbase = a.vt + (t64 * tile_elems + (size_t)sub * 16) * 2;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+            kv[kb] = *reinterpret_cast<const bf16x8_t*>(kbase + ((size_t)l16 * D + kb * 32 + lg * 8) * 2);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+            vv[db] = *reinterpret_cast<const bf16x4_t*>(vbase + ((size_t)(db * 16 + l16) * B + lg * 4) * 2);
+        return ntok;
+    };
+
+    bf16x8_t kc[KB];
+    bf16x4_t vc[DB];
+    int st = w;
+    int ntok = st < n_sub ? fetch(st, kc, vc) : 0;
+    while (st < n_sub) {
+        const int nx = st + 4;
+        bf16x8_t kn[KB];
+        bf16x4_t vn[DB];
+        const int ntok_n = nx < n_sub ? fetch(nx, kn, vn) : 0;
+        if (ntok > 0) {
+            if (ntok < 16) {
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (lg * 4 + e >= ntok) vc[db][e] = 0;
+            }
+#pragma unroll
+            for (int rg = 0; rg < NRG; ++rg) {
+                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kb], qv[rg][kb], s, 0, 0, 0);
+                float tmax = -__builtin_inff();
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    s[e] = (lg * 4 + e < ntok) ? s[e] * a.scale_log2 : -__builtin_inff();
+                    tmax = fmaxf(tmax, s[e]);
+                }
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+                const float mnew = fmaxf(m[rg], tmax);
+                const float corr = exp2f(m[rg] - mnew);
+                float p[4];
+                float psum = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = exp2f(s[e] - mnew);
+                    psum += p[e];
+                }
+                lsum[rg] = lsum[rg] * corr + psum;
+                m[rg] = mnew;
+                bf16x4_t pb;
+                pb[0] = (short)f32_to_bf16_bits(p[0]);
+                pb[1] = (short)f32_to_bf16_bits(p[1]);
+                pb[2] = (short)f32_to_bf16_bits(p[2]);
+                pb[3] = (short)f32_to_bf16_bits(p[3]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    acc[rg][db] *= corr;
+                    acc[rg][db] =
+                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vc[db], pb, acc[rg][db], 0, 0, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kc[kb] = kn[kb];
+#pragma unroll
+        for (int db = 0; db < DB; ++db) vc[db] = vn[db];
+        ntok = ntok_n;
+        st = nx;
+    }
+    // Row sums: the 4 lane groups hold disjoint tokens of the same rows.
+#pragma unroll
+    for (int rg = 0; rg < NRG; ++rg) {
+        lsum[rg] += __shfl_xor(lsum[rg], 16, 64);
+        lsum[rg] += __shfl_xor(lsum[rg], 32, 64);
+    }
+    // Waves 1..3 park their state, wave 0 combines in wave order.
+    if (w > 0) {
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) {
+            const int row = rg * 16 + l16;
+            if (row < NR) {
+                if (lg == 0) {
+                    lm[(w - 1) * NR + row] = m[rg];
+                    ll[(w - 1) * NR + row] = lsum[rg];
+                }
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        la[((size_t)(w - 1) * NR + row) * D + db * 16 + lg * 4 + e] = acc[rg][db][e];
+            }
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+        for (int rg = 0; rg < NRG; ++rg) {
+            const int row = rg * 16 + l16;
+            if (row >= NR) continue;
+            float mw[3];
+            float M = m[rg];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                mw[k] = lm[k * NR + row];
+                M = fmaxf(M, mw[k]);
+            }
+            const float f0 = (m[rg] == -__builtin_inff()) ? 0.f : exp2f(m[rg] - M);
+            float fk[3];
+            float Lr = lsum[rg] * f0;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                fk[k] = (mw[k] == -__builtin_inff()) ? 0.f : exp2f(mw[k] - M);
+                Lr += ll[k * NR + row] * fk[k];
+            }
+            if (lg == 0) {
+                F.m[row] = M;
+                F.l[row] = Lr;
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                f32x4_t o = acc[rg][db] * f0;
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] += fk[k] * la[((size_t)k * NR + row) * D + db * 16 + lg * 4 + e];
+                *reinterpret_cast<f32x4_t*>(F.acc + (size_t)row * D + db * 16 + lg * 4) = o;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// VALU split (any dtype and block size): 16-token sub-tiles of K and V staged
+// in LDS as fp32, scalar FMAs.
+template <int DT, int D>
+__device__ void attn_item_valu(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
+                               const int* tbl) {
+    constexpr int ST = 16;
+    constexpr int OPT = kMaxRows * D / kNT;
+    float* qs = cur.take<float>((size_t)kMaxRows * D);     // [row][D]
+    float* ks = cur.take<float>((size_t)ST * (D + 1));     // [tok][D+1]
+    float* vs = cur.take<float>((size_t)D * (ST + 1));     // [D][ST+1]
+    float* ps = cur.take<float>((size_t)kMaxRows * ST);    // [row][ST]
+    float* m_s = cur.take<float>(kMaxRows);
+    float* l_s = cur.take<float>(kMaxRows);
+    float* c_s = cur.take<float>(kMaxRows);
+    const int tid = threadIdx.x;
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int NR = a.NR, B = a.B;
+    for (int i = tid; i < NR * D; i += kNT) {
+        const int row = i / D, d = i - (i / D) * D;
+        const int j = row / a.G, hh = row - (row / a.G) * a.G;
+        qs[row * D + d] =
+            load_elem<DT>(a.q, (((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh) * D + d) *
+            a.scale_log2;
+    }
+    if (tid < NR) {
+        m_s[tid] = -__builtin_inff();
+        l_s[tid] = 0.f;
+    }
+    float acc[OPT];
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) acc[k] = 0.f;
+    __syncthreads();
+    const SplitRange sr = split_range(a, u, sp);
+    const int sub_tokens = B < ST ? B : ST;
+    const int spe = B / sub_tokens;
+    const int n_entry_sub = (sr.e1 - sr.e0) * spe;
+    const int n_sub = n_entry_sub + (sr.tail_len + sub_tokens - 1) / sub_tokens;
+    const size_t tile_elems = (size_t)B * D;
+    for (int st = 0; st < n_sub; ++st) {
+        int tile, sub, nt;
+        if (st < n_entry_sub) {
+            tile = tbl[st / spe];
+            sub = st - (st / spe) * spe;
+            nt = sub_tokens;
+            if (tile < 0) continue;
+        } else {
+            tile = sr.tail_tile;
+            sub = st - n_entry_sub;
+            nt = min(sub_tokens, sr.tail_len - sub * sub_tokens);
+        }
+        const size_t base = (size_t)((long long)u * a.unit_stride + tile) * tile_elems;
+        const int t0 = sub * sub_tokens;
+        for (int i = tid; i < nt * D; i += kNT) {
+            const int tt = i / D, d = i - (i / D) * D;
+            ks[tt * (D + 1) + d] = load_elem<DT>(a.kt, base + (size_t)(t0 + tt) * D + d);
+        }
+        for (int i = tid; i < D * nt; i += kNT) {
+            const int d = i / nt, tt = i - (i / nt) * nt;
+            vs[d * (ST + 1) + tt] = load_elem<DT>(a.vt, base + (size_t)d * B + t0 + tt);
+        }
+        __syncthreads();
+        for (int p = tid; p < NR * ST; p += kNT) {
+            const int row = p / ST, tt = p - (p / ST) * ST;
+            float z = -__builtin_inff();
+            if (tt < nt) {
+                z = 0.f;
+                for (int d = 0; d < D; ++d) z = fmaf(qs[row * D + d], ks[tt * (D + 1) + d], z);
+            }
+            ps[row * ST + tt] = z;
+        }
+        __syncthreads();
+        if (tid < NR) {
+            float mx = m_s[tid];
+            for (int tt = 0; tt < nt; ++tt) mx = fmaxf(mx, ps[tid * ST + tt]);
+            const float corr = exp2f(m_s[tid] - mx);
+            float sum = 0.f;
+            for (int tt = 0; tt < nt; ++tt) {
+                const float pv = exp2f(ps[tid * ST + tt] - mx);
+                ps[tid * ST + tt] = pv;
+                sum += pv;
+            }
+            l_s[tid] = l_s[tid] * corr + sum;
+            m_s[tid] = mx;
+            c_s[tid] = corr;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < OPT; ++k) {
+            const int o = tid + k * kNT;
+            if (o < NR * D) {
+                const int row = o / D, d = o - (o / D) * D;
+                float v = acc[k] * c_s[row];
+                for (int tt = 0; tt < nt; ++tt) v = fmaf(ps[row * ST + tt], vs[d * (ST + 1) + tt], v);
+                acc[k] = v;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < NR) {
+        F.m[tid] = m_s[tid];
+        F.l[tid] = l_s[tid];
+    }
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+        const int o = tid + k * kNT;
+        if (o < NR * D) F.acc[o] = acc[k];
+    }
+    __syncthreads();
+}
+
+// Output row of stacked row `row` (j * G + h within the group) of unit u.
+__device__ __forceinline__ size_t attn_out_row(const StepArgs& a, int u, int row) {
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int j = row / a.G, hh = row - (row / a.G) * a.G;
+    return ((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh;
+}
+
+// Output of an attention item: normalised outputs when the unit has one
+// split, else the split's partial (max, sum, acc) for finish_kernel.
+template <int DT, int D>
+__device__ void attn_emit(const StepArgs& a, int u, int sp, const AttnFin& F) {
+    const int tid = threadIdx.x;
+    const int NR = a.NR;
+    if (a.S == 1) {
+        for (int o = tid; o < NR * D; o += kNT) {
+            const int row = o / D, d = o - (o / D) * D;
+            const float L = F.l[row];
+            store_elem<DT>(a.out, attn_out_row(a, u, row) * D + d, L > 0.f ? F.acc[o] / L : 0.f);
+        }
+        if (a.lse && tid < NR) {
+            const float L = F.l[tid];
+            a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (F.m[tid] + log2f(L)) * kLn2 : -__builtin_inff();
+        }
+        return;
+    }
+    const size_t pb = ((size_t)u * a.S + sp) * NR;
+    for (int o = tid; o < NR * D; o += kNT) a.part_acc[pb * D + o] = F.acc[o];
+    if (tid < NR) {
+        a.part_ml[(pb + tid) * 2 + 0] = F.m[tid];
+        a.part_ml[(pb + tid) * 2 + 1] = F.l[tid];
+    }
+}
+
+// LSE merge of a unit's S split partials, in split order.
+template <int DT, int D>
+__device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr) {
+    const int tid = threadIdx.x;
+    const int NR = a.NR;
+    if (tid < NR) {
+        float M = -__builtin_inff();
+        for (int s = 0; s < a.S; ++s)
+            M = fmaxf(M, a.part_ml[(((size_t)u * a.S + s) * NR + tid) * 2]);
+        float L = 0.f;
+        if (M != -__builtin_inff()) {
+            for (int s = 0; s < a.S; ++s) {
+                const size_t pr = ((size_t)u * a.S + s) * NR + tid;
+                const float ms = a.part_ml[pr * 2];
+                if (ms != -__builtin_inff()) L += exp2f(ms - M) * a.part_ml[pr * 2 + 1];
+            }
+        }
+        Mr[tid] = M;
+        Lr[tid] = L;
+        if (a.lse) a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
+    }
+    __syncthreads();
+    for (int o = tid; o < NR * D; o += kNT) {
+        const int row = o / D, d = o - (o / D) * D;
+        const float M = Mr[row], L = Lr[row];
+        float acc = 0.f;
+        if (L > 0.f) {
+            for (int s = 0; s < a.S; ++s) {
+                const size_t pr = ((size_t)u * a.S + s) * NR + row;
+                const float ms = a.part_ml[pr * 2];
+                if (ms != -__builtin_inff()) acc = fmaf(exp2f(ms - M), a.part_acc[pr * D + d], acc);
+            }
+        }
+        store_elem<DT>(a.out, attn_out_row(a, u, row) * D + d, L > 0.f ? acc / L : 0.f);
+    }
+}
+
+template <int DT, int D, int ATT, int NRG>
+__device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) {
+    LdsCursor cur{lds};
+    int* tbl = cur.take<int>(a.per_split > 0 ? a.per_split : 1);
+    AttnFin F;
+    F.m = cur.take<float>(a.NR);
+    F.l = cur.take<float>(a.NR);
+    F.acc = cur.take<float>((size_t)a.NR * D);
+    const SplitRange sr = split_range(a, u, sp);
+    for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT) tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
+    __syncthreads();
+    if constexpr (ATT == kAttnMfma) {
+        attn_item_mfma<D, NRG>(a, u, sp, cur, F, tbl);
+    } else {
+        attn_item_valu<DT, D>(a, u, sp, cur, F, tbl);
+    }
+    attn_emit<DT, D>(a, u, sp, F);
+}
+
+// ============================================================ the kernels
+// Main launch.  Roles present are fixed at compile time (SCAN, ATT !=
+// kAttnNone); the number of items per unit of each role comes from the
+// arguments.
+template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN>
+__global__ void __launch_bounds__(kNT) step_kernel(StepArgs a) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int w = blockIdx.x;
+    const int x = w & 7;
+    int k = w >> 3;
+    const int nu = a.U > x ? (a.U - x + 7) / 8 : 0;  // units on this XCD
+    if constexpr (SCAN) {
+        const int ns = nu * a.scan_items;
+        if (k < ns) {
+            const int i = k / a.scan_items, c = k - (k / a.scan_items) * a.scan_items;
+            scan_item<DT, D, NQ>(a, x + 8 * i, c, lds);
+            return;
+        }
+        k -= ns;
+    }
+    if constexpr (ATT != kAttnNone) {
+        if (k < nu * a.attn_items) {
+            const int i = k / a.attn_items, s = k - (k / a.attn_items) * a.attn_items;
+            attn_item<DT, D, ATT, NRG>(a, x + 8 * i, s, lds);
+        }
+    }
+}
+
+// Second launch for split units: top-K (+ plan) from the global scores when
+// NC > 1 (`select` items), LSE merge of the attention partials when S > 1
+// (`merge` items).  Same XCD mapping as the main launch.
+template <int DT, int D, int NQ>
+__global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_items, int merge_items) {
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int w = blockIdx.x;
+    const int x = w & 7;
+    int k = w >> 3;
+    const int nu = a.U > x ? (a.U - x + 7) / 8 : 0;
+    LdsCursor cur{lds};
+    if (select_items) {
+        if (k < nu) {
+            const int u = x + 8 * k;
+            const int K4 = pad4(a.K);
+            const TopkLds T = carve_topk(cur, NQ, K4);
+            const PlanLds Pl = carve_plan(cur, K4);
+            if (a.do_plan)
+                plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
+            const int r = u / a.H, g = u - (u / a.H) * a.H;
+            select_unit<NQ>(a, u, a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max,
+                            (size_t)a.H * a.n_blk_max, T, Pl);
+            return;
+        }
+        k -= nu;
+    }
+    if (merge_items && k < nu) {
+        float* Mr = cur.take<float>(kMaxRows);
+        float* Lr = cur.take<float>(kMaxRows);
+        attn_merge_unit<DT, D>(a, x + 8 * k, Mr, Lr);
+    }
+}
+
+__host__ __device__ inline size_t finish_lds_bytes(int NQ, int K) {
+    const size_t s = scan_lds_bytes(NQ, 0, K, 0);
+    return s > 256 ? s : 256;
+}
+
+// ============================================================ host helpers
+struct StepPlan {
+    int NC, chunk, S, per_split;
+};
+
+// Items per unit.  With at least 256 units (one per CU) every unit gets one
+// scan item and one attention item: no partials, one launch.  Smaller batches
+// split units until about 512 main workgroups (two per CU) are in flight,
+// sharing the items between scan and attention by their bytes, with at least
+// 64 blocks per scan item and 4 tiles per attention split; the split units
+// then take a second, small launch.
+inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb, bool scan,
+                           bool attn, int want_nc, int want_s) {
+    StepPlan p{0, 0, 0, 0};
+    const double scan_b = scan ? (double)n_blk_max * 2 * D * eb : 0.0;
+    const double attn_b = attn ? (double)n_sel * 2 * B * D * eb : 0.0;
+    const int items = U >= 256 ? (scan ? 1 : 0) + (attn ? 1 : 0) : (511 + U) / U;
+    const double tot = scan_b + attn_b > 0 ? scan_b + attn_b : 1.0;
+    if (scan) {
+        int nc = want_nc > 0 ? want_nc
+                             : (U >= 256 ? 1 : (int)(items * scan_b / tot + 0.5));
+        const int max_nc = want_nc > 0 ? n_blk_max : (n_blk_max + 63) / 64;
+        if (nc > max_nc) nc = max_nc;
+        if (nc < 1) nc = 1;
+        const int chunk = (n_blk_max + nc - 1) / nc;
+        p.chunk = chunk;
+        p.NC = (n_blk_max + chunk - 1) / chunk;
+    }
+    if (attn) {
+        int s = want_s > 0 ? want_s : (U >= 256 ? 1 : (int)(items * attn_b / tot + 0.5));
+        if (want_s <= 0 && s > (n_sel + 3) / 4) s = (n_sel + 3) / 4;
+        const int min_s = (n_sel + kMaxSplitEntries - 1) / kMaxSplitEntries;
+        if (s < min_s) s = min_s;
+        if (n_sel > 0 && s > n_sel) s = n_sel;
+        if (s < 1) s = 1;
+        const int per = n_sel > 0 ? (n_sel + s - 1) / s : 0;
+        p.per_split = per;
+        p.S = per > 0 ? (n_sel + per - 1) / per : 1;
+    }
+    return p;
+}
+
+}  // namespace oasis

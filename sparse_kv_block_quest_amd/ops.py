@@ -13,7 +13,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import IMPL_AUTO, IMPL_MFMA, IMPL_VALU, OasisShape, check  # noqa: F401
+from ._lib import IMPL_AUTO, IMPL_MFMA, IMPL_VALU, OasisShape, OasisStepOpts, check  # noqa: F401
 
 _DTYPES = {torch.float32: _lib.OASIS_F32, torch.bfloat16: _lib.OASIS_BF16}
 
@@ -106,7 +106,7 @@ def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
         val = torch.empty((R, n_q, H, top_k), dtype=torch.float32, device=dev)
         sc = torch.empty((R, n_q, H, nb), dtype=torch.float32, device=dev) if want_scores else None
         wsb = lib.oasis_score_topk_workspace(ctypes.byref(shp), nb, int(top_k))
-        ws = torch.empty(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+        ws = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
     if n_blk is not None:
         _i32(n_blk, "n_blk")
     check("oasis_score_topk",
@@ -201,7 +201,7 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
         lse = torch.empty((R, n_q, Hq), dtype=torch.float32, device=dev)
     if workspace is None:
         wsb = lib.oasis_sparse_attn_workspace(ctypes.byref(shp), n_sel)
-        workspace = torch.empty(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
     for t, n in ((tail_tile, "tail_tile"), (tail_len, "tail_len")):
         if t is not None:
             _i32(t, n)
@@ -212,3 +212,130 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
                                      _ptr(lse if want_lse else None), _ptr(workspace),
                                      workspace.numel(), int(impl), _stream(stream)))
     return out, (lse if want_lse else None)
+
+
+def step_opts(scan_chunks: int = 0, attn_splits: int = 0, impl: int = IMPL_AUTO) -> OasisStepOpts:
+    return OasisStepOpts(int(scan_chunks), int(attn_splits), int(impl))
+
+
+def lookahead_step_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_blk_max: int,
+                                   top_k: int, n_sel: int, dtype: torch.dtype,
+                                   opts: OasisStepOpts | None = None) -> int:
+    R, n_q, Hq, D = q_shape
+    shp = _shape(R, n_q, Hq, n_kv_heads, D, block_size, _DTYPES[dtype])
+    return int(_lib.load().oasis_lookahead_step_workspace(
+        ctypes.byref(shp), int(n_blk_max), int(top_k), int(n_sel),
+        ctypes.byref(opts) if opts is not None else None))
+
+
+class PreparedStep:
+    """A validated oasis_lookahead_step call whose ctypes arguments are built
+    once; calling it re-issues the step with a new step index (and,
+    optionally, new query and tile-table pointers of the same shape).  Meant
+    for decode loops where Python marshalling would otherwise cost as much as
+    the kernel."""
+
+    _Q, _STEP, _BI, _SI, _BO, _SO, _TBL = 1, 13, 9, 10, 11, 12, 22
+
+    def __init__(self, args, res, lib):
+        self.args = args
+        self.res = res
+        self._fn = lib.oasis_lookahead_step
+
+    def __call__(self, step: int, q: torch.Tensor | None = None) -> dict:
+        a = self.args
+        a[self._STEP] = int(step)
+        if q is not None:
+            a[self._Q] = ctypes.c_void_p(q.data_ptr())
+        st = self._fn(*a)
+        if st != 0:
+            check("oasis_lookahead_step", st)
+        return self.res
+
+
+def lookahead_step(*args, **kwargs) -> dict:
+    """One fused layer-step; see ``prepare_lookahead_step`` for the arguments."""
+    call = prepare_lookahead_step(*args, **kwargs)
+    return call(call.args[PreparedStep._STEP])
+
+
+def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
+                   slot_block: torch.Tensor, slot_stamp: torch.Tensor,
+                   slot_block_out: torch.Tensor, slot_stamp_out: torch.Tensor,
+                   step: int, cap: int, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
+                   tile_table: torch.Tensor, unit_stride: int, block_size: int,
+                   pred_row: int = 1, n_blk: torch.Tensor | None = None,
+                   tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
+                   scale: float = 0.0, want_scores: bool = False, want_lse: bool = True,
+                   want_evicted: bool = True, opts: OasisStepOpts | None = None,
+                   bufs: dict | None = None, stream=None) -> PreparedStep:
+    """One fused layer-step (attention over ``tile_table`` + scan, top-K and plan).
+
+    q [R][n_q][Hq][D]; summaries [R][H][n_blk_max][2][D]; slot tables [R][H][top_k]
+    (the ``*_out`` pair must not overlap ``tile_table``); tiles and table as in
+    ``sparse_attn``.  ``bufs`` may hold preallocated outputs under the keys of the
+    result dict plus ``workspace`` (zero-filled); missing ones are allocated and
+    added to it.  Returns the prepared call; its result is a dict with out, lse,
+    topk_idx, topk_score, scores, plan_count, plan_src, plan_dst, plan_evicted.
+    """
+    lib = _lib.load()
+    R, n_q, Hq, D = q.shape
+    R2, H, nb, two, D2 = summaries.shape
+    if R2 != R or two != 2 or D2 != D or summaries.dtype != q.dtype:
+        raise ValueError("summaries do not match q")
+    if k_tiles.dtype != q.dtype or v_tiles.dtype != q.dtype:
+        raise ValueError("q, k_tiles and v_tiles must share a dtype")
+    K = int(top_k)
+    for t, n in ((slot_block, "slot_block"), (slot_stamp, "slot_stamp"),
+                 (slot_block_out, "slot_block_out"), (slot_stamp_out, "slot_stamp_out")):
+        _i32(t, n)
+        if t.shape != (R, H, K):
+            raise ValueError(f"{n} must be [R][H][top_k]")
+    _i32(tile_table, "tile_table")
+    if tile_table.shape[:2] != (R, H):
+        raise ValueError("tile_table must be [R][H][n_sel]")
+    n_sel = tile_table.shape[2]
+    B = int(block_size)
+    shp = _shape(R, n_q, Hq, H, D, B, _dt(q))
+    dev = q.device
+    b = {} if bufs is None else bufs
+
+    def get(key, shape, dtype, zero=False):
+        t = b.get(key)
+        if t is None:
+            t = (torch.zeros if zero else torch.empty)(shape, dtype=dtype, device=dev)
+            b[key] = t
+        return t
+
+    res = {
+        "out": get("out", q.shape, q.dtype),
+        "lse": get("lse", (R, n_q, Hq), torch.float32) if want_lse else None,
+        "topk_idx": get("topk_idx", (R, n_q, H, K), torch.int32),
+        "topk_score": get("topk_score", (R, n_q, H, K), torch.float32),
+        "scores": get("scores", (R, n_q, H, nb), torch.float32) if want_scores else None,
+        "plan_count": get("plan_count", (R, H), torch.int32),
+        "plan_src": get("plan_src", (R, H, K), torch.int32),
+        "plan_dst": get("plan_dst", (R, H, K), torch.int32),
+        "plan_evicted": get("plan_evicted", (R, H, K), torch.int32) if want_evicted else None,
+    }
+    if b.get("workspace") is None:
+        wsb = lib.oasis_lookahead_step_workspace(ctypes.byref(shp), nb, K, n_sel,
+                                                 ctypes.byref(opts) if opts is not None else None)
+        b["workspace"] = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+    ws = b["workspace"]
+    for t, n in ((n_blk, "n_blk"), (tail_tile, "tail_tile"), (tail_len, "tail_len")):
+        if t is not None:
+            _i32(t, n)
+    args = [ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk), K,
+            _ptr(res["topk_idx"]), _ptr(res["topk_score"]), _ptr(res["scores"]),
+            _ptr(slot_block), _ptr(slot_stamp), _ptr(slot_block_out), _ptr(slot_stamp_out),
+            int(step), int(cap), int(pred_row), _ptr(res["plan_count"]), _ptr(res["plan_src"]),
+            _ptr(res["plan_dst"]), _ptr(res["plan_evicted"]), _ptr(k_tiles), _ptr(v_tiles),
+            _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile), _ptr(tail_len),
+            float(scale), _ptr(res["out"]), _ptr(res["lse"]),
+            ctypes.byref(opts) if opts is not None else None, _ptr(ws), ws.numel(),
+            _stream(stream)]
+    call = PreparedStep(args, res, lib)
+    call._keep = (shp, opts, q, summaries, slot_block, slot_stamp, slot_block_out,
+                  slot_stamp_out, k_tiles, v_tiles, tile_table, n_blk, tail_tile, tail_len, ws)
+    return call

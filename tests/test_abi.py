@@ -81,9 +81,10 @@ def test_argument_validation(lib):
                                 0, None) == E
     assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 40000, None, 8, FAKE, None, FAKE,
                                 None, 0, None) == _lib.OASIS_EUNSUPPORTED
-    # scores NULL and no workspace
-    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 2, FAKE, None, None, None, 0,
-                                None) == _lib.OASIS_EWORKSPACE
+    # scores NULL and no workspace, at a shape whose units are split (needs scratch)
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4096, 2) > 0
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4096, None, 2, FAKE, None, None, None,
+                                0, None) == _lib.OASIS_EWORKSPACE
     # plan: pred_row out of range, negative cap, K too large
     args = [FAKE] * 5
     assert lib.oasis_select_plan(1, 2, 2, 2, 8, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
@@ -91,8 +92,9 @@ def test_argument_validation(lib):
     assert lib.oasis_select_plan(1, 2, 2, 1, 2048, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
     assert lib.oasis_select_plan(1, 2, 2, 1, 8, None, *args[1:], 0, 1, FAKE, FAKE, FAKE, None,
                                  None) == E
-    # attention: workspace too small, group too large, MFMA forced on fp32
-    assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
+    # attention: workspace too small (split units), group too large, MFMA forced on fp32
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 64) > 0
+    assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 64, 64, None, None, 0.0,
                                  FAKE, None, FAKE, 0, None) == _lib.OASIS_EWORKSPACE
     big = _shape(n_q_heads=34, n_kv_heads=1)
     assert lib.oasis_sparse_attn(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
@@ -106,6 +108,57 @@ def test_argument_validation(lib):
 
 
 def test_workspace_queries(lib):
+    # 256 units: one workgroup per unit and role, scores in LDS, no scratch
     s = _shape(batch=32, n_q_heads=32, n_kv_heads=8)
-    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 2048, 128) >= 32 * 2 * 8 * 2048 * 4
-    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 128) > 0
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 2048, 128) == 0
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 128) == 0
+    assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), 2048, 128, 128, None) == 0
+    # split units: global scores and attention partials
+    small = _shape(batch=1, n_q_heads=32, n_kv_heads=8)
+    assert lib.oasis_score_topk_workspace(ctypes.byref(small), 2048, 128) >= 2 * 8 * 2048 * 4
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(small), 128) >= 8 * 2 * 8 * 2 * 128 * 4
+    # forced splits at 256 units need scratch too
+    o = _lib.OasisStepOpts(2, 2, 0)
+    assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), 2048, 128, 128,
+                                              ctypes.byref(o)) >= 32 * 2 * 8 * 2048 * 4
+
+
+def _step(lib, s, **kw):
+    """oasis_lookahead_step with every pointer FAKE unless overridden."""
+    a = dict(q=FAKE, summ=FAKE, nb=8, n_blk=None, K=4, idx=FAKE, tsc=None, sc=None,
+             bi=FAKE, si=FAKE, bo=ctypes.c_void_p(0x9000), so=ctypes.c_void_p(0xA000), step=1,
+             cap=2, pred=1, cnt=FAKE, src=FAKE, dst=FAKE, ev=None, kt=FAKE, vt=FAKE,
+             tbl=ctypes.c_void_p(0x100000), n_sel=4, stride=8, tt=None, tl=None, scale=0.0,
+             out=FAKE, lse=None, opts=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib.oasis_lookahead_step(
+        ctypes.byref(s), a["q"], a["summ"], a["nb"], a["n_blk"], a["K"], a["idx"], a["tsc"],
+        a["sc"], a["bi"], a["si"], a["bo"], a["so"], a["step"], a["cap"], a["pred"], a["cnt"],
+        a["src"], a["dst"], a["ev"], a["kt"], a["vt"], a["tbl"], a["n_sel"], a["stride"],
+        a["tt"], a["tl"], a["scale"], a["out"], a["lse"], a["opts"], a["ws"], a["wsb"], None)
+
+
+def test_lookahead_step_validation(lib):
+    s = _shape()
+    E = _lib.OASIS_EINVAL
+    assert _step(lib, s, q=None) == E
+    assert _step(lib, s, pred=2) == E
+    assert _step(lib, s, cap=-1) == E
+    assert _step(lib, s, K=0) == E
+    assert _step(lib, s, K=1025) == E
+    assert _step(lib, s, n_sel=-1) == E
+    assert _step(lib, s, stride=-1) == E
+    assert _step(lib, s, tbl=None) == E
+    # new slot table overlapping the tile table the attention reads
+    assert _step(lib, s, bo=ctypes.c_void_p(0x100000 + 8)) == E
+    assert _step(lib, s, so=ctypes.c_void_p(0x100000 - 8)) == E
+    bad = _lib.OasisStepOpts(-1, 0, 0)
+    assert _step(lib, s, opts=ctypes.byref(bad)) == E
+    mf = _lib.OasisStepOpts(0, 0, 2)
+    assert _step(lib, _shape(dtype=0), opts=ctypes.byref(mf)) == _lib.OASIS_EUNSUPPORTED
+    assert _step(lib, _shape(head_dim=96)) == _lib.OASIS_EUNSUPPORTED
+    big = dict(nb=2048, K=64, n_sel=64)  # one request: split units need scratch
+    assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), 2048, 64, 64, None) > 0
+    assert _step(lib, s, wsb=0, **big) == _lib.OASIS_EWORKSPACE
+    assert _step(lib, s, ws=None, **big) == _lib.OASIS_EWORKSPACE
+    assert lib.oasis_lookahead_step_workspace(ctypes.byref(_shape(batch=0)), 8, 4, 4, None) == 0

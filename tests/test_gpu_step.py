@@ -1,0 +1,230 @@
+"""GPU parity of the fused layer-step (oasis_lookahead_step) against the CPU
+oracle, over chains of decode steps with double-buffered slot tables.
+
+Per step the fused call must give
+  - attention of both rows over the current resident set: within 1e-5 (fp32)
+    / 2e-2 (bf16) max-abs of the oracle;
+  - block scores within 1e-5 relative of the oracle's, and bitwise equal to
+    the standalone oasis_score_topk;
+  - top-K exactly the oracle's selection on the kernel's own fp32 scores;
+  - the plan and new slot tables bit-exact against the oracle's plan on the
+    kernel's top-K.
+Workgroup splits (scan chunks, attention splits) are swept through the
+options so the arrival-counter merges are exercised.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_kv_block_quest_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+ATTN_TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+SCORE_RTOL = 1e-5
+
+
+def np64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def score_scale(q64, summ64, G):
+    R, nq, Hq, D = q64.shape
+    H = Hq // G
+    amax = np.maximum(np.abs(summ64[:, :, :, 0]), np.abs(summ64[:, :, :, 1]))
+    qa = np.abs(q64).reshape(R, nq, H, G, D).sum(axis=3)
+    return np.einsum("rjhd,rhbd->rjhb", qa, amax)
+
+
+def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0):
+    """Seed the resident set, then run `steps` fused steps, checking each."""
+    qf = synth.queries(wl, cuda)
+    keys = synth.keys(wl, qf[:, 0], cuda)
+    vals = synth.values(wl, cuda)
+    vt = synth.v_tiles(vals, wl.B)
+    del vals
+    summ = ops.build_summaries(keys, wl.B)
+    kt = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
+    R, H, K = wl.R, wl.H, wl.K
+    dev = cuda
+    if tail and n_blk is None:
+        n_blk = [wl.n_blk - 1] * wl.R  # the active block is not scored
+    nbk = None if n_blk is None else torch.tensor(n_blk, dtype=torch.int32, device=dev)
+    n_valid = np.full(R, wl.n_blk, np.int32) if n_blk is None else np.array(n_blk, np.int32)
+    tt = tl = None
+    if tail:
+        # the active block: the last block of the store, `tail` valid tokens
+        tt = torch.full((R, H), wl.n_blk - 1, dtype=torch.int32, device=dev)
+        tl = torch.tensor([max(1, tail - (r % 3)) for r in range(R)], dtype=torch.int32, device=dev)
+    # seeding from row 0 of the first queries
+    q = qf.to(wl.dtype)
+    idx, _, _ = ops.score_topk(q, summ, K, n_blk=nbk)
+    slots = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    stamps = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    ops.select_plan(idx, slots[0], stamps[0], 0, wl.cap, pred_row=0)
+    gen = synth.generator(wl.seed + seed, synth.S_DRIFT, dev)
+    cur = qf
+    bufs = {}
+    if units is None:
+        units = [(r, g) for r in range(R) for g in range(H)]
+    for t in range(steps):
+        a, b = t % 2, 1 - t % 2
+        q = cur.to(wl.dtype)
+        say(f"  step {t}: opts={None if opts is None else (opts.scan_chunks, opts.attn_splits, opts.attn_impl)}")
+        res = ops.lookahead_step(q, summ, K, slots[a], stamps[a], slots[b], stamps[b], t + 1,
+                                 wl.cap, kt, vt, slots[a], wl.n_blk, wl.B, pred_row=1,
+                                 n_blk=nbk, tail_tile=tt, tail_len=tl, want_scores=True,
+                                 opts=opts, bufs=bufs)
+        torch.cuda.synchronize()
+        # standalone scan + top-K: identical fp32 scores and selection
+        i2, v2, s2 = ops.score_topk(q, summ, K, n_blk=nbk, want_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(res["scores"], s2)
+        assert torch.equal(res["topk_idx"], i2)
+        assert torch.equal(res["topk_score"], v2)
+        check_step(wl, q, summ, kt, vt, slots[a], stamps[a], slots[b], stamps[b], res, t + 1,
+                   n_valid, tt, tl, units)
+        cur = synth.drift(cur[:, 0], wl.rho, gen)
+    return res
+
+
+def check_step(wl, q, summ, kt, vt, blk_in, stamp_in, blk_out, stamp_out, res, step, n_valid,
+               tt, tl, units):
+    R, H, K, G = wl.R, wl.H, wl.K, wl.G
+    q64 = np64(q)
+    blk_in_np = blk_in.cpu().numpy()
+    # scores against the fp64 oracle, on the sampled units
+    sc = res["scores"].cpu().double().numpy()
+    for r, g in units:
+        s_sub = np64(summ[r:r + 1, g:g + 1])
+        qs = q64[r:r + 1, :, g * G:(g + 1) * G]
+        ref = oracle.block_scores(qs, s_sub, n_blk=n_valid[r:r + 1])
+        got = sc[r:r + 1, :, g:g + 1]
+        fin = np.isfinite(ref)
+        assert np.array_equal(np.isfinite(got), fin)
+        scale = score_scale(qs, s_sub, G)
+        err = np.abs(got[fin] - ref[fin])
+        assert np.all(err <= SCORE_RTOL * np.maximum(np.abs(ref[fin]), scale[fin]))
+    # top-K: the oracle's selection on the kernel's scores
+    i_ref, v_ref = oracle.topk(sc, K, n_blk=n_valid)
+    np.testing.assert_array_equal(res["topk_idx"].cpu().numpy(), i_ref)
+    np.testing.assert_array_equal(res["topk_score"].cpu().double().numpy(), v_ref)
+    # plan on the kernel's top-K
+    p_ref = oracle.select_plan(res["topk_idx"].cpu().numpy(), blk_in_np, stamp_in.cpu().numpy(),
+                               step, wl.cap, pred_row=1)
+    np.testing.assert_array_equal(blk_out.cpu().numpy(), p_ref["slot_block"])
+    np.testing.assert_array_equal(stamp_out.cpu().numpy(), p_ref["slot_stamp"])
+    for key in ("plan_count", "plan_src", "plan_dst", "plan_evicted"):
+        np.testing.assert_array_equal(res[key].cpu().numpy(), p_ref[key], err_msg=key)
+    # attention over the input resident set (sampled units)
+    D, B = wl.D, wl.B
+    for r, g in units:
+        sl = slice(g * G, (g + 1) * G)
+        k_u = np64(kt[r, g]).reshape(-1, B, D)
+        v_u = np64(synth.v_tiles_to_tokens(vt[r, g].reshape(-1, 1, D, B))).reshape(-1, B, D)
+        o_ref, l_ref = oracle.sparse_attn(
+            q64[r:r + 1, :, sl], k_u, v_u, blk_in_np[r:r + 1, g:g + 1], wl.n_blk,
+            None if tt is None else tt[r:r + 1, g:g + 1].cpu().numpy(),
+            None if tl is None else tl[r:r + 1].cpu().numpy())
+        out = np64(res["out"][r:r + 1, :, sl])
+        err = np.max(np.abs(out - o_ref))
+        assert err <= ATTN_TOL[wl.dtype], f"unit {(r, g)} attention err {err}"
+        lse = res["lse"][r:r + 1, :, sl].cpu().double().numpy()
+        fin = np.isfinite(l_ref)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.max(np.abs(lse[fin] - l_ref[fin]), initial=0.0) <= max(ATTN_TOL[wl.dtype], 1e-5)
+
+
+def small(name="tiny-fp32", **kw):
+    return synth.replace(synth.workload(name), **kw)
+
+
+@pytest.mark.parametrize("case", [
+    dict(wl=dict(), opts=None),
+    dict(wl=dict(), opts=(3, 2, 0)),
+    dict(wl=dict(L=1040), opts=(1, 1, 0), tail=7),
+])
+def test_step_tiny_fp32(cuda, case):
+    wl = small(**case["wl"])
+    o = None if case["opts"] is None else ops.step_opts(*case["opts"])
+    say(f"fused step tiny fp32 {case}")
+    run_chain(cuda, wl, 4, opts=o, tail=case.get("tail", 0))
+
+
+@pytest.mark.parametrize("G,D,B,L,K,nq_opts", [
+    (4, 128, 16, 4096, 32, (1, 1, 0)),
+    (4, 128, 16, 4096, 32, (4, 3, 0)),
+    (4, 128, 16, 4112, 32, (0, 0, 1)),   # VALU attention in the fused kernel
+    (16, 128, 16, 2048, 24, (2, 2, 0)),  # 32 rows: two MFMA row groups
+    (8, 64, 32, 2048, 16, (0, 0, 0)),
+    (4, 128, 8, 1024, 20, (2, 3, 0)),    # B < 16: VALU
+])
+def test_step_bf16(cuda, G, D, B, L, K, nq_opts):
+    wl = small("qwen3-8b-1layer", R=3, H=2, Hq=2 * G, D=D, B=B, L=L, K=K, cap=5)
+    say(f"fused step bf16 G={G} D={D} B={B} L={L} K={K} opts={nq_opts}")
+    run_chain(cuda, wl, 3, opts=ops.step_opts(*nq_opts), tail=5 if L % 64 else 0)
+
+
+def test_step_short_contexts(cuda):
+    """Requests with fewer full blocks than K, and an empty one."""
+    wl = small("qwen3-8b-1layer", R=3, H=2, Hq=8, L=1024, K=32, cap=4)
+    say("fused step short contexts")
+    run_chain(cuda, wl, 3, opts=ops.step_opts(2, 2, 0), n_blk=[64, 20, 0])
+
+
+@pytest.mark.parametrize("name,steps,units", [
+    ("qwen3-8b-1layer", 3, None),
+    ("llama3.1-8b-32layer", 2, [(0, 0), (13, 5), (31, 7)]),
+    ("qwen3-235b-1layer", 2, [(0, 1), (7, 3)]),
+])
+def test_step_full_size(cuda, name, steps, units):
+    """The benchmark's launch configuration (automatic splits) at full shape."""
+    wl = synth.workload(name, layers=1)
+    say(f"fused step full size {name}")
+    run_chain(cuda, wl, steps, units=units)
+
+
+def test_step_resident_layout(cuda):
+    """Resident store of K slots per head (unit_stride = K) read through an
+    identity tile table, the layout the pinned-host pipeline uses."""
+    wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=2048, K=16, cap=4)
+    say("fused step resident layout")
+    dev = cuda
+    qf = synth.queries(wl, dev)
+    keys = synth.keys(wl, qf[:, 0], dev)
+    vt_full = synth.v_tiles(synth.values(wl, dev), wl.B)
+    summ = ops.build_summaries(keys, wl.B)
+    kt_full = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
+    q = qf.to(wl.dtype)
+    R, H, K = wl.R, wl.H, wl.K
+    blk = torch.stack([torch.stack([torch.randperm(wl.n_blk, device=dev)[:K] for _ in range(H)])
+                       for _ in range(R)]).to(torch.int32)
+    stamp = torch.zeros_like(blk)
+    res_k = kt_full[torch.arange(R, device=dev)[:, None, None],
+                    torch.arange(H, device=dev)[None, :, None], blk.long()].contiguous()
+    res_v = vt_full[torch.arange(R, device=dev)[:, None, None],
+                    torch.arange(H, device=dev)[None, :, None], blk.long()].contiguous()
+    ident = torch.arange(K, dtype=torch.int32, device=dev).repeat(R, H, 1).contiguous()
+    bo, so = torch.empty_like(blk), torch.empty_like(stamp)
+    res = ops.lookahead_step(q, summ, K, blk, stamp, bo, so, 1, wl.cap, res_k, res_v, ident, K,
+                             wl.B, want_scores=True, opts=ops.step_opts(2, 2, 0))
+    torch.cuda.synchronize()
+    check_step(wl, q, summ, kt_full, vt_full, blk, stamp, bo, so, res, 1,
+               np.full(R, wl.n_blk, np.int32), None, None, [(r, g) for r in range(R) for g in range(H)])
+
+
+def test_step_rejects_aliased_slots(cuda):
+    wl = small("qwen3-8b-1layer", R=1, H=2, Hq=8, L=512, K=8)
+    dev = cuda
+    q = torch.zeros((1, 2, 8, wl.D), dtype=wl.dtype, device=dev)
+    summ = torch.zeros((1, 2, wl.n_blk, 2, wl.D), dtype=wl.dtype, device=dev)
+    kt = torch.zeros((1, 2, wl.n_blk, wl.B, wl.D), dtype=wl.dtype, device=dev)
+    blk = torch.zeros((1, 2, 8), dtype=torch.int32, device=dev)
+    st = torch.zeros_like(blk)
+    with pytest.raises(ops._lib.OasisError):
+        ops.lookahead_step(q, summ, 8, blk, st, blk, st, 1, 2, kt, kt, blk, wl.n_blk, wl.B)

@@ -56,6 +56,9 @@ def parse_args(argv=None):
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU work budget of the oracle baseline (0 = skip)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times and exit "
+                        "(the known-size reference for HBM byte counters)")
     return p.parse_args(argv)
 
 
@@ -90,7 +93,7 @@ def pmc_traffic(kernel_name, src_hash):
     if not os.path.exists(path):
         return None
     txt = open(path).read()
-    m = re.search(r"kernel sources sha256\[:16\]:\s*`?([0-9a-f]{16})", txt)
+    m = re.search(r"kernel sources sha256\[:16\]:\s*`?([0-9a-f]{16})", txt, re.I)
     if not m or m.group(1) != src_hash:
         return None
     m = re.search(rf"^\|\s*{re.escape(kernel_name)}\s*\|\s*([0-9.]+)\s*\|\s*([0-9.]+)\s*\|"
@@ -333,6 +336,15 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (liboasis.so runs only on gfx950)", file=sys.stderr)
         return 1
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return 0
     _lib.load()
     over = {}
     if args.batch:

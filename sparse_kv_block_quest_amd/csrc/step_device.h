@@ -174,13 +174,13 @@ __host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_sco
 
 // ============================================================ summary scan
 // Scores of blocks [c*chunk, (c+1)*chunk) of unit u for all NQ rows, written to
-// dst (row j at dst + j*drs; LDS or global) and, if dst2 is set, also to dst2.
+// dst (row j at dst + j*drs; LDS or global).
 // LPR lanes share one block: lane cl owns the 16-byte chunk cl of the min row
 // and of the max row.  The loop is software-pipelined: the next UNR blocks of
 // every lane group are in flight while the current ones are reduced.
 template <int DT, int D, int NQ>
 __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, float* pn, float* dst,
-                                            size_t drs, float* dst2, size_t drs2) {
+                                            size_t drs) {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int VEC = 16 / EB;
     constexpr int LPR = D / VEC;     // lanes per summary row
@@ -216,24 +216,18 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
     const int b_end = min(b_begin + a.chunk, a.n_blk_max);
     const int v_end = min(b_end, n_r);
     const uint4* base = reinterpret_cast<const uint4*>(a.summ) + (size_t)u * a.n_blk_max * 2 * LPR + cl;
+    // Every lane loads on every pass (blocks past the chunk are clamped into
+    // the unit's rows and their results discarded), so the number of loads
+    // in flight is the same on every path and the prefetch is never drained.
     auto load = [&](int b0, uint4 (&mn)[UNR], uint4 (&mx)[UNR]) {
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
-            const int b = b0 + k * BPP + lb;
-            if (b < v_end) {
-                mn[k] = base[(size_t)b * 2 * LPR];
-                mx[k] = base[(size_t)b * 2 * LPR + LPR];
-            } else {
-                mn[k] = make_uint4(0, 0, 0, 0);
-                mx[k] = make_uint4(0, 0, 0, 0);
-            }
+            const int b = min(b0 + k * BPP + lb, b_end - 1);
+            mn[k] = base[(size_t)b * 2 * LPR];
+            mx[k] = base[(size_t)b * 2 * LPR + LPR];
         }
     };
-    uint4 mn[UNR], mx[UNR];
-    load(b_begin, mn, mx);
-    for (int b0 = b_begin; b0 < b_end; b0 += BPP * UNR) {
-        uint4 mn2[UNR], mx2[UNR];
-        if (b0 + BPP * UNR < b_end) load(b0 + BPP * UNR, mn2, mx2);
+    auto process = [&](int b0, const uint4 (&mn)[UNR], const uint4 (&mx)[UNR]) {
         float acc[UNR][NQ];
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
@@ -263,19 +257,30 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
                 const int b = b0 + k * BPP + lb;
                 if (b < b_end) {
 #pragma unroll
-                    for (int j = 0; j < NQ; ++j) {
-                        const float v = b < v_end ? acc[k][j] : -__builtin_inff();
-                        dst[j * drs + b] = v;
-                        if (dst2) dst2[j * drs2 + b] = v;
-                    }
+                    for (int j = 0; j < NQ; ++j)
+                        dst[j * drs + b] = b < v_end ? acc[k][j] : -__builtin_inff();
                 }
             }
         }
-#pragma unroll
-        for (int k = 0; k < UNR; ++k) {
-            mn[k] = mn2[k];
-            mx[k] = mx2[k];
-        }
+    };
+    // Ping-pong over two register buffers (no copies of in-flight loads).
+    constexpr int STEP = BPP * UNR;
+    uint4 mnA[UNR], mxA[UNR], mnB[UNR], mxB[UNR];
+    load(b_begin, mnA, mxA);
+    int b0 = b_begin;
+    // sched_barrier keeps every load of the next buffer issued before the
+    // current buffer's arithmetic (the scheduler would otherwise interleave
+    // them and wait on the current buffer with part of the prefetch unsent).
+    while (b0 < b_end) {
+        load(b0 + STEP, mnB, mxB);  // past the chunk: re-reads its last block
+        __builtin_amdgcn_sched_barrier(0);
+        process(b0, mnA, mxA);
+        b0 += STEP;
+        if (b0 >= b_end) break;
+        load(b0 + STEP, mnA, mxA);
+        __builtin_amdgcn_sched_barrier(0);
+        process(b0, mnB, mxB);
+        b0 += STEP;
     }
 }
 
@@ -695,17 +700,22 @@ __device__ void scan_item(const StepArgs& a, int u, int c, unsigned char* lds) {
     float* gsc = a.scores ? a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max : nullptr;
     const size_t grs = (size_t)a.H * a.n_blk_max;
     if (a.NC > 1) {  // one chunk of a split unit: scores to global, selection later
-        scan_blocks<DT, D, NQ>(a, u, c, pn, gsc, grs, nullptr, 0);
+        scan_blocks<DT, D, NQ>(a, u, c, pn, gsc, grs);
         return;
     }
     if (a.do_plan) plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
     if (a.scores_lds) {
         float* lsc = cur.take<float>((size_t)NQ * a.n_blk_max);
-        scan_blocks<DT, D, NQ>(a, u, 0, pn, lsc, a.n_blk_max, gsc, grs);
+        scan_blocks<DT, D, NQ>(a, u, 0, pn, lsc, a.n_blk_max);
         lds_barrier();
+        if (gsc)  // the caller asked for every block score
+            for (int i = threadIdx.x; i < NQ * a.n_blk_max; i += kNT) {
+                const int j = i / a.n_blk_max, b = i - j * a.n_blk_max;
+                gsc[j * grs + b] = lsc[i];
+            }
         select_unit<NQ>(a, u, lsc, a.n_blk_max, T, Pl);
     } else {
-        scan_blocks<DT, D, NQ>(a, u, 0, pn, gsc, grs, nullptr, 0);
+        scan_blocks<DT, D, NQ>(a, u, 0, pn, gsc, grs);
         __syncthreads();
         select_unit<NQ>(a, u, gsc, grs, T, Pl);
     }
@@ -742,7 +752,7 @@ __host__ __device__ inline size_t attn_lds_bytes(int att, int NR, int D, int per
     auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
     size_t b = a16((size_t)per_split * 4) + a16(NR * 4) * 2 + a16((size_t)NR * D * 4);
     if (att == kAttnMfma) {
-        b += a16(3 * NR * 4) * 2 + a16((size_t)3 * NR * D * 4);
+        b += a16(3 * NR * 4) * 2 + a16((size_t)3 * NR * D * 4) + a16((size_t)4 * 16 * D * 2);
     } else {
         b += a16((size_t)kMaxRows * D * 4) + a16(16 * (D + 1) * 4) + a16((size_t)D * 17 * 4) +
              a16(kMaxRows * 16 * 4) + a16(kMaxRows * 4) * 3;
@@ -757,12 +767,19 @@ struct AttnFin {
 };
 
 // MFMA split (bf16, B % 16 == 0).  Per 16-token sub-tile:
-//   S^T[16 tok][16 rows] = K_sub[16][D] * Q^T  (v_mfma_f32_16x16x32_bf16; K rows
-//   go straight from HBM into the A operand, q stays in registers),
+//   S^T[16 tok][16 rows] = K_sub[16][D] * Q^T  (v_mfma_f32_16x16x32_bf16, q in
+//   registers),
 //   O^T[D][rows] += V^T * P^T                  (v_mfma_f32_16x16x16_bf16; the A
 //   operand is 4 consecutive tokens of one dim, contiguous in a [D][B] V tile).
-// The 4 waves take sub-tiles round robin and prefetch their next sub-tile
-// into registers while the current one is computed.  P is rounded to bf16.
+// The K operand wants 16 tokens x 16 bytes per instruction, i.e. 16 separate
+// 64-byte pieces of the tile; such loads stream ~30% slower than contiguous
+// ones on this part.  K is therefore loaded contiguously (lane i of load j
+// takes bytes [1024 j + 16 i, +16)) and passed through a per-wave LDS stage:
+// 16-byte chunk c of token t goes to slot 16 c + (t ^ c), which makes both the
+// contiguous writes (one token, 16 chunks) and the operand reads (one chunk,
+// 16 tokens) hit 16 distinct bank groups.
+// The 4 waves take sub-tiles round robin and keep their next two sub-tiles in
+// flight in registers while the current one is computed.  P is rounded to bf16.
 template <int D, int NRG>
 __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
                                const int* tbl) {
@@ -772,9 +789,11 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
     const int l16 = lane & 15, lg = lane >> 4;
     const int r = u / a.H, g = u - (u / a.H) * a.H;
     const int NR = a.NR, B = a.B;
+    constexpr int CPR = D * 2 / 16;  // 16-byte chunks per K row (KB loads of 1 KiB per sub-tile)
     float* lm = cur.take<float>(3 * NR);
     float* ll = cur.take<float>(3 * NR);
     float* la = cur.take<float>((size_t)3 * NR * D);
+    uint4* kst = cur.take<uint4>((size_t)4 * 16 * CPR) + (size_t)w * 16 * CPR;  // this wave's stage
 
     bf16x8_t qv[NRG][KB];
 #pragma unroll
@@ -805,91 +824,128 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
     const int n_sub = n_entry_sub + (sr.tail_len + 15) / 16;
     const size_t tile_elems = (size_t)B * D;
 
+    // Loads of sub-tile st (the table lives in LDS).  Every call issues the
+    // same loads whether or not st is a real sub-tile (a -1 entry, or past
+    // the end): then the compiler's count of loads in flight is exact and it
+    // waits only for the buffer being consumed, never for the prefetch.  A
+    // placeholder call reads one 16-byte piece of the unit's first tile.
     auto fetch = [&](int st, bf16x8_t (&kv)[KB], bf16x4_t (&vv)[DB]) -> int {
-        int tile, sub, ntok;
+        int tile = 0, sub = 0, ntok = 0;
         if (st < n_entry_sub) {
-            tile = tbl[st / spe];
-            sub = st - (st / spe) * spe;
-            ntok = 16;
-            if (tile < 0) return 0;
-        } else {
+            const int e = st / spe;
+            tile = tbl[e];
+            sub = st - e * spe;
+            ntok = tile >= 0 ? 16 : 0;
+        } else if (st < n_sub) {
             tile = sr.tail_tile;
             sub = st - n_entry_sub;
             ntok = min(16, sr.tail_len - sub * 16);
         }
-        const size_t t64 = (size_t)((long long)u * a.unit_stride + tile);
-        const uint8_t* kbase = a.kt + (t64 * tile_elems + (size_t)sub * 16 * D) * 2;
-        const uint8_t* vbase = a.vt + (t64 * tile_elems + (size_t)sub * 16) * 2;
+        const bool real = ntok > 0;
+        const size_t t64 = (size_t)((long long)u * a.unit_stride + (real ? tile : 0));
+        const uint8_t* kbase = a.kt + (t64 * tile_elems + (real ? (size_t)sub * 16 * D : 0)) * 2;
+        const uint8_t* vbase = a.vt + (t64 * tile_elems + (real ? (size_t)sub * 16 : 0)) * 2;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            kv[kb] = *reinterpret_cast<const bf16x8_t*>(kbase + ((size_t)l16 * D + kb * 32 + lg * 8) * 2);
+        for (int j = 0; j < KB; ++j)
+            kv[j] = *reinterpret_cast<const bf16x8_t*>(kbase + (real ? ((size_t)j * 64 + lane) * 16 : 0));
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            vv[db] = *reinterpret_cast<const bf16x4_t*>(vbase + ((size_t)(db * 16 + l16) * B + lg * 4) * 2);
+            vv[db] = *reinterpret_cast<const bf16x4_t*>(
+                vbase + (real ? ((size_t)(db * 16 + l16) * B + lg * 4) * 2 : 0));
         return ntok;
     };
 
-    bf16x8_t kc[KB];
-    bf16x4_t vc[DB];
-    int st = w;
-    int ntok = st < n_sub ? fetch(st, kc, vc) : 0;
-    while (st < n_sub) {
-        const int nx = st + 4;
-        bf16x8_t kn[KB];
-        bf16x4_t vn[DB];
-        const int ntok_n = nx < n_sub ? fetch(nx, kn, vn) : 0;
-        if (ntok > 0) {
-            if (ntok < 16) {
+    // One 16-token sub-tile: stage K, S = K q^T, online softmax, O += V^T P^T.
+    auto compute = [&](const bf16x8_t (&kc)[KB], bf16x4_t (&vc)[DB], int ntok) {
+        if (ntok < 16) {
 #pragma unroll
-                for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (lg * 4 + e >= ntok) vc[db][e] = 0;
-            }
+                for (int e = 0; e < 4; ++e)
+                    if (lg * 4 + e >= ntok) vc[db][e] = 0;
+        }
+        // Contiguous K chunks -> swizzled stage -> MFMA operand layout.
 #pragma unroll
-            for (int rg = 0; rg < NRG; ++rg) {
-                f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < KB; ++jj) {
+            const int t = jj * (64 / CPR) + lane / CPR, c = lane % CPR;
+            kst[c * 16 + (t ^ (c & 15))] = *reinterpret_cast<const uint4*>(&kc[jj]);
+        }
+        bf16x8_t kop[KB];
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kc[kb], qv[rg][kb], s, 0, 0, 0);
-                float tmax = -__builtin_inff();
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    s[e] = (lg * 4 + e < ntok) ? s[e] * a.scale_log2 : -__builtin_inff();
-                    tmax = fmaxf(tmax, s[e]);
-                }
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-                const float mnew = fmaxf(m[rg], tmax);
-                const float corr = exp2f(m[rg] - mnew);
-                float p[4];
-                float psum = 0.f;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    p[e] = exp2f(s[e] - mnew);
-                    psum += p[e];
-                }
-                lsum[rg] = lsum[rg] * corr + psum;
-                m[rg] = mnew;
-                bf16x4_t pb;
-                pb[0] = (short)f32_to_bf16_bits(p[0]);
-                pb[1] = (short)f32_to_bf16_bits(p[1]);
-                pb[2] = (short)f32_to_bf16_bits(p[2]);
-                pb[3] = (short)f32_to_bf16_bits(p[3]);
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    acc[rg][db] *= corr;
-                    acc[rg][db] =
-                        __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vc[db], pb, acc[rg][db], 0, 0, 0);
-                }
-            }
+        for (int kb = 0; kb < KB; ++kb) {
+            const int c = kb * 4 + lg;
+            const uint4 x = kst[c * 16 + (l16 ^ (c & 15))];
+            kop[kb] = *reinterpret_cast<const bf16x8_t*>(&x);
         }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kc[kb] = kn[kb];
+        for (int rg = 0; rg < NRG; ++rg) {
+            f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vc[db] = vn[db];
-        ntok = ntok_n;
-        st = nx;
+            for (int kb = 0; kb < KB; ++kb)
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kb], qv[rg][kb], sc, 0, 0, 0);
+            // sc[e] = score of token lg*4+e for row l16.
+            float tmax = -__builtin_inff();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sc[e] = (lg * 4 + e < ntok) ? sc[e] * a.scale_log2 : -__builtin_inff();
+                tmax = fmaxf(tmax, sc[e]);
+            }
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            const float mnew = fmaxf(m[rg], tmax);
+            // A row that has seen no token yet keeps m = -inf: weight 0, no NaN.
+            const bool none = mnew == -__builtin_inff();
+            const float corr = none ? 1.f : exp2f(m[rg] - mnew);
+            float p[4];
+            float psum = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                p[e] = none ? 0.f : exp2f(sc[e] - mnew);
+                psum += p[e];
+            }
+            lsum[rg] = lsum[rg] * corr + psum;
+            m[rg] = mnew;
+            bf16x4_t pb;
+            pb[0] = (short)f32_to_bf16_bits(p[0]);
+            pb[1] = (short)f32_to_bf16_bits(p[1]);
+            pb[2] = (short)f32_to_bf16_bits(p[2]);
+            pb[3] = (short)f32_to_bf16_bits(p[3]);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                acc[rg][db] *= corr;
+                acc[rg][db] =
+                    __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vc[db], pb, acc[rg][db], 0, 0, 0);
+            }
+        }
+    };
+    // Three register buffers in rotation (unrolled, so no buffer is ever
+    // copied): two sub-tiles of this wave are in flight while the third is
+    // computed.  Copying a prefetched buffer into a "current" one would make
+    // the wave wait for the prefetch at every step; compute() runs for
+    // placeholder sub-tiles too (ntok = 0 masks every token), so no path
+    // leaves a buffer's loads unconsumed.  sched_barrier keeps each buffer's
+    // loads issued before the arithmetic on the previous one.
+    bf16x8_t kA[KB], kB[KB], kC[KB];
+    bf16x4_t vA[DB], vB[DB], vC[DB];
+    int st = w;
+    int nA = fetch(st, kA, vA);
+    int nB = fetch(st + 4, kB, vB);
+    int nC = 0;
+    while (st < n_sub) {
+        nC = fetch(st + 8, kC, vC);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kA, vA, nA);
+        st += 4;
+        if (st >= n_sub) break;
+        nA = fetch(st + 8, kA, vA);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kB, vB, nB);
+        st += 4;
+        if (st >= n_sub) break;
+        nB = fetch(st + 8, kB, vB);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kC, vC, nC);
+        st += 4;
     }
     // Row sums: the 4 lane groups hold disjoint tokens of the same rows.
 #pragma unroll

@@ -51,6 +51,8 @@ def parse_args(argv=None):
     p.add_argument("--path", choices=("fused", "unfused"), default="fused",
                    help="fused: one oasis_lookahead_step launch per layer-step; unfused: "
                         "oasis_sparse_attn + oasis_score_topk + oasis_select_plan")
+    p.add_argument("--kv-layout", choices=("interleaved", "split"), default="interleaved",
+                   help="one K|V record per block-head, or separate K and V stores")
     p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
     p.add_argument("--attn-splits", type=int, default=0, help="fused path: 0 = automatic")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -104,7 +106,9 @@ def pmc_traffic(kernel_name, src_hash):
 
 
 # ----------------------------------------------------------------- GPU leg
-def setup_layers(wl, dev, n_layers, torch, synth, ops):
+def setup_layers(wl, dev, n_layers, interleaved, torch, synth, ops):
+    """Per layer: the KV store (interleaved K|V records, or separate K and V
+    stores), its summaries and the first queries."""
     layers = []
     t_summ = []
     for l in range(n_layers):
@@ -113,14 +117,17 @@ def setup_layers(wl, dev, n_layers, torch, synth, ops):
         vals = synth.values(wl, dev, layer=l)
         vt = synth.v_tiles(vals, wl.B)
         del vals
+        kt = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
+        if interleaved:
+            _, kt, vt = synth.interleave_kv(kt, vt)
+            del keys
         summ = torch.empty((wl.R, wl.H, wl.n_blk, 2, wl.D), dtype=wl.dtype, device=dev)
-        ops.build_summaries(keys, wl.B, out=summ)  # warm
+        ops.build_summaries(kt, wl.B, out=summ)  # warm
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        ops.build_summaries(keys, wl.B, out=summ)
+        ops.build_summaries(kt, wl.B, out=summ)
         e1.record()
-        layers.append({"keys": keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D), "vt": vt,
-                       "summ": summ, "q0": qf})
+        layers.append({"keys": kt, "vt": vt, "summ": summ, "q0": qf})
         t_summ.append((e0, e1))
         if (l + 1) % 8 == 0 or l + 1 == n_layers:
             print(f"# layer {l + 1}/{n_layers} generated", file=sys.stderr, flush=True)
@@ -145,7 +152,8 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     dev = torch.device("cuda:0")
     n_layers = wl.layers
     impl = {"auto": ops.IMPL_AUTO, "valu": ops.IMPL_VALU, "mfma": ops.IMPL_MFMA}[args.impl]
-    layers, summ_ms = setup_layers(wl, dev, n_layers, torch, synth, ops)
+    layers, summ_ms = setup_layers(wl, dev, n_layers, args.kv_layout == "interleaved", torch,
+                                   synth, ops)
     T = args.warmup + args.steps + 1
     qseq = query_sequence(wl, dev, n_layers, T, torch, synth)
 
@@ -411,7 +419,8 @@ def main(argv=None):
                                f"{wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}",
                    "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
                    "budget_tokens": wl.K * wl.B, "layers": wl.layers, "cap": wl.cap,
-                   "stacked_queries": wl.n_q, "impl": args.impl, "path": args.path},
+                   "stacked_queries": wl.n_q, "impl": args.impl, "path": args.path,
+                   "kv_layout": args.kv_layout},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -36,7 +36,8 @@
  *    pair with index u = r*H + g.
  *  - Tiles: a K tile holds the B keys of one block of one KV head, token-major
  *    [B][D].  A V tile holds the same block's values DIM-major [D][B] (value
- *    of token i, dim d at d*B + i).  Tile ids are 64-bit element offsets / (B*D).
+ *    of token i, dim d at d*B + i).  Tile t of a store starts t * tile_stride
+ *    elements after the store's base (oasis_shape.tile_stride; B*D when 0).
  */
 #ifndef OASIS_H
 #define OASIS_H
@@ -59,13 +60,18 @@ extern "C" {
 typedef enum { OASIS_F32 = 0, OASIS_BF16 = 1 } oasis_dtype;
 
 typedef struct oasis_shape {
-    int32_t batch;      /* R >= 1 */
-    int32_t n_q;        /* stacked query rows, 1 or 2 */
-    int32_t n_q_heads;  /* Hq >= 1, multiple of n_kv_heads */
-    int32_t n_kv_heads; /* H >= 1 */
-    int32_t head_dim;   /* D: 64 or 128 */
-    int32_t block_size; /* B: power of two, 1..64 (16 in every measured workload) */
-    int32_t dtype;      /* oasis_dtype */
+    int32_t batch;       /* R >= 1 */
+    int32_t n_q;         /* stacked query rows, 1 or 2 */
+    int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads;  /* H >= 1 */
+    int32_t head_dim;    /* D: 64 or 128 */
+    int32_t block_size;  /* B: power of two, 1..64 (16 in every measured workload) */
+    int32_t dtype;       /* oasis_dtype */
+    int64_t tile_stride; /* elements from one K (or V) tile to the next in a tile store;
+                            0 = B*D (dense).  2*B*D with v = k + B*D interleaves each
+                            block-head's K and V tiles into one 2*B*D-element record, which
+                            the attention gathers as one contiguous piece.  Otherwise
+                            >= B*D and a multiple of 16 bytes. */
 } oasis_shape;
 
 /* Human-readable text of a status code.  Never NULL; static storage. */
@@ -84,7 +90,8 @@ int oasis_version(void);
  * min/max pooling); [v2] §4.1 (two summary rows per 16-token block, 1/16 of
  * the KV cache).
  *   s          shape; uses batch, n_kv_heads, head_dim, block_size, dtype
- *   keys       [R][H][n_blk_max][B][D] (dtype): the full key store of the layer
+ *   keys       K tile store of the layer, tile (u*n_blk_max + b) = block b of
+ *              unit u, [B][D] (dtype), tiles tile_stride apart
  *   n_blk_max  blocks per unit in `keys` and `summaries`
  *   seq_len    [R] int32 context lengths, or NULL = n_blk_max*B for every
  *              request; each must be in [0, n_blk_max*B]
@@ -187,9 +194,10 @@ int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t pr
  * per-head entries from pinned host memory over PCIe and writes them into
  * HBM) and §4.1 Implementation.  Run it on a background stream ordered after
  * the attention that last read the destination slots.
- *   src_k, src_v  [R][H][n_blk_max] tiles; device memory or pinned host
- *                 memory the GPU can address (hipHostMalloc / pinned torch)
- *   res_k, res_v  [R][H][top_k] tiles in device memory
+ *   src_k, src_v  [R][H][n_blk_max] tiles (tile_stride apart); device memory or
+ *                 pinned host memory the GPU can address (hipHostMalloc / pinned
+ *                 torch)
+ *   res_k, res_v  [R][H][top_k] tiles in device memory, same tile_stride
  *   plan_*        as written by oasis_select_plan (device memory)
  * Errors: EINVAL, EUNSUPPORTED, EHIP.
  */

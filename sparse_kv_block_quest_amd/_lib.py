@@ -50,6 +50,7 @@ class OasisShape(ctypes.Structure):
         ("head_dim", ctypes.c_int32),
         ("block_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("tile_stride", ctypes.c_int64),
     ]
 
 

@@ -17,15 +17,15 @@ namespace oasis {
 __global__ void __launch_bounds__(256)
 copy_blocks_kernel(const uint4* __restrict__ src_k, const uint4* __restrict__ src_v,
                    uint4* __restrict__ res_k, uint4* __restrict__ res_v, int H, int n_blk_max,
-                   int K, int tile_u4, const int32_t* __restrict__ plan_count,
+                   int K, int tile_u4, long long stride_u4, const int32_t* __restrict__ plan_count,
                    const int32_t* __restrict__ plan_src, const int32_t* __restrict__ plan_dst) {
     const int i = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
     const size_t u = (size_t)r * H + g;
     if (i >= plan_count[u]) return;
     const int src = plan_src[u * K + i];
     const int dst = plan_dst[u * K + i];
-    const size_t so = (u * n_blk_max + src) * (size_t)tile_u4;
-    const size_t d_o = (u * K + dst) * (size_t)tile_u4;
+    const size_t so = (u * n_blk_max + src) * (size_t)stride_u4;
+    const size_t d_o = (u * K + dst) * (size_t)stride_u4;
     for (int t = threadIdx.x; t < tile_u4; t += 256) {
         const uint4 a = src_k[so + t];
         const uint4 b = src_v[so + t];
@@ -83,7 +83,9 @@ extern "C" int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const 
                        stream, reinterpret_cast<const uint4*>(dk),
                        reinterpret_cast<const uint4*>(dv), reinterpret_cast<uint4*>(res_k),
                        reinterpret_cast<uint4*>(res_v), s->n_kv_heads, n_blk_max, top_k,
-                       int(tile_bytes / 16), plan_count, plan_src, plan_dst);
+                       int(tile_bytes / 16),
+                       tile_stride_of(s) * (s->dtype == OASIS_F32 ? 4 : 2) / 16, plan_count,
+                       plan_src, plan_dst);
     return launch_status();
 }
 

@@ -111,7 +111,17 @@ inline int check_shape(const oasis_shape* s) {
     if (s->dtype != OASIS_F32 && s->dtype != OASIS_BF16) return OASIS_EUNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return OASIS_EUNSUPPORTED;
     if (!is_pow2(s->block_size) || s->block_size > 64) return OASIS_EUNSUPPORTED;
+    if (s->tile_stride != 0) {
+        const long long eb = s->dtype == OASIS_F32 ? 4 : 2;
+        if (s->tile_stride < (long long)s->block_size * s->head_dim || (s->tile_stride * eb) % 16)
+            return OASIS_EINVAL;
+    }
     return OASIS_OK;
+}
+
+// Elements from one tile of a K / V store to the next.
+inline long long tile_stride_of(const oasis_shape* s) {
+    return s->tile_stride ? s->tile_stride : (long long)s->block_size * s->head_dim;
 }
 
 inline int launch_status() {

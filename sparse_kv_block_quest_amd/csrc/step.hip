@@ -214,6 +214,7 @@ static void fill_attn(StepArgs& a, const oasis_shape* s, const void* q, const vo
     a.table = tile_table;
     a.n_sel = n_sel;
     a.unit_stride = unit_stride;
+    a.tile_stride = tile_stride_of(s);
     a.tail_tile = tail_tile;
     a.tail_len = tail_len;
     const float sc = scale > 0.f ? scale : 1.f / sqrtf((float)s->head_dim);

@@ -83,6 +83,7 @@ struct StepArgs {
     const int32_t* table;  // [U][n_sel]
     int n_sel;
     long long unit_stride;
+    long long tile_stride;  // elements between consecutive tiles of the K / V stores
     const int32_t* tail_tile;  // [U] or null
     const int32_t* tail_len;   // [R] or null
     float scale_log2;
@@ -822,7 +823,7 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
     const int spe = B / 16;
     const int n_entry_sub = (sr.e1 - sr.e0) * spe;
     const int n_sub = n_entry_sub + (sr.tail_len + 15) / 16;
-    const size_t tile_elems = (size_t)B * D;
+    const size_t tile_elems = (size_t)a.tile_stride;
 
     // Loads of sub-tile st (the table lives in LDS).  Every call issues the
     // same loads whether or not st is a real sub-tile (a -1 entry, or past
@@ -1048,7 +1049,7 @@ __device__ void attn_item_valu(const StepArgs& a, int u, int sp, LdsCursor& cur,
     const int spe = B / sub_tokens;
     const int n_entry_sub = (sr.e1 - sr.e0) * spe;
     const int n_sub = n_entry_sub + (sr.tail_len + sub_tokens - 1) / sub_tokens;
-    const size_t tile_elems = (size_t)B * D;
+    const size_t tile_elems = (size_t)a.tile_stride;
     for (int st = 0; st < n_sub; ++st) {
         int tile, sub, nt;
         if (st < n_entry_sub) {

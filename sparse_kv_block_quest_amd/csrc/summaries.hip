@@ -5,7 +5,8 @@
 // logical block); metallab.ai summary, Fig. 7 caption (per-block min/max
 // pooling); paperpeel v2 text, §4.1 (two summary rows per 16-token block).
 //
-// Mapping: a block's B key rows are D*e bytes each.  LPR = D*e/16 lanes share
+// Mapping: a block's B key rows are D*e bytes each (one K tile; tiles are
+// tile_stride elements apart in the store).  LPR = D*e/16 lanes share
 // one block; lane c owns the 16-byte column chunk c of every row, walks the B
 // rows with 16-byte loads (one coalesced D*e-byte segment per row per lane
 // group) and writes its chunk of the min row and of the max row.  Min/max of
@@ -20,7 +21,7 @@ template <int DT, int D, int B>
 __global__ void __launch_bounds__(256)
 build_summaries_kernel(const uint8_t* __restrict__ keys, uint8_t* __restrict__ summ,
                        const int32_t* __restrict__ seq_len, int H, int n_blk_max,
-                       int blk_begin, int n_range, long long total_lanes) {
+                       int blk_begin, int n_range, long long total_lanes, long long tile_u4) {
     constexpr int EB = Elem<DT>::bytes;
     constexpr int VEC = 16 / EB;
     constexpr int LPR = D / VEC;           // lanes per block
@@ -35,8 +36,7 @@ build_summaries_kernel(const uint8_t* __restrict__ keys, uint8_t* __restrict__ s
     const int n_full = seq_len ? seq_len[r] / B : n_blk_max;
     if (b >= n_full) return;
 
-    const uint4* src = reinterpret_cast<const uint4*>(keys) +
-                       ((unit * n_blk_max + b) * (long long)B) * ROW_U4 + c;
+    const uint4* src = reinterpret_cast<const uint4*>(keys) + (unit * n_blk_max + b) * tile_u4 + c;
     float lo[VEC], hi[VEC];
     {
         float v[VEC];
@@ -69,14 +69,14 @@ build_summaries_kernel(const uint8_t* __restrict__ keys, uint8_t* __restrict__ s
 template <int DT, int D>
 static void launch_summaries_d(int B, const void* keys, void* summ, const int32_t* seq_len,
                                int H, int n_blk_max, int blk_begin, int n_range,
-                               long long total_lanes, hipStream_t st) {
+                               long long total_lanes, long long tile_u4, hipStream_t st) {
     dim3 grid((unsigned)((total_lanes + 255) / 256));
     auto k8 = reinterpret_cast<const uint8_t*>(keys);
     auto s8 = reinterpret_cast<uint8_t*>(summ);
 #define OASIS_SUMM_CASE(BB)                                                                   \
     case BB:                                                                                  \
         hipLaunchKernelGGL((build_summaries_kernel<DT, D, BB>), grid, dim3(256), 0, st, k8, s8, \
-                           seq_len, H, n_blk_max, blk_begin, n_range, total_lanes);           \
+                           seq_len, H, n_blk_max, blk_begin, n_range, total_lanes, tile_u4); \
         break;
     switch (B) {
         OASIS_SUMM_CASE(1)
@@ -110,20 +110,21 @@ extern "C" int oasis_build_summaries(const oasis_shape* s, const void* keys, int
     const int lpr = D * (s->dtype == OASIS_F32 ? 4 : 2) / 16;
     const long long total = (long long)s->batch * s->n_kv_heads * n_range * lpr;
     const int H = s->n_kv_heads, B = s->block_size;
+    const long long tu4 = tile_stride_of(s) * (s->dtype == OASIS_F32 ? 4 : 2) / 16;
     if (s->dtype == OASIS_F32) {
         if (D == 64)
             launch_summaries_d<OASIS_F32, 64>(B, keys, summaries, seq_len, H, n_blk_max,
-                                              blk_begin, n_range, total, stream);
+                                              blk_begin, n_range, total, tu4, stream);
         else
             launch_summaries_d<OASIS_F32, 128>(B, keys, summaries, seq_len, H, n_blk_max,
-                                               blk_begin, n_range, total, stream);
+                                               blk_begin, n_range, total, tu4, stream);
     } else {
         if (D == 64)
             launch_summaries_d<OASIS_BF16, 64>(B, keys, summaries, seq_len, H, n_blk_max,
-                                               blk_begin, n_range, total, stream);
+                                               blk_begin, n_range, total, tu4, stream);
         else
             launch_summaries_d<OASIS_BF16, 128>(B, keys, summaries, seq_len, H, n_blk_max,
-                                                blk_begin, n_range, total, stream);
+                                                blk_begin, n_range, total, tu4, stream);
     }
     return launch_status();
 }

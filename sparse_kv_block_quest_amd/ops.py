@@ -53,32 +53,91 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _shape(R, n_q, Hq, H, D, B, dtype) -> OasisShape:
-    return OasisShape(int(R), int(n_q), int(Hq), int(H), int(D), int(B), int(dtype))
+def _shape(R, n_q, Hq, H, D, B, dtype, tile_stride=0) -> OasisShape:
+    return OasisShape(int(R), int(n_q), int(Hq), int(H), int(D), int(B), int(dtype),
+                      int(tile_stride))
+
+
+def _tile_store(t: torch.Tensor, name: str, tile: int) -> tuple[int, int]:
+    """Pointer and tile stride (elements) of a store of ``tile``-element tiles: the
+    trailing dims that make up one tile must be dense, and the leading dims must
+    step by one uniform tile stride (a dense store such as [..][L][D] or
+    [..][n][B][D], or the K or V half of an interleaved store)."""
+    dims = list(zip(t.shape, t.stride()))
+    inner = 1
+    while dims and inner < tile:
+        n, st = dims.pop()
+        if n > 1 and st != inner:
+            raise ValueError(f"{name}: tiles must be dense")
+        if inner * n > tile:
+            # this dim spans several tiles (e.g. L of [..][L][D]): split it
+            part = tile // inner
+            if tile % inner or n % part:
+                break
+            dims.append((n // part, st * part))
+            n = part
+        inner *= n
+    if inner != tile:
+        raise ValueError(f"{name}: trailing dims do not split into {tile}-element tiles")
+    step, span = None, 1
+    for n, st in reversed(dims):
+        if n > 1:
+            if step is None:
+                step = st
+            elif st != step * span:
+                raise ValueError(f"{name}: leading dims must step by one tile stride")
+        span *= n
+    step = tile if step is None else step
+    if step < tile:
+        raise ValueError(f"{name}: tiles overlap")
+    return t.data_ptr(), int(step)
+
+
+def interleaved_kv(kv: torch.Tensor) -> tuple[torch.Tensor, torch.Tensor]:
+    """K and V tile views of an interleaved store kv [..][n][2][B][D]: block-head
+    (.., n) keeps its K tile ([B][D], token-major) and V tile ([D][B], dim-major)
+    side by side as one contiguous 2*B*D record.  The views are [..][n][B][D]
+    and [..][n][D][B]."""
+    if kv.dim() < 3 or kv.shape[-3] != 2:
+        raise ValueError("interleaved store must be [..][n][2][B][D]")
+    if not kv.is_contiguous():
+        raise ValueError("interleaved store must be contiguous")
+    B, D = kv.shape[-2:]
+    flat = kv.view(*kv.shape[:-3], 2, B * D)
+    return kv[..., 0, :, :], flat[..., 1, :].unflatten(-1, (D, B))
 
 
 def build_summaries(keys: torch.Tensor, block_size: int, seq_len: torch.Tensor | None = None,
                     blk_begin: int = 0, blk_end: int | None = None,
                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """keys [R][H][L_max][D] -> summaries [R][H][L_max/B][2][D] (0 = min, 1 = max)."""
+    """keys [R][H][L_max][D], or a K tile store [R][H][n][B][D] (dense or the K half
+    of an interleaved store) -> summaries [R][H][n][2][D] (0 = min, 1 = max)."""
     lib = _lib.load()
-    if keys.dim() == 5:
-        keys = keys.flatten(2, 3)
-    R, H, Lmax, D = keys.shape
     B = int(block_size)
-    if Lmax % B:
-        raise ValueError("L_max must be a multiple of block_size")
-    nb = Lmax // B
+    if keys.dim() == 4:
+        R, H, Lmax, D = keys.shape
+        if Lmax % B:
+            raise ValueError("L_max must be a multiple of block_size")
+        nb = Lmax // B
+    elif keys.dim() == 5:
+        R, H, nb, B2, D = keys.shape
+        if B2 != B:
+            raise ValueError("key tiles do not match block_size")
+    else:
+        raise ValueError("keys must be [R][H][L_max][D] or [R][H][n][B][D]")
+    kptr, ts = _tile_store(keys, "keys", B * D)
     if out is None:
         out = torch.zeros((R, H, nb, 2, D), dtype=keys.dtype, device=keys.device)
     if out.shape != (R, H, nb, 2, D) or out.dtype != keys.dtype:
         raise ValueError("summaries buffer has the wrong shape or dtype")
     if seq_len is not None:
         _i32(seq_len, "seq_len")
-    shp = _shape(R, 1, H, H, D, B, _dt(keys))
+    shp = _shape(R, 1, H, H, D, B, _dt(keys), ts)
     end = nb if blk_end is None else int(blk_end)
+    if not keys.is_cuda:
+        raise ValueError("keys must live on the GPU")
     check("oasis_build_summaries",
-          lib.oasis_build_summaries(ctypes.byref(shp), _ptr(keys), nb, _ptr(seq_len),
+          lib.oasis_build_summaries(ctypes.byref(shp), ctypes.c_void_p(kptr), nb, _ptr(seq_len),
                                     int(blk_begin), end, _ptr(out), _stream(stream)))
     return out
 
@@ -149,25 +208,40 @@ def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: to
 
 def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
                 res_v: torch.Tensor, plan: dict, block_size: int, stream=None) -> None:
-    """src_* [R][H][n_blk_max][tile] (device or pinned host), res_* [R][H][K][tile] (device),
-    where a tile is B*D elements (K tiles [B][D], V tiles [D][B])."""
+    """src_* [R][H][n_blk_max][..tile..] (device or pinned host), res_* [R][H][K][..tile..]
+    (device); K tiles [B][D], V tiles [D][B]; dense or interleaved, one shared tile stride."""
     lib = _lib.load()
+    if any(t.dim() < 4 for t in (src_k, src_v, res_k, res_v)):
+        raise ValueError("tile stores must be [R][H][n][..tile..]")
     R, H, nb = src_k.shape[:3]
     K = res_k.shape[2]
-    tile = src_k[0, 0, 0].numel()
     B = int(block_size)
+    tile = src_k[0, 0, 0].numel()
     D = tile // B
+    if D * B != tile:
+        raise ValueError("tile size is not a multiple of block_size")
     if src_v.shape[:3] != src_k.shape[:3] or res_v.shape[:3] != res_k.shape[:3] or \
             res_k.shape[:2] != (R, H):
         raise ValueError("store shapes do not match")
     for t in (src_v, res_k, res_v):
         if t[0, 0, 0].numel() != tile or t.dtype != src_k.dtype:
             raise ValueError("tile size or dtype mismatch")
-    shp = _shape(R, 1, H, H, D, B, _dt(src_k))
+    for t in (src_k, src_v):
+        if not t.is_cuda and not t.is_pinned():
+            raise ValueError("source store must be device memory or pinned host memory")
+    for t in (res_k, res_v):
+        if not t.is_cuda:
+            raise ValueError("resident store must live on the GPU")
+    ptrs, strides = zip(*(_tile_store(t, n, tile) for t, n in
+                          ((src_k, "src_k"), (src_v, "src_v"), (res_k, "res_k"), (res_v, "res_v"))))
+    if len(set(strides)) != 1:
+        raise ValueError("all four stores must share one tile stride")
+    shp = _shape(R, 1, H, H, D, B, _dt(src_k), strides[0])
+    cp = [ctypes.c_void_p(x) for x in ptrs]
     check("oasis_copy_blocks",
-          lib.oasis_copy_blocks(ctypes.byref(shp), _host_or_dev_ptr(src_k), _host_or_dev_ptr(src_v),
-                                nb, _ptr(res_k), _ptr(res_v), K, _ptr(plan["plan_count"]),
-                                _ptr(plan["plan_src"]), _ptr(plan["plan_dst"]), _stream(stream)))
+          lib.oasis_copy_blocks(ctypes.byref(shp), cp[0], cp[1], nb, cp[2], cp[3], K,
+                                _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
+                                _ptr(plan["plan_dst"]), _stream(stream)))
 
 
 def sparse_attn_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_sel: int,
@@ -193,7 +267,13 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
     if k_tiles.dtype != q.dtype or v_tiles.dtype != q.dtype:
         raise ValueError("q, k_tiles and v_tiles must share a dtype")
     B = int(block_size)
-    shp = _shape(R, n_q, Hq, H, D, B, _dt(q))
+    kptr, ks = _tile_store(k_tiles, "k_tiles", B * D)
+    vptr, vs = _tile_store(v_tiles, "v_tiles", B * D)
+    if ks != vs:
+        raise ValueError("k_tiles and v_tiles must share one tile stride")
+    if not (k_tiles.is_cuda and v_tiles.is_cuda):
+        raise ValueError("tile stores must live on the GPU")
+    shp = _shape(R, n_q, Hq, H, D, B, _dt(q), ks)
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
@@ -206,7 +286,8 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
         if t is not None:
             _i32(t, n)
     check("oasis_sparse_attn_impl",
-          lib.oasis_sparse_attn_impl(ctypes.byref(shp), _ptr(q), _ptr(k_tiles), _ptr(v_tiles),
+          lib.oasis_sparse_attn_impl(ctypes.byref(shp), _ptr(q), ctypes.c_void_p(kptr),
+                                     ctypes.c_void_p(vptr),
                                      _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile),
                                      _ptr(tail_len), float(scale), _ptr(out),
                                      _ptr(lse if want_lse else None), _ptr(workspace),
@@ -296,7 +377,13 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
         raise ValueError("tile_table must be [R][H][n_sel]")
     n_sel = tile_table.shape[2]
     B = int(block_size)
-    shp = _shape(R, n_q, Hq, H, D, B, _dt(q))
+    kptr, ks = _tile_store(k_tiles, "k_tiles", B * D)
+    vptr, vs = _tile_store(v_tiles, "v_tiles", B * D)
+    if ks != vs:
+        raise ValueError("k_tiles and v_tiles must share one tile stride")
+    if not (k_tiles.is_cuda and v_tiles.is_cuda):
+        raise ValueError("tile stores must live on the GPU")
+    shp = _shape(R, n_q, Hq, H, D, B, _dt(q), ks)
     dev = q.device
     b = {} if bufs is None else bufs
 
@@ -330,7 +417,8 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             _ptr(res["topk_idx"]), _ptr(res["topk_score"]), _ptr(res["scores"]),
             _ptr(slot_block), _ptr(slot_stamp), _ptr(slot_block_out), _ptr(slot_stamp_out),
             int(step), int(cap), int(pred_row), _ptr(res["plan_count"]), _ptr(res["plan_src"]),
-            _ptr(res["plan_dst"]), _ptr(res["plan_evicted"]), _ptr(k_tiles), _ptr(v_tiles),
+            _ptr(res["plan_dst"]), _ptr(res["plan_evicted"]), ctypes.c_void_p(kptr),
+            ctypes.c_void_p(vptr),
             _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile), _ptr(tail_len),
             float(scale), _ptr(res["out"]), _ptr(res["lse"]),
             ctypes.byref(opts) if opts is not None else None, _ptr(ws), ws.numel(),

@@ -146,6 +146,19 @@ def v_tiles_to_tokens(vt: torch.Tensor) -> torch.Tensor:
     return vt.transpose(-1, -2).reshape(*lead, n * B, D)
 
 
+def interleave_kv(kt: torch.Tensor, vt: torch.Tensor, out: torch.Tensor | None = None):
+    """Pack K tiles [..][n][B][D] and dim-major V tiles [..][n][D][B] into one
+    interleaved store [..][n][2][B][D] (each block-head's K tile, then its V
+    tile).  Returns (store, K view, V view); the views are what the kernels take."""
+    *lead, B, D = kt.shape
+    if out is None:
+        out = torch.empty((*lead, 2, B, D), dtype=kt.dtype, device=kt.device)
+    out[..., 0, :, :] = kt
+    out[..., 1, :, :] = vt.reshape(*lead, B, D)  # same bytes, V tile order kept
+    flat = out.view(*lead, 2, B * D)
+    return out, out[..., 0, :, :], flat[..., 1, :].unflatten(-1, (D, B))
+
+
 def random_tile_table(R: int, H: int, n_sel: int, n_blk: int, gen: torch.Generator,
                       device) -> torch.Tensor:
     """Distinct block ids per (request, KV head): [R][H][n_sel] int32."""

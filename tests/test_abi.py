@@ -56,6 +56,9 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
     (dict(head_dim=96), _lib.OASIS_EUNSUPPORTED),
     (dict(block_size=12), _lib.OASIS_EUNSUPPORTED),
     (dict(block_size=128), _lib.OASIS_EUNSUPPORTED),
+    (dict(tile_stride=2047), _lib.OASIS_EINVAL),       # below one tile (B*D = 2048)
+    (dict(tile_stride=-4096), _lib.OASIS_EINVAL),
+    (dict(tile_stride=2052), _lib.OASIS_EINVAL),       # 4104 bytes: not 16-byte aligned
 ])
 def test_shape_validation(lib, kw, code):
     s = _shape(**kw)

@@ -101,6 +101,24 @@ def test_summaries_bitwise(cuda, dtype, D, B, L):
     np.testing.assert_array_equal(np64(part), ref2)
 
 
+@pytest.mark.parametrize("dtype,D,B", [(torch.float32, 64, 16), (torch.bfloat16, 128, 16),
+                                        (torch.bfloat16, 64, 8)])
+def test_summaries_interleaved_store(cuda, dtype, D, B):
+    """Summaries read from the K half of an interleaved K|V store (tile stride
+    2*B*D) equal those of the dense key store, bit for bit."""
+    say(f"summaries interleaved dtype={dtype} D={D} B={B}")
+    R, H, nb = 2, 3, 37
+    gen = synth.generator(12, synth.S_KEYS, cuda)
+    kt = synth.normal((R, H, nb, B, D), gen, cuda, dtype)
+    vt = synth.normal((R, H, nb, D, B), gen, cuda, dtype)
+    _, k2, _ = synth.interleave_kv(kt, vt)
+    seq = torch.tensor([nb * B, nb * B - 2 * B - 1], dtype=torch.int32, device=cuda)
+    out = ops.build_summaries(k2, B, seq_len=seq)
+    torch.cuda.synchronize()
+    ref = oracle.build_summaries(np64(kt.reshape(R, H, nb * B, D)), B, seq_len=seq.cpu().numpy())
+    np.testing.assert_array_equal(np64(out), ref)
+
+
 def test_summaries_full_size_qwen3_8b(cuda):
     say("summaries qwen3-8b-1layer full size")
     wl, k, _, _ = make_layer(synth.workload("qwen3-8b-1layer"), cuda)
@@ -234,9 +252,10 @@ def test_plan_separate_outputs_and_large_k(cuda):
 
 
 # ------------------------------------------------------------------ copy
-@pytest.mark.parametrize("pinned", [False, True])
-def test_copy_blocks_bitwise(cuda, pinned):
-    say(f"copy_blocks pinned={pinned}")
+@pytest.mark.parametrize("pinned,interleaved", [(False, False), (True, False), (False, True),
+                                                (True, True)])
+def test_copy_blocks_bitwise(cuda, pinned, interleaved):
+    say(f"copy_blocks pinned={pinned} interleaved={interleaved}")
     R, H, nb, K, B, D = 2, 4, 40, 16, 16, 128
     gen = synth.generator(23, synth.S_MISC, cuda)
     sk = synth.normal((R, H, nb, B, D), gen, cuda, torch.bfloat16)
@@ -245,6 +264,11 @@ def test_copy_blocks_bitwise(cuda, pinned):
         sk, sv = sk.cpu().pin_memory(), sv.cpu().pin_memory()
     rk = synth.normal((R, H, K, B, D), gen, cuda, torch.bfloat16)
     rv = synth.normal((R, H, K, D, B), gen, cuda, torch.bfloat16)
+    if interleaved:
+        buf = torch.empty((R, H, nb, 2, B, D), dtype=torch.bfloat16, pin_memory=pinned,
+                          device="cpu" if pinned else cuda)
+        _, sk, sv = synth.interleave_kv(sk, sv, out=buf)
+        _, rk, rv = synth.interleave_kv(rk, rv)
     rng = np.random.default_rng(8)
     cnt = rng.integers(0, K + 1, (R, H)).astype(np.int32)
     src = np.stack([[rng.permutation(nb)[:K] for _ in range(H)] for _ in range(R)]).astype(np.int32)
@@ -307,6 +331,7 @@ def test_attn_parity(cuda, dtype, G, B, nb, n_sel, tail):
         tt = torch.full((R, H), nb - 1, dtype=torch.int32, device=cuda)
         tl = torch.tensor([tail, max(1, tail // 2)], dtype=torch.int32, device=cuda)
     ref = attn_reference(q, k, vt, table, nb, B, tt, tl)
+    _, ki, vi = synth.interleave_kv(k, vt)
     for impl in IMPLS[dtype]:
         if impl == ops.IMPL_MFMA and B % 16:
             continue
@@ -316,6 +341,9 @@ def test_attn_parity(cuda, dtype, G, B, nb, n_sel, tail):
         check_attn(out, lse, ref, dtype)
         out2, lse2 = ops.sparse_attn(q, k, vt, table, nb, B, tail_tile=tt, tail_len=tl, impl=impl)
         assert torch.equal(out, out2) and torch.equal(lse, lse2)  # deterministic
+        # the same tiles in an interleaved K|V store: identical results
+        o3, l3 = ops.sparse_attn(q, ki, vi, table, nb, B, tail_tile=tt, tail_len=tl, impl=impl)
+        assert torch.equal(out, o3) and torch.equal(lse, l3)
         # stacked rows == two single-row calls, bitwise
         for j in range(2):
             o1, l1 = ops.sparse_attn(q[:, j:j + 1].contiguous(), k, vt, table, nb, B, tail_tile=tt,

@@ -41,8 +41,11 @@ def score_scale(q64, summ64, G):
     return np.einsum("rjhd,rhbd->rjhb", qa, amax)
 
 
-def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0):
-    """Seed the resident set, then run `steps` fused steps, checking each."""
+def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0,
+              interleaved=False):
+    """Seed the resident set, then run `steps` fused steps, checking each.  With
+    `interleaved` the K and V tiles live in one interleaved store (tile stride
+    2*B*D) and the summaries are built from its K half."""
     qf = synth.queries(wl, cuda)
     keys = synth.keys(wl, qf[:, 0], cuda)
     vals = synth.values(wl, cuda)
@@ -50,6 +53,10 @@ def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0
     del vals
     summ = ops.build_summaries(keys, wl.B)
     kt = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
+    if interleaved:
+        _, kt, vt = synth.interleave_kv(kt, vt)
+        del keys
+        assert torch.equal(ops.build_summaries(kt, wl.B), summ)
     R, H, K = wl.R, wl.H, wl.K
     dev = cuda
     if tail and n_blk is None:
@@ -170,6 +177,21 @@ def test_step_bf16(cuda, G, D, B, L, K, nq_opts):
     run_chain(cuda, wl, 3, opts=ops.step_opts(*nq_opts), tail=5 if L % 64 else 0)
 
 
+@pytest.mark.parametrize("name,G,D,B,L,K,opts", [
+    ("tiny-fp32", None, None, None, 1040, None, (1, 1, 0)),
+    ("qwen3-8b-1layer", 4, 128, 16, 4112, 32, (2, 2, 0)),
+    ("qwen3-8b-1layer", 4, 128, 16, 4096, 32, (0, 0, 1)),  # VALU attention
+    ("qwen3-8b-1layer", 4, 128, 8, 1024, 20, (2, 3, 0)),   # B < 16: VALU
+])
+def test_step_interleaved_store(cuda, name, G, D, B, L, K, opts):
+    """K and V tiles interleaved in one store (tile stride 2*B*D)."""
+    kw = dict(L=L) if G is None else dict(R=3, H=2, Hq=2 * G, D=D, B=B, L=L, K=K, cap=5)
+    wl = small(name, **kw)
+    say(f"fused step interleaved store {name} {kw} opts={opts}")
+    run_chain(cuda, wl, 3, opts=ops.step_opts(*opts), tail=5 if L % 64 else 0,
+              interleaved=True)
+
+
 def test_step_short_contexts(cuda):
     """Requests with fewer full blocks than K, and an empty one."""
     wl = small("qwen3-8b-1layer", R=3, H=2, Hq=8, L=1024, K=32, cap=4)
@@ -177,16 +199,17 @@ def test_step_short_contexts(cuda):
     run_chain(cuda, wl, 3, opts=ops.step_opts(2, 2, 0), n_blk=[64, 20, 0])
 
 
-@pytest.mark.parametrize("name,steps,units", [
-    ("qwen3-8b-1layer", 3, None),
-    ("llama3.1-8b-32layer", 2, [(0, 0), (13, 5), (31, 7)]),
-    ("qwen3-235b-1layer", 2, [(0, 1), (7, 3)]),
+@pytest.mark.parametrize("name,steps,units,interleaved", [
+    ("qwen3-8b-1layer", 3, None, False),
+    ("llama3.1-8b-32layer", 2, [(0, 0), (13, 5), (31, 7)], True),
+    ("llama3.1-8b-32layer", 2, [(3, 2), (30, 1)], False),
+    ("qwen3-235b-1layer", 2, [(0, 1), (7, 3)], True),
 ])
-def test_step_full_size(cuda, name, steps, units):
+def test_step_full_size(cuda, name, steps, units, interleaved):
     """The benchmark's launch configuration (automatic splits) at full shape."""
     wl = synth.workload(name, layers=1)
-    say(f"fused step full size {name}")
-    run_chain(cuda, wl, steps, units=units)
+    say(f"fused step full size {name} interleaved={interleaved}")
+    run_chain(cuda, wl, steps, units=units, interleaved=interleaved)
 
 
 def test_step_resident_layout(cuda):

@@ -51,6 +51,8 @@ def parse_args(argv=None):
     p.add_argument("--path", choices=("fused", "unfused"), default="fused",
                    help="fused: one oasis_lookahead_step launch per layer-step; unfused: "
                         "oasis_sparse_attn + oasis_score_topk + oasis_select_plan")
+    p.add_argument("--pipeline", action="store_true",
+                   help="pinned-host pipeline (use with --workload qwen3-8b-pipeline)")
     p.add_argument("--kv-layout", choices=("interleaved", "split"), default="interleaved",
                    help="one K|V record per block-head, or separate K and V stores")
     p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
@@ -279,6 +281,141 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     return res
 
 
+# ----------------------------------------------------------------- pipeline leg
+PEAK_PCIE_GBS = 64.0  # PCIe Gen5 x16, one direction, nominal
+
+
+def run_pipeline(args, wl, torch, synth, ops):
+    """The pinned-host pipeline: each layer's full K|V store in pinned host
+    memory, K slots per KV head resident in HBM, the fused step on the main
+    stream and the planned block copies on a background stream (ordered by
+    events, see sparse_kv_block_quest_amd.pipeline)."""
+    from sparse_kv_block_quest_amd import pipeline
+
+    dev = torch.device("cuda:0")
+    n_layers = wl.layers
+    impl = {"auto": ops.IMPL_AUTO, "valu": ops.IMPL_VALU, "mfma": ops.IMPL_MFMA}[args.impl]
+    opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
+    layers = []
+    t0 = time.perf_counter()
+    for l in range(n_layers):
+        qf = synth.queries(wl, dev, layer=l)
+        keys = synth.keys(wl, qf[:, 0], dev, layer=l)
+        vt = synth.v_tiles(synth.values(wl, dev, layer=l), wl.B)
+        store, k, _ = synth.interleave_kv(keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D), vt)
+        del keys, vt
+        summ = ops.build_summaries(k, wl.B)
+        host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
+        host.copy_(store)
+        del store, k
+        layers.append(pipeline.PipelineLayer(wl, host, summ, qf.to(wl.dtype), dev, opts=opts))
+        if (l + 1) % 6 == 0 or l + 1 == n_layers:
+            print(f"# layer {l + 1}/{n_layers} in pinned host memory "
+                  f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    T = args.warmup + 2 * args.steps
+    qseq = query_sequence(wl, dev, n_layers, T, torch, synth)
+    pipe = pipeline.Pipeline(layers)
+    main = torch.cuda.current_stream()
+    pipe.seed([qseq[0, l] for l in range(n_layers)])
+    torch.cuda.synchronize()
+    for t in range(args.warmup):
+        for l in range(n_layers):
+            pipe.layer_step(t, l, qseq[t, l])
+    torch.cuda.synchronize()
+
+    # Timed region: free-running, no markers between launches; the end waits
+    # for the copy stream, so every copy is inside it.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record()
+    for t in range(args.warmup, args.warmup + args.steps):
+        for l in range(n_layers):
+            pipe.layer_step(t, l, qseq[t, l])
+    main.wait_stream(pipe.copy_stream)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    total_ms = ev0.elapsed_time(ev1)
+
+    # Breakdown replay on the following steps: events around every fused step
+    # (main stream) and every copy (copy stream), and the admitted blocks.
+    admitted = torch.zeros((), dtype=torch.int64, device=dev)
+    ev_step, ev_copy = [], []
+    cs = pipe.copy_stream
+    for t in range(args.warmup + args.steps, T):
+        for l in range(n_layers):
+            L = layers[l]
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            main.wait_event(L.copy_done)
+            a0.record(main)
+            res = L.step_calls[t % 2](t + 1, qseq[t, l])
+            a1.record(main)
+            admitted.add_(res["plan_count"].sum())
+            L.attn_done.record(main)
+            cs.wait_event(L.attn_done)
+            c0.record(cs)
+            L.copy_call(cs)
+            c1.record(cs)
+            L.copy_done.record(cs)
+            ev_step.append((a0, a1))
+            ev_copy.append((c0, c1))
+    torch.cuda.synchronize()
+
+    def avg_us(evs):
+        return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+    return {"total_ms": total_ms, "wall_s": wall, "step_us": avg_us(ev_step),
+            "copy_us": avg_us(ev_copy),
+            "admitted_per_head_step": float(admitted.item()) / (args.steps * n_layers * wl.R * wl.H),
+            "setup_s": time.perf_counter() - t0}
+
+
+def report_pipeline(args, wl, g):
+    e = 2 if str(wl.dtype).endswith("bfloat16") else 4
+    n_ls = args.steps * wl.layers
+    units = wl.R * wl.H
+    ab = algo_bytes(wl, e)
+    per_ls = units * per_ls_alg(1, ab)
+    tile_bytes = 2 * wl.B * wl.D * e
+    copied = g["admitted_per_head_step"] * units * tile_bytes  # per layer-step
+    ls_us = g["total_ms"] * 1000.0 / n_ls
+    step_gbs = per_ls / (g["step_us"] * 1e-6) / 1e9
+    pcie_gbs = copied / (g["copy_us"] * 1e-6) / 1e9
+    line = {
+        "metric": "layer-steps/s (pinned-host pipeline: scan+top-K+plan+sparse attn, "
+                  "block copies overlapped)",
+        "value": round(n_ls / (g["total_ms"] / 1000.0), 2),
+        "unit": "layer-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(g["total_ms"] / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if e == 2 else "f32", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: Qwen3-8B attention shape, {wl.Hq} q / {wl.H} KV "
+                               f"heads, head_dim {wl.D}; full K|V in pinned host memory",
+                   "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
+                   "layers": wl.layers, "cap": wl.cap, "stacked_queries": wl.n_q,
+                   "host_store_GiB": round(wl.layers * units * wl.n_blk * tile_bytes / 2**30, 2)},
+        "roofline": {"bound": "pcie", "kernel": "oasis_copy_blocks", "achieved": round(pcie_gbs, 2),
+                     "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                     "frac": round(pcie_gbs / PEAK_PCIE_GBS, 4), "traffic": None},
+        "stages_us_per_layer_step": {
+            "fused_step": round(g["step_us"], 2), "copy": round(g["copy_us"], 2),
+            "pipeline_interval": round(ls_us, 2),
+            "stall": round(max(0.0, ls_us - g["step_us"]), 2)},
+        "fused_step": {"algo_bytes": per_ls, "GBps": round(step_gbs, 1),
+                       "frac": round(step_gbs / PEAK_HBM_GBS, 4)},
+        "pcie": {"bytes_per_layer_step": round(copied), "copy_kernel_GBps": round(pcie_gbs, 2),
+                 "wall_GBps": round(copied / (ls_us * 1e-6) / 1e9, 2)},
+        "admitted_blocks_per_head_step": round(g["admitted_per_head_step"], 3),
+        "host_issue_us_per_layer_step": round(g["wall_s"] * 1e6 / n_ls, 2),
+        "kernel_sources": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ----------------------------------------------------------------- CPU leg
 def run_cpu_baseline(args, wl, g, torch, synth):
     """The oracle, as it stands, on a bounded sample of the same workload: whole
@@ -366,6 +503,8 @@ def main(argv=None):
     print(f"# workload {wl.name}: R={wl.R} Hq={wl.Hq} H={wl.H} D={wl.D} L={wl.L} B={wl.B} "
           f"K={wl.K} layers={wl.layers} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
+    if args.pipeline:
+        return report_pipeline(args, wl, run_pipeline(args, wl, torch, synth, ops))
     g = run_gpu(args, wl, torch, synth, ops, _lib)
     print(f"# gpu timed region {g['total_ms']:.2f} ms", file=sys.stderr, flush=True)
 

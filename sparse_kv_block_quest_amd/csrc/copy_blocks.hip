@@ -6,31 +6,37 @@
 // writes them into HBM) and §4.1 Implementation (the full KV cache lives in
 // pinned CPU memory; the gather writes directly into the resident GPU pages).
 //
-// One workgroup per (plan entry, KV head, request); entries at or past the
-// unit's plan_count exit at once.  Each thread moves 16-byte words of the K
-// tile and of the V tile, so one workgroup keeps 2*tile bytes of reads in
-// flight; the device-resident plan is consumed without a host round trip.
+// Workgroup (j, u), one wave, moves plan entries j, j + S, j + 2S, ... of
+// unit u (S = kCopySplit).  Offsets are uniform, so they stay in scalar
+// registers, and a lane carries one 16-byte word at a time: the kernel needs
+// about 10 VGPRs.  That lets copy waves share a SIMD with two waves of the
+// fused step kernel when the copy runs beside it on another stream, and a
+// small grid (2 waves per unit) keeps few SIMDs busy with waits on PCIe while
+// still holding enough reads in flight to fill the link.  The device-resident
+// plan is consumed without a host round trip.
 #include "oasis_internal.h"
 
 namespace oasis {
 
-__global__ void __launch_bounds__(256)
+constexpr int kCopySplit = 2;
+constexpr int kCopyThreads = 64;
+
+__global__ void __launch_bounds__(kCopyThreads)
 copy_blocks_kernel(const uint4* __restrict__ src_k, const uint4* __restrict__ src_v,
-                   uint4* __restrict__ res_k, uint4* __restrict__ res_v, int H, int n_blk_max,
+                   uint4* __restrict__ res_k, uint4* __restrict__ res_v, int n_blk_max,
                    int K, int tile_u4, long long stride_u4, const int32_t* __restrict__ plan_count,
                    const int32_t* __restrict__ plan_src, const int32_t* __restrict__ plan_dst) {
-    const int i = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
-    const size_t u = (size_t)r * H + g;
-    if (i >= plan_count[u]) return;
-    const int src = plan_src[u * K + i];
-    const int dst = plan_dst[u * K + i];
-    const size_t so = (u * n_blk_max + src) * (size_t)stride_u4;
-    const size_t d_o = (u * K + dst) * (size_t)stride_u4;
-    for (int t = threadIdx.x; t < tile_u4; t += 256) {
-        const uint4 a = src_k[so + t];
-        const uint4 b = src_v[so + t];
-        res_k[d_o + t] = a;
-        res_v[d_o + t] = b;
+    const size_t u = blockIdx.y;
+    const int n = plan_count[u];
+    for (int i = blockIdx.x; i < n; i += kCopySplit) {
+        const int src = plan_src[u * K + i];
+        const int dst = plan_dst[u * K + i];
+        const uint4* sk = src_k + (u * n_blk_max + src) * (size_t)stride_u4;
+        const uint4* sv = src_v + (u * n_blk_max + src) * (size_t)stride_u4;
+        uint4* dk = res_k + (u * K + dst) * (size_t)stride_u4;
+        uint4* dv = res_v + (u * K + dst) * (size_t)stride_u4;
+        for (unsigned t = threadIdx.x; t < (unsigned)tile_u4; t += kCopyThreads) dk[t] = sk[t];
+        for (unsigned t = threadIdx.x; t < (unsigned)tile_u4; t += kCopyThreads) dv[t] = sv[t];
     }
 }
 
@@ -79,10 +85,12 @@ extern "C" int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const 
     const void* dv = nullptr;
     if (device_view(src_k, &dk) != OASIS_OK || device_view(src_v, &dv) != OASIS_OK)
         return OASIS_EINVAL;
-    hipLaunchKernelGGL(copy_blocks_kernel, dim3(top_k, s->n_kv_heads, s->batch), dim3(256), 0,
+    const long long units = (long long)s->batch * s->n_kv_heads;
+    if (units > 65535) return OASIS_EUNSUPPORTED;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(kCopySplit, (unsigned)units), dim3(kCopyThreads), 0,
                        stream, reinterpret_cast<const uint4*>(dk),
                        reinterpret_cast<const uint4*>(dv), reinterpret_cast<uint4*>(res_k),
-                       reinterpret_cast<uint4*>(res_v), s->n_kv_heads, n_blk_max, top_k,
+                       reinterpret_cast<uint4*>(res_v), n_blk_max, top_k,
                        int(tile_bytes / 16),
                        tile_stride_of(s) * (s->dtype == OASIS_F32 ? 4 : 2) / 16, plan_count,
                        plan_src, plan_dst);

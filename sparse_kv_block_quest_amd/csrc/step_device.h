@@ -926,26 +926,32 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
     // placeholder sub-tiles too (ntok = 0 masks every token), so no path
     // leaves a buffer's loads unconsumed.  sched_barrier keeps each buffer's
     // loads issued before the arithmetic on the previous one.
-    bf16x8_t kA[KB], kB[KB], kC[KB];
-    bf16x4_t vA[DB], vB[DB], vC[DB];
+    bf16x8_t kA[KB], kB[KB], kC[KB], kD[KB];
+    bf16x4_t vA[DB], vB[DB], vC[DB], vD[DB];
     int st = w;
     int nA = fetch(st, kA, vA);
     int nB = fetch(st + 4, kB, vB);
-    int nC = 0;
+    int nC = fetch(st + 8, kC, vC);
+    int nD = 0;
     while (st < n_sub) {
-        nC = fetch(st + 8, kC, vC);
+        nD = fetch(st + 12, kD, vD);
         __builtin_amdgcn_sched_barrier(0);
         compute(kA, vA, nA);
         st += 4;
         if (st >= n_sub) break;
-        nA = fetch(st + 8, kA, vA);
+        nA = fetch(st + 12, kA, vA);
         __builtin_amdgcn_sched_barrier(0);
         compute(kB, vB, nB);
         st += 4;
         if (st >= n_sub) break;
-        nB = fetch(st + 8, kB, vB);
+        nB = fetch(st + 12, kB, vB);
         __builtin_amdgcn_sched_barrier(0);
         compute(kC, vC, nC);
+        st += 4;
+        if (st >= n_sub) break;
+        nC = fetch(st + 12, kC, vC);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(kD, vD, nD);
         st += 4;
     }
     // Row sums: the 4 lane groups hold disjoint tokens of the same rows.
@@ -1216,7 +1222,7 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) 
 // kAttnNone); the number of items per unit of each role comes from the
 // arguments.
 template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN>
-__global__ void __launch_bounds__(kNT) step_kernel(StepArgs a) {
+__global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG == 1 ? 2 : 1))) step_kernel(StepArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int w = blockIdx.x;
     const int x = w & 7;

@@ -34,14 +34,6 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _host_or_dev_ptr(t: torch.Tensor):
-    if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    if not t.is_cuda and not t.is_pinned():
-        raise ValueError("source store must be device memory or pinned host memory")
-    return ctypes.c_void_p(t.data_ptr())
-
-
 def _i32(t: torch.Tensor, name: str) -> torch.Tensor:
     if t.dtype != torch.int32:
         raise TypeError(f"{name} must be int32")
@@ -210,6 +202,32 @@ def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
                 res_v: torch.Tensor, plan: dict, block_size: int, stream=None) -> None:
     """src_* [R][H][n_blk_max][..tile..] (device or pinned host), res_* [R][H][K][..tile..]
     (device); K tiles [B][D], V tiles [D][B]; dense or interleaved, one shared tile stride."""
+    prepare_copy_blocks(src_k, src_v, res_k, res_v, plan, block_size, stream)()
+
+
+class PreparedCopy:
+    """A validated oasis_copy_blocks call with its ctypes arguments built once;
+    calling it enqueues the copy again (on the stream given at preparation, or
+    on ``stream``)."""
+
+    def __init__(self, args, keep, lib):
+        self.args = args
+        self._keep = keep
+        self._fn = lib.oasis_copy_blocks
+
+    def __call__(self, stream=None) -> None:
+        a = self.args
+        if stream is not None:
+            a = a[:-1] + [_stream(stream)]
+        st = self._fn(*a)
+        if st != 0:
+            check("oasis_copy_blocks", st)
+
+
+def prepare_copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
+                        res_v: torch.Tensor, plan: dict, block_size: int,
+                        stream=None) -> PreparedCopy:
+    """``copy_blocks`` with the argument checks done once (see ``PreparedCopy``)."""
     lib = _lib.load()
     if any(t.dim() < 4 for t in (src_k, src_v, res_k, res_v)):
         raise ValueError("tile stores must be [R][H][n][..tile..]")
@@ -238,10 +256,16 @@ def copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
         raise ValueError("all four stores must share one tile stride")
     shp = _shape(R, 1, H, H, D, B, _dt(src_k), strides[0])
     cp = [ctypes.c_void_p(x) for x in ptrs]
-    check("oasis_copy_blocks",
-          lib.oasis_copy_blocks(ctypes.byref(shp), cp[0], cp[1], nb, cp[2], cp[3], K,
-                                _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
-                                _ptr(plan["plan_dst"]), _stream(stream)))
+    for k in ("plan_count", "plan_src", "plan_dst"):
+        _i32(plan[k], k)
+    if plan["plan_count"].shape != (R, H) or plan["plan_src"].shape != (R, H, K) or \
+            plan["plan_dst"].shape != (R, H, K):
+        raise ValueError("plan tensors must be [R][H] and [R][H][K]")
+    args = [ctypes.byref(shp), cp[0], cp[1], nb, cp[2], cp[3], K, _ptr(plan["plan_count"]),
+            _ptr(plan["plan_src"]), _ptr(plan["plan_dst"]), _stream(stream)]
+    keep = (shp, src_k, src_v, res_k, res_v, plan["plan_count"], plan["plan_src"],
+            plan["plan_dst"])
+    return PreparedCopy(args, keep, lib)
 
 
 def sparse_attn_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_sel: int,

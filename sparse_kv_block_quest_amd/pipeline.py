@@ -1,0 +1,98 @@
+"""Two-stream decode pipeline over a pinned-host KV store: orchestration only.
+
+Per layer the full K|V store stays in pinned host memory and a resident set
+of top_k slots per KV head lives in HBM.  One layer-step is
+
+  main stream:  wait for this layer's previous copy, then the fused step
+                (attention of both query rows over the resident slots, and
+                scan, top-K and plan for the next step);
+  copy stream:  wait for that attention, then copy the planned blocks from
+                host to their resident slots (oasis_copy_blocks reads the
+                mapped pinned memory from the GPU).
+
+The copy overwrites slots the attention has just read, so it is ordered after
+it; the next step's attention of the same layer reads what the copy wrote, so
+it is ordered after the copy.  Other layers run meanwhile.  This is the
+pipelined transfer of the OasisKV paper (Section 4, the pinned-host path with a
+background copy stream and events that keep each layer's order); the steps
+themselves are the library's kernels, called through ``ops``.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class PipelineLayer:
+    """State of one layer: host store views, resident store, slot tables
+    (double-buffered: step t reads buffer t % 2 and plans into the other),
+    per-layer plan buffers and the prepared calls."""
+
+    def __init__(self, wl, host_store: torch.Tensor, summaries: torch.Tensor,
+                 q0: torch.Tensor, device, opts=None, want_scores=False):
+        R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
+        if not host_store.is_pinned():
+            raise ValueError("the host store must be pinned")
+        self.wl = wl
+        self.host = host_store
+        self.host_k, self.host_v = ops.interleaved_kv(host_store)
+        self.res = torch.empty((R, H, K, 2, B, D), dtype=wl.dtype, device=device)
+        self.res_k, self.res_v = ops.interleaved_kv(self.res)
+        self.summ = summaries
+        self.blk = [torch.full((R, H, K), -1, dtype=torch.int32, device=device) for _ in range(2)]
+        self.stamp = [torch.full((R, H, K), -1, dtype=torch.int32, device=device)
+                      for _ in range(2)]
+        self.ident = torch.arange(K, dtype=torch.int32, device=device).repeat(R, H, 1).contiguous()
+        self.bufs = {}
+        self.step_calls = [ops.prepare_lookahead_step(
+            q0, summaries, K, self.blk[p], self.stamp[p], self.blk[1 - p], self.stamp[1 - p], 0,
+            wl.cap, self.res_k, self.res_v, self.ident, K, B, pred_row=1, want_scores=want_scores,
+            want_evicted=False, opts=opts, bufs=self.bufs) for p in range(2)]
+        self.plan = {k: self.bufs[k] for k in ("plan_count", "plan_src", "plan_dst")}
+        self.copy_call = ops.prepare_copy_blocks(self.host_k, self.host_v, self.res_k,
+                                                 self.res_v, self.plan, B)
+        self.attn_done = torch.cuda.Event()
+        self.copy_done = torch.cuda.Event()
+
+    def seed(self, q0: torch.Tensor, copy_stream) -> None:
+        """First working set from row 0 of the first queries (empty slots, no
+        cap), copied on ``copy_stream``; the next step's attention waits for it."""
+        wl = self.wl
+        idx, _, _ = ops.score_topk(q0, self.summ, wl.K)
+        ops.select_plan(idx, self.blk[0], self.stamp[0], 0, wl.cap, pred_row=0,
+                        plan=dict(self.plan, plan_evicted=None))
+        self.attn_done.record()
+        copy_stream.wait_event(self.attn_done)
+        self.copy_call(copy_stream)
+        self.copy_done.record(copy_stream)
+
+
+class Pipeline:
+    """Layers sharing one main stream (the caller's current stream) and one
+    background copy stream."""
+
+    def __init__(self, layers: list[PipelineLayer], copy_stream=None):
+        self.layers = layers
+        self.copy_stream = copy_stream or torch.cuda.Stream()
+
+    def seed(self, q0s) -> None:
+        for layer, q0 in zip(self.layers, q0s):
+            layer.seed(q0, self.copy_stream)
+
+    def layer_step(self, t: int, l: int, q: torch.Tensor) -> dict:
+        """Step t of layer l with stacked queries q; returns the fused call's
+        result dict (its buffers are reused by this layer's next step)."""
+        L = self.layers[l]
+        main = torch.cuda.current_stream()
+        main.wait_event(L.copy_done)
+        res = L.step_calls[t % 2](t + 1, q)
+        L.attn_done.record(main)
+        self.copy_stream.wait_event(L.attn_done)
+        L.copy_call(self.copy_stream)
+        L.copy_done.record(self.copy_stream)
+        return res
+
+    def resident_blocks(self, l: int, t: int) -> torch.Tensor:
+        """Slot table that describes layer l's resident store during step t."""
+        return self.layers[l].blk[t % 2]

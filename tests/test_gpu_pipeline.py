@@ -1,0 +1,124 @@
+"""GPU parity of the two-stream pinned-host pipeline: resident slots in HBM,
+the full K|V store in pinned host memory, copies on a background stream.
+
+Run A synchronises after every layer-step and checks each step against the
+oracle: scores, top-K, plan and slot tables, and attention over the resident
+store (which must hold exactly the host tiles its slot table names, byte for
+byte).  Run B repeats the same steps free-running, ordered only by the
+pipeline's events, and must reproduce run A bit for bit; a missing wait
+between a copy and the attention that reads or last read its slots would
+show up there.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_block_quest_amd import ops, pipeline, synth
+from test_gpu_step import check_step, small
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def build(wl, dev, n_layers, opts=None, want_scores=True):
+    layers, q0s, full = [], [], []
+    for l in range(n_layers):
+        qf = synth.queries(wl, dev, layer=l)
+        keys = synth.keys(wl, qf[:, 0], dev, layer=l)
+        vt = synth.v_tiles(synth.values(wl, dev, layer=l), wl.B)
+        kt = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
+        store, k, v = synth.interleave_kv(kt, vt)
+        summ = ops.build_summaries(k, wl.B)
+        host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
+        host.copy_(store)
+        q0 = qf.to(wl.dtype)
+        layers.append(pipeline.PipelineLayer(wl, host, summ, q0, dev, opts=opts,
+                                             want_scores=want_scores))
+        q0s.append(q0)
+        full.append((k, v, store))
+    return pipeline.Pipeline(layers), q0s, full
+
+
+def query_steps(wl, dev, n_layers, n_steps):
+    """[t][l] stacked queries in wl.dtype, the AR(1) drift of each layer's first queries."""
+    out = [[None] * n_layers for _ in range(n_steps)]
+    for l in range(n_layers):
+        g = synth.generator(wl.seed + 1000 * l, synth.S_DRIFT, "cuda")
+        cur = synth.queries(wl, dev, layer=l)
+        for t in range(n_steps):
+            out[t][l] = cur.to(wl.dtype)
+            cur = synth.drift(cur[:, 0], wl.rho, g)
+    return out
+
+
+def resident_matches_host(layer, blk):
+    """Every filled slot holds the host tiles of the block its slot table names."""
+    R, H, K = blk.shape
+    b = blk.long()
+    assert bool((b >= 0).all()), "pipeline slots are all filled after seeding"
+    r = torch.arange(R, device=b.device)[:, None, None]
+    g = torch.arange(H, device=b.device)[None, :, None]
+    host_dev = layer.host.to(b.device)
+    want = host_dev[r, g, b]
+    assert torch.equal(layer.res.view(torch.int16), want.view(torch.int16))
+
+
+def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None):
+    dev = cuda
+    qs = query_steps(wl, dev, n_layers, n_steps)
+    n_valid = np.full(wl.R, wl.n_blk, np.int32)
+    if units is None:
+        units = [(r, g) for r in range(wl.R) for g in range(wl.H)]
+
+    # run A: checked step by step
+    pa, q0s, full = build(wl, dev, n_layers, opts)
+    pa.seed(q0s)
+    torch.cuda.synchronize()
+    outs_a = []
+    for l, layer in enumerate(pa.layers):
+        resident_matches_host(layer, pa.resident_blocks(l, 0))
+    for t in range(n_steps):
+        for l in range(n_layers):
+            say(f"  pipeline A step {t} layer {l}")
+            L = pa.layers[l]
+            res = pa.layer_step(t, l, qs[t][l])
+            torch.cuda.synchronize()
+            a, b = t % 2, 1 - t % 2
+            k, v, _ = full[l]
+            check_step(wl, qs[t][l], L.summ, k, v, L.blk[a], L.stamp[a], L.blk[b], L.stamp[b],
+                       res, t + 1, n_valid, None, None, units)
+            outs_a.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
+            resident_matches_host(L, L.blk[b])
+    del pa
+
+    # run B: free-running, events only
+    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False)
+    pb.seed(q0s)
+    outs_b = []
+    for t in range(n_steps):
+        for l in range(n_layers):
+            res = pb.layer_step(t, l, qs[t][l])
+            outs_b.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
+    torch.cuda.synchronize()
+    say("  pipeline B done")
+    for i, (xa, xb) in enumerate(zip(outs_a, outs_b)):
+        for ta, tb in zip(xa, xb):
+            assert torch.equal(ta, tb), f"free-running layer-step {i} differs"
+    for l in range(n_layers):
+        resident_matches_host(pb.layers[l], pb.resident_blocks(l, n_steps))
+
+
+def test_pipeline_small(cuda):
+    wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=2048, K=16, cap=4)
+    say("pipeline small: R=2 H=2 K=16 cap=4, 2 layers x 4 steps")
+    run_pipeline_case(cuda, wl, 2, 4)
+
+
+def test_pipeline_full_shape(cuda):
+    """The Qwen3-8B pipeline shape (R=8, 32K context, K=128, cap 16), two layers."""
+    wl = synth.workload("qwen3-8b-pipeline", layers=2)
+    say("pipeline qwen3-8b shape, 2 layers x 2 steps")
+    run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)])

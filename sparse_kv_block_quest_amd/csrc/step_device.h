@@ -189,29 +189,7 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
     constexpr int UNR = kScanUnroll;
     const int tid = threadIdx.x;
     const int r = u / a.H, g = u - (u / a.H) * a.H;
-    // P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0) over the group's heads.
-    for (int idx = tid; idx < NQ * D; idx += kNT) {
-        const int j = idx / D, d = idx - (idx / D) * D;
-        float p = 0.f, n = 0.f;
-        for (int h = 0; h < a.G; ++h) {
-            const float x =
-                load_elem<DT>(a.q, (((size_t)r * NQ + j) * a.Hq + (size_t)g * a.G + h) * D + d);
-            p += x > 0.f ? x : 0.f;
-            n += x < 0.f ? x : 0.f;
-        }
-        pn[(j * 2) * D + d] = p;
-        pn[(j * 2 + 1) * D + d] = n;
-    }
-    lds_barrier();
     const int cl = tid % LPR, lb = tid / LPR;
-    float P[NQ][VEC], N[NQ][VEC];
-#pragma unroll
-    for (int j = 0; j < NQ; ++j)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-            P[j][e] = pn[(j * 2) * D + cl * VEC + e];
-            N[j][e] = pn[(j * 2 + 1) * D + cl * VEC + e];
-        }
     const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
     const int b_begin = c * a.chunk;
     const int b_end = min(b_begin + a.chunk, a.n_blk_max);
@@ -228,6 +206,32 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
             mx[k] = base[(size_t)b * 2 * LPR + LPR];
         }
     };
+    // The first summaries do not depend on q: they are in flight while the
+    // group's P/N vectors are formed.
+    uint4 mnA[UNR], mxA[UNR], mnB[UNR], mxB[UNR];
+    load(b_begin, mnA, mxA);
+    // P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0) over the group's heads.
+    for (int idx = tid; idx < NQ * D; idx += kNT) {
+        const int j = idx / D, d = idx - (idx / D) * D;
+        float p = 0.f, n = 0.f;
+        for (int h = 0; h < a.G; ++h) {
+            const float x =
+                load_elem<DT>(a.q, (((size_t)r * NQ + j) * a.Hq + (size_t)g * a.G + h) * D + d);
+            p += x > 0.f ? x : 0.f;
+            n += x < 0.f ? x : 0.f;
+        }
+        pn[(j * 2) * D + d] = p;
+        pn[(j * 2 + 1) * D + d] = n;
+    }
+    lds_barrier();
+    float P[NQ][VEC], N[NQ][VEC];
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            P[j][e] = pn[(j * 2) * D + cl * VEC + e];
+            N[j][e] = pn[(j * 2 + 1) * D + cl * VEC + e];
+        }
     auto process = [&](int b0, const uint4 (&mn)[UNR], const uint4 (&mx)[UNR]) {
         float acc[UNR][NQ];
 #pragma unroll
@@ -266,8 +270,6 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
     };
     // Ping-pong over two register buffers (no copies of in-flight loads).
     constexpr int STEP = BPP * UNR;
-    uint4 mnA[UNR], mxA[UNR], mnB[UNR], mxB[UNR];
-    load(b_begin, mnA, mxA);
     int b0 = b_begin;
     // sched_barrier keeps every load of the next buffer issued before the
     // current buffer's arithmetic (the scheduler would otherwise interleave
@@ -783,7 +785,7 @@ struct AttnFin {
 // flight in registers while the current one is computed.  P is rounded to bf16.
 template <int D, int NRG>
 __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
-                               const int* tbl) {
+                               int* tbl) {
     constexpr int KB = D / 32;
     constexpr int DB = D / 16;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -810,6 +812,12 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
             for (int kb = 0; kb < KB; ++kb) qv[rg][kb] = qp[kb * 4 + lg];
         }
     }
+    // The unit's tile table goes to LDS while the q loads above are in
+    // flight (one round trip for both before the first tile load).
+    const SplitRange sr = split_range(a, u, sp);
+    for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
+        tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
+    __syncthreads();
     float m[NRG], lsum[NRG];
     f32x4_t acc[NRG][DB];
 #pragma unroll
@@ -819,7 +827,6 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[rg][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
-    const SplitRange sr = split_range(a, u, sp);
     const int spe = B / 16;
     const int n_entry_sub = (sr.e1 - sr.e0) * spe;
     const int n_sub = n_entry_sub + (sr.tail_len + 15) / 16;
@@ -1206,12 +1213,13 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) 
     F.m = cur.take<float>(a.NR);
     F.l = cur.take<float>(a.NR);
     F.acc = cur.take<float>((size_t)a.NR * D);
-    const SplitRange sr = split_range(a, u, sp);
-    for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT) tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
-    __syncthreads();
     if constexpr (ATT == kAttnMfma) {
-        attn_item_mfma<D, NRG>(a, u, sp, cur, F, tbl);
+        attn_item_mfma<D, NRG>(a, u, sp, cur, F, tbl);  // stages the table after loading q
     } else {
+        const SplitRange sr = split_range(a, u, sp);
+        for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
+            tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
+        __syncthreads();
         attn_item_valu<DT, D>(a, u, sp, cur, F, tbl);
     }
     attn_emit<DT, D>(a, u, sp, F);

@@ -41,7 +41,7 @@ def _load():
     lib.oro_topk.argtypes = [ctypes.c_int] * 4 + [_f64p, _i32p, ctypes.c_int, _i32p, _f64p]
     lib.oro_select_plan.argtypes = [ctypes.c_int] * 5 + [_i32p, _i32p, _i32p, ctypes.c_int,
                                                            ctypes.c_int, _i32p, _i32p, _i32p,
-                                                           _i32p]
+                                                           _i32p, _i32p]
     lib.oro_copy_blocks.argtypes = [ctypes.c_int] * 4 + [ctypes.c_long, _u8p, _u8p, _u8p,
                                                            _u8p, _i32p, _i32p, _i32p]
     lib.oro_sparse_attn.argtypes = ([ctypes.c_int] * 6 + [_f64p, _f64p, _f64p, ctypes.c_long,
@@ -126,8 +126,10 @@ def topk(scores, k: int, n_blk=None):
     return idx, val
 
 
-def select_plan(topk_idx, slot_block, slot_stamp, step: int, cap: int, pred_row: int = 1):
-    """Capped least-recently-selected plan.
+def select_plan(topk_idx, slot_block, slot_stamp, step: int, cap: int, pred_row: int = 1,
+                ins_blk=None):
+    """Capped least-recently-selected plan, plus the optional insertion of each
+    request's newly completed block (ins_blk [R], -1 = none).
 
     topk_idx [R][n_q][H][K]; slot_block / slot_stamp [R][H][K] (not modified).
     Returns dict with new slot_block, slot_stamp and plan_count [R][H],
@@ -138,12 +140,15 @@ def select_plan(topk_idx, slot_block, slot_stamp, step: int, cap: int, pred_row:
     blk = _i32(slot_block).copy()
     stp = _i32(slot_stamp).copy()
     assert blk.shape == (R, H, K) and stp.shape == (R, H, K)
+    ins = None if ins_blk is None else _i32(ins_blk)
+    assert ins is None or ins.shape == (R,)
     cnt = np.empty((R, H), dtype=np.int32)
     src = np.empty((R, H, K), dtype=np.int32)
     dst = np.empty((R, H, K), dtype=np.int32)
     ev = np.empty((R, H, K), dtype=np.int32)
     _check(_load().oro_select_plan(R, H, nq, int(pred_row), K, _p(t, _i32p), _p(blk, _i32p),
-                                   _p(stp, _i32p), int(step), int(cap), _p(cnt, _i32p),
+                                   _p(stp, _i32p), int(step), int(cap),
+                                   None if ins is None else _p(ins, _i32p), _p(cnt, _i32p),
                                    _p(src, _i32p), _p(dst, _i32p), _p(ev, _i32p)),
            "select_plan")
     return {"slot_block": blk, "slot_stamp": stp, "plan_count": cnt, "plan_src": src,

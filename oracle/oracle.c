@@ -206,6 +206,17 @@ static int victim_cmp(const void* pa, const void* pb) {
  *   pair i < n: src = missing[i], dst = victims[i], evicted = old block;
  *            the slot takes the new block with stamp = step.
  * Everything else stays as it was.  Plan entries i >= n are set to -1.
+ *
+ * Newly generated block (ins_blk[r] >= 0, optional): after the admissions the
+ * block completed by request r's last token joins every KV head's resident
+ * set, outside the cap.  If it is already resident its slot's stamp becomes
+ * step; otherwise it replaces the slot with the smallest (stamp, slot) and is
+ * recorded as plan entry n (count n + 1).  If that slot was itself admitted by
+ * this plan (every slot then carries stamp = step), the insertion takes over
+ * that entry instead: its source becomes the new block and the count stays.
+ * [v2] §3.2.1 (newly generated blocks replace existing entries independently
+ * for each KV head); the victim order is the plan's own (least recently
+ * selected first).
  * [reader] paragraphs on the capped eviction policy (intersect, rank by
  * last-selected step, pair admitted blocks with eviction targets, at most C
  * pairs per KV head) and on partial transfer (first working set from the
@@ -214,8 +225,9 @@ static int victim_cmp(const void* pa, const void* pb) {
  */
 int oro_select_plan(int R, int H, int n_q, int pred_row, int K,
                     const int32_t* topk_idx, int32_t* slot_block,
-                    int32_t* slot_stamp, int step, int cap, int32_t* plan_count,
-                    int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted) {
+                    int32_t* slot_stamp, int step, int cap, const int32_t* ins_blk,
+                    int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
+                    int32_t* plan_evicted) {
     if (R <= 0 || H <= 0 || n_q <= 0 || K <= 0 || pred_row < 0 || pred_row >= n_q ||
         cap < 0 || !topk_idx || !slot_block || !slot_stamp || !plan_count || !plan_src ||
         !plan_dst)
@@ -275,6 +287,32 @@ int oro_select_plan(int R, int H, int n_q, int pred_row, int K,
                 if (plan_evicted) plan_evicted[po + i] = blk[dst];
                 blk[dst] = missing[i];
                 stamp[dst] = step;
+            }
+            const int32_t ins = ins_blk ? ins_blk[r] : -1;
+            if (ins >= 0) {
+                int at = -1;
+                for (int s = 0; s < K; ++s)
+                    if (blk[s] == ins) at = s;
+                if (at >= 0) {
+                    stamp[at] = step;
+                } else {
+                    int v = 0;
+                    for (int s = 1; s < K; ++s)
+                        if (stamp[s] < stamp[v] || (stamp[s] == stamp[v] && s < v)) v = s;
+                    int entry = -1;
+                    for (int i = 0; i < n; ++i)
+                        if (plan_dst[po + i] == v) entry = i;
+                    if (entry >= 0) {
+                        plan_src[po + entry] = ins;
+                    } else {
+                        plan_src[po + n] = ins;
+                        plan_dst[po + n] = v;
+                        if (plan_evicted) plan_evicted[po + n] = blk[v];
+                        ++n;
+                    }
+                    blk[v] = ins;
+                    stamp[v] = step;
+                }
             }
             plan_count[(size_t)r * H + g] = n;
             free(hit);

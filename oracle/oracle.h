@@ -49,8 +49,9 @@ int oro_topk(int R, int n_q, int H, int n_blk_max, const double* scores,
 
 int oro_select_plan(int R, int H, int n_q, int pred_row, int K,
                     const int32_t* topk_idx, int32_t* slot_block,
-                    int32_t* slot_stamp, int step, int cap, int32_t* plan_count,
-                    int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted);
+                    int32_t* slot_stamp, int step, int cap, const int32_t* ins_blk,
+                    int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
+                    int32_t* plan_evicted);
 
 int oro_copy_blocks(int R, int H, int n_blk_max, int K, long tile_bytes,
                     const uint8_t* host_k, const uint8_t* host_v,

@@ -52,12 +52,13 @@ def test_topk_equals_full_sort(n, k, levels):
 
 
 # ---------------------------------------------------------------- plan
-def _plan_one(P, blk, stamp, step, cap):
+def _plan_one(P, blk, stamp, step, cap, ins=None):
     R, H, K = 1, 1, len(blk)
     t = np.array(P, dtype=np.int32).reshape(1, 1, 1, K)
     return oracle.select_plan(t, np.array(blk, dtype=np.int32).reshape(R, H, K),
                               np.array(stamp, dtype=np.int32).reshape(R, H, K), step, cap,
-                              pred_row=0)
+                              pred_row=0,
+                              ins_blk=None if ins is None else np.array([ins], np.int32))
 
 
 def test_plan_hand_sequence():
@@ -85,6 +86,85 @@ def test_plan_hand_cases(name):
         assert out["plan_dst"][0, 0].tolist() == ex["dst"]
     assert out["slot_block"][0, 0].tolist() == ex["expected_block"]
     assert out["slot_stamp"][0, 0].tolist() == ex["expected_stamp"]
+
+
+@pytest.mark.parametrize("name", ["plan_insert_basic", "plan_insert_resident",
+                                  "plan_insert_over_admission"])
+def test_plan_insert_hand_cases(name):
+    ex = GOLD[name]
+    out = _plan_one(ex["P"], ex["slot_block"], ex["slot_stamp"], ex["step"], ex["cap"], ex["ins"])
+    assert int(out["plan_count"][0, 0]) == ex["count"], ex["derivation"]
+    assert out["plan_src"][0, 0].tolist() == ex["src"]
+    assert out["plan_dst"][0, 0].tolist() == ex["dst"]
+    assert out["plan_evicted"][0, 0].tolist() == ex["evicted"]
+    assert out["slot_block"][0, 0].tolist() == ex["expected_block"]
+    assert out["slot_stamp"][0, 0].tolist() == ex["expected_stamp"]
+
+
+def test_plan_insert_none_is_the_plain_plan():
+    for step, topk, blk, stamp in _random_history(9, 8, 30, 2, steps=6, churn=0.3):
+        pr = 0 if step == 0 else 1
+        a = oracle.select_plan(topk, blk, stamp, step, 2, pred_row=pr)
+        b = oracle.select_plan(topk, blk, stamp, step, 2, pred_row=pr,
+                               ins_blk=-np.ones(topk.shape[0], np.int32))
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k])
+
+
+def _set_based_insert(pairs, blk, stamp, step, ins):
+    """The new block after the plan, written with lists: refresh if resident,
+    else take the oldest (stamp, slot); an entry that admitted into that slot
+    is taken over."""
+    blk, stamp, pairs = list(blk), list(stamp), list(pairs)
+    if ins in blk:
+        stamp[blk.index(ins)] = step
+        return pairs, blk, stamp
+    v = min(range(len(blk)), key=lambda s: (stamp[s], s))
+    hit = [i for i, p in enumerate(pairs) if p[1] == v]
+    if hit:
+        i = hit[0]
+        pairs[i] = (ins, v, pairs[i][2])
+    else:
+        pairs.append((ins, v, blk[v]))
+    blk[v] = ins
+    stamp[v] = step
+    return pairs, blk, stamp
+
+
+@pytest.mark.parametrize("seed,K,n_blocks,cap", [(11, 8, 20, 2), (12, 16, 64, 4), (13, 4, 6, 1),
+                                                  (14, 32, 200, 16), (15, 4, 50, 0)])
+def test_plan_insert_matches_set_formulation_and_invariants(seed, K, n_blocks, cap):
+    rng = np.random.default_rng(seed)
+    for step, topk, blk, stamp in _random_history(seed, K, n_blocks, cap, steps=10, churn=0.3):
+        pred_row = 0 if step == 0 else 1
+        R, _, H, _ = topk.shape
+        # a fresh block id per request (beyond every scored block), some requests without
+        ins = np.where(rng.random(R) < 0.7, n_blocks + step * R + np.arange(R), -1).astype(np.int32)
+        if step % 3 == 2:  # an already resident block now and then
+            ins[0] = blk[0, 0, 0]
+        out = oracle.select_plan(topk, blk, stamp, step, cap, pred_row=pred_row, ins_blk=ins)
+        for r in range(R):
+            for h in range(H):
+                P = topk[r, pred_row, h].tolist()
+                b0, s0 = blk[r, h].tolist(), stamp[r, h].tolist()
+                pairs, nb, ns = _set_based_plan(P, b0, s0, step, cap)
+                if ins[r] >= 0:
+                    pairs, nb, ns = _set_based_insert(pairs, nb, ns, step, int(ins[r]))
+                n = int(out["plan_count"][r, h])
+                got = list(zip(out["plan_src"][r, h, :n].tolist(), out["plan_dst"][r, h, :n].tolist(),
+                               out["plan_evicted"][r, h, :n].tolist()))
+                assert got == pairs
+                assert out["slot_block"][r, h].tolist() == nb
+                assert out["slot_stamp"][r, h].tolist() == ns
+                new = nb
+                live = [b for b in new if b >= 0]
+                assert len(live) == len(set(live)), "duplicate resident block"
+                if ins[r] >= 0:
+                    assert int(ins[r]) in new
+                    seeding = any(b == -1 for b in b0)
+                    if not seeding:
+                        assert n <= cap + 1
+                assert all(x == -1 for x in out["plan_src"][r, h, n:].tolist())
 
 
 def _set_based_plan(P, blk, stamp, step, cap):

@@ -168,10 +168,19 @@ int oasis_score_topk(const oasis_shape* s, const void* q, const void* summaries,
  * capped eviction policy and on partial transfer at admission; [v2] §3.3.2
  * (at most f_HBM*K admissions per head per step once the first working set
  * is seeded; exactly K resident blocks per head).
+ * Newly completed block (ins_blk[r] >= 0): after the admissions, the block
+ * that request r's last token completed joins every KV head's set outside
+ * the cap ([v2] §3.2.1: newly generated blocks replace existing entries
+ * independently per KV head).  If resident, its slot's stamp becomes `step`;
+ * otherwise it takes the slot with the smallest (stamp, slot) and is plan
+ * entry n (count n + 1), or, when that slot was admitted by this very plan,
+ * that entry's source becomes the new block (count unchanged).
  *   topk_idx         [R][n_q][H][K] int32 (distinct entries per row; -1 pad)
  *   slot_block_in    [R][H][K] int32 resident block per slot (-1 = empty)
  *   slot_stamp_in    [R][H][K] int32 last step the slot's block was selected
  *   slot_block_out, slot_stamp_out  [R][H][K] outputs; may alias the inputs
+ *   ins_blk          [R] int32 block each request just completed (-1 none),
+ *                    or NULL for none; a block id the top-K rows never hold
  *   plan_count       [R][H] int32 output
  *   plan_src, plan_dst [R][H][K] int32 outputs
  *   plan_evicted     [R][H][K] int32 output or NULL
@@ -183,8 +192,8 @@ int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q, int32_t pr
                       int32_t top_k, const int32_t* topk_idx, const int32_t* slot_block_in,
                       const int32_t* slot_stamp_in, int32_t* slot_block_out,
                       int32_t* slot_stamp_out, int32_t step, int32_t cap,
-                      int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
-                      int32_t* plan_evicted, hipStream_t stream);
+                      const int32_t* ins_blk, int32_t* plan_count, int32_t* plan_src,
+                      int32_t* plan_dst, int32_t* plan_evicted, hipStream_t stream);
 
 /*
  * Gather planned block-head tiles into the resident store: for every unit u
@@ -285,7 +294,7 @@ size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max, i
  *                    topk_idx, topk_score, scores)
  *   oasis_select_plan(R, H, n_q, pred_row, top_k, topk_idx, slot_block_in,
  *                     slot_stamp_in, slot_block_out, slot_stamp_out, step,
- *                     cap, plan_count, plan_src, plan_dst, plan_evicted)
+ *                     cap, ins_blk, plan_count, plan_src, plan_dst, plan_evicted)
  * run in that order (arguments as documented there; the resident set holds
  * K = top_k slots per KV head).  In the full-cache layout (unit_stride =
  * n_blk_max) the caller passes slot_block_in as tile_table; the plan's outputs
@@ -301,7 +310,8 @@ int oasis_lookahead_step(const oasis_shape* s, const void* q, const void* summar
                          int32_t* topk_idx, float* topk_score, float* scores,
                          const int32_t* slot_block_in, const int32_t* slot_stamp_in,
                          int32_t* slot_block_out, int32_t* slot_stamp_out, int32_t step,
-                         int32_t cap, int32_t pred_row, int32_t* plan_count, int32_t* plan_src,
+                         int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+                         int32_t* plan_count, int32_t* plan_src,
                          int32_t* plan_dst, int32_t* plan_evicted, const void* k_tiles,
                          const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
                          int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len,

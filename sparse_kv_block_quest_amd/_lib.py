@@ -95,7 +95,7 @@ def load() -> ctypes.CDLL:
     lib.oasis_score_topk_workspace.restype = _sz
     lib.oasis_score_topk.argtypes = [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
     lib.oasis_select_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
-                                      _i32, _i32, _vp, _vp, _vp, _vp, _vp]
+                                      _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.oasis_copy_blocks.argtypes = [_shp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
     lib.oasis_sparse_attn_workspace.argtypes = [_shp, _i32]
     lib.oasis_sparse_attn_workspace.restype = _sz
@@ -108,7 +108,7 @@ def load() -> ctypes.CDLL:
     lib.oasis_lookahead_step_workspace.restype = _sz
     lib.oasis_lookahead_step.argtypes = (
         [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp,          # q .. scores
-         _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,  # slots .. plan
+         _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan",

@@ -11,7 +11,8 @@ namespace oasis {
 __global__ void __launch_bounds__(kNT)
 plan_kernel(int H, int NQ, int pred_row, int K, const int32_t* __restrict__ topk_idx,
             const int32_t* slot_blk_in, const int32_t* slot_stamp_in, int32_t* slot_blk_out,
-            int32_t* slot_stamp_out, int step, int cap, int32_t* __restrict__ plan_count,
+            int32_t* slot_stamp_out, int step, int cap, const int32_t* __restrict__ ins_blk,
+            int32_t* __restrict__ plan_count,
             int32_t* __restrict__ plan_src, int32_t* __restrict__ plan_dst,
             int32_t* __restrict__ plan_evicted) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -26,14 +27,15 @@ plan_kernel(int H, int NQ, int pred_row, int K, const int32_t* __restrict__ topk
     const size_t so = (size_t)u * K;
     plan_load(slot_blk_in + so, slot_stamp_in + so, K, L);
     __syncthreads();
-    plan_unit(P, K, slot_blk_out + so, slot_stamp_out + so, step, cap, plan_count + u,
-              plan_src + so, plan_dst + so, plan_evicted ? plan_evicted + so : nullptr, L);
+    plan_unit(P, K, slot_blk_out + so, slot_stamp_out + so, step, cap, ins_blk ? ins_blk[r] : -1,
+              plan_count + u, plan_src + so, plan_dst + so,
+              plan_evicted ? plan_evicted + so : nullptr, L);
 }
 
 static size_t plan_lds_bytes(int K) {
     const size_t k4 = (size_t)pad4(K);
     auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
-    return a16(k4 * 4) * 9 + a16(k4 * 8) + a16(64);
+    return a16(k4 * 4) * 10 + a16(k4 * 8) + a16(64) + a16(16);
 }
 
 // ------------------------------------------------------------ launching
@@ -342,8 +344,9 @@ extern "C" int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q,
                                  int32_t top_k, const int32_t* topk_idx,
                                  const int32_t* slot_block_in, const int32_t* slot_stamp_in,
                                  int32_t* slot_block_out, int32_t* slot_stamp_out, int32_t step,
-                                 int32_t cap, int32_t* plan_count, int32_t* plan_src,
-                                 int32_t* plan_dst, int32_t* plan_evicted, hipStream_t stream) {
+                                 int32_t cap, const int32_t* ins_blk, int32_t* plan_count,
+                                 int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted,
+                                 hipStream_t stream) {
     if (batch <= 0 || n_kv_heads <= 0 || (n_q != 1 && n_q != 2) || pred_row < 0 ||
         pred_row >= n_q || top_k <= 0 || top_k > kMaxTopK || cap < 0)
         return OASIS_EINVAL;
@@ -354,8 +357,8 @@ extern "C" int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q,
     if (U > 0x7fffffffLL) return OASIS_EINVAL;
     hipLaunchKernelGGL(plan_kernel, dim3((unsigned)U), dim3(kNT), plan_lds_bytes(top_k), stream,
                        n_kv_heads, n_q, pred_row, top_k, topk_idx, slot_block_in, slot_stamp_in,
-                       slot_block_out, slot_stamp_out, step, cap, plan_count, plan_src, plan_dst,
-                       plan_evicted);
+                       slot_block_out, slot_stamp_out, step, cap, ins_blk, plan_count, plan_src,
+                       plan_dst, plan_evicted);
     return launch_status();
 }
 
@@ -383,7 +386,8 @@ extern "C" int oasis_lookahead_step(
     const oasis_shape* s, const void* q, const void* summaries, int32_t n_blk_max,
     const int32_t* n_blk, int32_t top_k, int32_t* topk_idx, float* topk_score, float* scores,
     const int32_t* slot_block_in, const int32_t* slot_stamp_in, int32_t* slot_block_out,
-    int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, int32_t* plan_count,
+    int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+    int32_t* plan_count,
     int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted, const void* k_tiles,
     const void* v_tiles, const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
     const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out, float* lse,
@@ -417,6 +421,7 @@ extern "C" int oasis_lookahead_step(
     a.pred_row = pred_row;
     a.step = step;
     a.cap = cap;
+    a.ins_blk = ins_blk;
     a.slot_blk_in = slot_block_in;
     a.slot_stamp_in = slot_stamp_in;
     a.slot_blk_out = slot_block_out;

@@ -69,6 +69,7 @@ struct StepArgs {
     int scores_lds;      // NC = 1 and the unit's scores fit in LDS
     // plan
     int do_plan, pred_row, step, cap;
+    const int32_t* ins_blk;  // [R] newly completed block per request (-1 none) or null
     const int32_t* slot_blk_in;
     const int32_t* slot_stamp_in;
     int32_t* slot_blk_out;
@@ -168,7 +169,7 @@ __host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_sco
     size_t b = a16(NQ * 2 * D * 4);                                     // pn
     b += a16(NQ * 512 * 4) + a16(4 * 2 * 4) + a16(16 * 4);             // hist, scan, sh
     b += a16(NQ * kp * 4) * 2 + a16(kp * 4);                            // sel key/idx, P
-    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 4 + a16(64);     // plan
+    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 5 + a16(64) + a16(16);  // plan
     b += a16((size_t)n_scores * 4);                                     // scores
     return b;
 }
@@ -535,7 +536,9 @@ struct PlanLds {
     int* victim_of_rank;   // [K4]
     int* new_blk;          // [K4]
     int* new_stamp;        // [K4]
+    int* rank_of_slot;     // [K4] victim rank of a slot (K for hits)
     uint32_t* scanbuf;     // [4][2]
+    unsigned long long* ins_key;  // [2]: oldest (stamp, slot) key; slot holding the new block
 };
 
 __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
@@ -549,7 +552,9 @@ __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
     L.victim_of_rank = cur.take<int>(K4);
     L.new_blk = cur.take<int>(K4);
     L.new_stamp = cur.take<int>(K4);
+    L.rank_of_slot = cur.take<int>(K4);
     L.scanbuf = cur.take<uint32_t>(16);
+    L.ins_key = cur.take<unsigned long long>(2);
     return L;
 }
 
@@ -566,10 +571,13 @@ __device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* 
 }
 
 // Capped least-recently-selected plan of one unit from the ranked predicted
-// list P (LDS, -1 padded) and the staged slot tables.  The outputs may alias
-// the slot tables the stage was loaded from.
+// list P (LDS, -1 padded) and the staged slot tables, then the insertion of
+// the request's newly completed block `ins` (-1 = none): outside the cap it
+// refreshes its slot if resident, else takes the slot with the smallest
+// (stamp, slot) after the admissions, taking over that slot's admission if it
+// had one.  The outputs may alias the slot tables the stage was loaded from.
 __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_out, int step,
-                          int cap, int32_t* cnt_out, int32_t* src_out, int32_t* dst_out,
+                          int cap, int ins, int32_t* cnt_out, int32_t* src_out, int32_t* dst_out,
                           int32_t* ev_out, const PlanLds& L) {
     const int tid = threadIdx.x;
     const int K4 = pad4(K);
@@ -631,6 +639,9 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
                 r += (x.x < e) + (x.y < e);
             }
             L.victim_of_rank[r] = s;
+            L.rank_of_slot[s] = r;
+        } else {
+            L.rank_of_slot[s] = K;
         }
         L.new_blk[s] = L.blk[s];
         L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
@@ -639,22 +650,59 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     const int n_victims = K - (int)n_hits;
     int n = min((int)n_missing, n_victims);
     if (!seeding) n = min(n, cap);
+    for (int i = tid; i < n; i += kNT) {
+        const int dst = L.victim_of_rank[i];
+        L.new_blk[dst] = L.missing_of_rank[i];
+        L.new_stamp[dst] = step;
+    }
+    if (ins >= 0 && tid == 0) {
+        L.ins_key[0] = ~0ull;
+        L.ins_key[1] = ~0ull;
+    }
+    lds_barrier();
+    if (ins >= 0) {  // uniform: one value per request
+        for (int s = tid; s < K; s += kNT) {
+            // Stamps are >= -1: the offset keeps the unsigned order of (stamp, slot).
+            const unsigned long long key =
+                ((unsigned long long)((long long)L.new_stamp[s] + 0x80000000LL) << 32) | (unsigned)s;
+            atomicMin(&L.ins_key[0], key);
+            if (L.new_blk[s] == ins) L.ins_key[1] = (unsigned)s;  // at most one slot
+        }
+        lds_barrier();
+        if (tid == 0) {
+            const unsigned long long at = L.ins_key[1];
+            if (at != ~0ull) {
+                L.new_stamp[(int)at] = step;
+            } else {
+                const int v = (int)(L.ins_key[0] & 0xffffffffu);
+                const int e = L.rank_of_slot[v];
+                if (e < n) {  // v was admitted by this plan: its entry brings the new block
+                    L.missing_of_rank[e] = ins;
+                } else {
+                    L.missing_of_rank[n] = ins;
+                    L.victim_of_rank[n] = v;
+                    ++n;
+                }
+                L.new_blk[v] = ins;
+                L.new_stamp[v] = step;
+            }
+            L.scanbuf[12] = (uint32_t)n;
+        }
+        lds_barrier();
+        n = (int)L.scanbuf[12];
+    }
     for (int i = tid; i < K; i += kNT) {
         if (i < n) {
             const int dst = L.victim_of_rank[i];
-            const int src = L.missing_of_rank[i];
-            src_out[i] = src;
+            src_out[i] = L.missing_of_rank[i];
             dst_out[i] = dst;
             if (ev_out) ev_out[i] = L.blk[dst];
-            L.new_blk[dst] = src;
-            L.new_stamp[dst] = step;
         } else {
             src_out[i] = -1;
             dst_out[i] = -1;
             if (ev_out) ev_out[i] = -1;
         }
     }
-    lds_barrier();
     for (int s = tid; s < K; s += kNT) {
         blk_out[s] = L.new_blk[s];
         stamp_out[s] = L.new_stamp[s];
@@ -687,7 +735,7 @@ __device__ void select_unit(const StepArgs& a, int u, const float* sc, size_t rs
     if (!a.do_plan) return;
     const size_t so = (size_t)u * a.K;
     plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
-              a.plan_count + u, a.plan_src + so, a.plan_dst + so,
+              a.ins_blk ? a.ins_blk[r] : -1, a.plan_count + u, a.plan_src + so, a.plan_dst + so,
               a.plan_evicted ? a.plan_evicted + so : nullptr, Pl);
 }
 

@@ -169,13 +169,19 @@ def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
 
 def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: torch.Tensor,
                 step: int, cap: int, pred_row: int = 1, slot_block_out=None,
-                slot_stamp_out=None, plan=None, want_evicted: bool = True, stream=None):
-    """Capped least-recently-selected plan.  Slot tables are updated in place
-    unless *_out tensors are given.  Returns dict of plan tensors."""
+                slot_stamp_out=None, plan=None, want_evicted: bool = True,
+                ins_blk: torch.Tensor | None = None, stream=None):
+    """Capped least-recently-selected plan, plus the insertion of each request's
+    newly completed block (``ins_blk`` [R] int32, -1 = none).  Slot tables are
+    updated in place unless *_out tensors are given.  Returns dict of plan tensors."""
     lib = _lib.load()
     R, n_q, H, K = topk_idx.shape
     for t, n in ((topk_idx, "topk_idx"), (slot_block, "slot_block"), (slot_stamp, "slot_stamp")):
         _i32(t, n)
+    if ins_blk is not None:
+        _i32(ins_blk, "ins_blk")
+        if ins_blk.shape != (R,):
+            raise ValueError("ins_blk must be [R]")
     if slot_block.shape != (R, H, K) or slot_stamp.shape != (R, H, K):
         raise ValueError("slot tables must be [R][H][K]")
     bo = slot_block if slot_block_out is None else slot_block_out
@@ -192,7 +198,7 @@ def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: to
     check("oasis_select_plan",
           lib.oasis_select_plan(R, H, n_q, int(pred_row), K, _ptr(topk_idx), _ptr(slot_block),
                                 _ptr(slot_stamp), _ptr(bo), _ptr(so), int(step), int(cap),
-                                _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
+                                _ptr(ins_blk), _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
                                 _ptr(plan["plan_dst"]), _ptr(plan.get("plan_evicted")),
                                 _stream(stream)))
     return plan
@@ -340,7 +346,7 @@ class PreparedStep:
     for decode loops where Python marshalling would otherwise cost as much as
     the kernel."""
 
-    _Q, _STEP, _BI, _SI, _BO, _SO, _TBL = 1, 13, 9, 10, 11, 12, 22
+    _Q, _STEP, _BI, _SI, _BO, _SO, _INS, _TBL = 1, 13, 9, 10, 11, 12, 16, 23
 
     def __init__(self, args, res, lib):
         self.args = args
@@ -370,6 +376,7 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                    step: int, cap: int, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
                    tile_table: torch.Tensor, unit_stride: int, block_size: int,
                    pred_row: int = 1, n_blk: torch.Tensor | None = None,
+                   ins_blk: torch.Tensor | None = None,
                    tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
                    scale: float = 0.0, want_scores: bool = False, want_lse: bool = True,
                    want_evicted: bool = True, opts: OasisStepOpts | None = None,
@@ -434,13 +441,17 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                                                  ctypes.byref(opts) if opts is not None else None)
         b["workspace"] = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
     ws = b["workspace"]
-    for t, n in ((n_blk, "n_blk"), (tail_tile, "tail_tile"), (tail_len, "tail_len")):
+    for t, n in ((n_blk, "n_blk"), (tail_tile, "tail_tile"), (tail_len, "tail_len"),
+                 (ins_blk, "ins_blk")):
         if t is not None:
             _i32(t, n)
+    if ins_blk is not None and ins_blk.shape != (R,):
+        raise ValueError("ins_blk must be [R]")
     args = [ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk), K,
             _ptr(res["topk_idx"]), _ptr(res["topk_score"]), _ptr(res["scores"]),
             _ptr(slot_block), _ptr(slot_stamp), _ptr(slot_block_out), _ptr(slot_stamp_out),
-            int(step), int(cap), int(pred_row), _ptr(res["plan_count"]), _ptr(res["plan_src"]),
+            int(step), int(cap), int(pred_row), _ptr(ins_blk), _ptr(res["plan_count"]),
+            _ptr(res["plan_src"]),
             _ptr(res["plan_dst"]), _ptr(res["plan_evicted"]), ctypes.c_void_p(kptr),
             ctypes.c_void_p(vptr),
             _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile), _ptr(tail_len),
@@ -449,5 +460,6 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             _stream(stream)]
     call = PreparedStep(args, res, lib)
     call._keep = (shp, opts, q, summaries, slot_block, slot_stamp, slot_block_out,
-                  slot_stamp_out, k_tiles, v_tiles, tile_table, n_blk, tail_tile, tail_len, ws)
+                  slot_stamp_out, k_tiles, v_tiles, tile_table, n_blk, tail_tile, tail_len, ins_blk,
+                  ws)
     return call

@@ -90,11 +90,14 @@ def test_argument_validation(lib):
                                 0, None) == _lib.OASIS_EWORKSPACE
     # plan: pred_row out of range, negative cap, K too large
     args = [FAKE] * 5
-    assert lib.oasis_select_plan(1, 2, 2, 2, 8, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
-    assert lib.oasis_select_plan(1, 2, 2, 1, 8, *args, 0, -1, FAKE, FAKE, FAKE, None, None) == E
-    assert lib.oasis_select_plan(1, 2, 2, 1, 2048, *args, 0, 1, FAKE, FAKE, FAKE, None, None) == E
-    assert lib.oasis_select_plan(1, 2, 2, 1, 8, None, *args[1:], 0, 1, FAKE, FAKE, FAKE, None,
+    assert lib.oasis_select_plan(1, 2, 2, 2, 8, *args, 0, 1, None, FAKE, FAKE, FAKE, None,
                                  None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 8, *args, 0, -1, None, FAKE, FAKE, FAKE, None,
+                                 None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 2048, *args, 0, 1, None, FAKE, FAKE, FAKE, None,
+                                 None) == E
+    assert lib.oasis_select_plan(1, 2, 2, 1, 8, None, *args[1:], 0, 1, None, FAKE, FAKE, FAKE,
+                                 None, None) == E
     # attention: workspace too small (split units), group too large, MFMA forced on fp32
     assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 64) > 0
     assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 64, 64, None, None, 0.0,
@@ -130,13 +133,14 @@ def _step(lib, s, **kw):
     """oasis_lookahead_step with every pointer FAKE unless overridden."""
     a = dict(q=FAKE, summ=FAKE, nb=8, n_blk=None, K=4, idx=FAKE, tsc=None, sc=None,
              bi=FAKE, si=FAKE, bo=ctypes.c_void_p(0x9000), so=ctypes.c_void_p(0xA000), step=1,
-             cap=2, pred=1, cnt=FAKE, src=FAKE, dst=FAKE, ev=None, kt=FAKE, vt=FAKE,
+             cap=2, pred=1, ins=None, cnt=FAKE, src=FAKE, dst=FAKE, ev=None, kt=FAKE, vt=FAKE,
              tbl=ctypes.c_void_p(0x100000), n_sel=4, stride=8, tt=None, tl=None, scale=0.0,
              out=FAKE, lse=None, opts=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return lib.oasis_lookahead_step(
         ctypes.byref(s), a["q"], a["summ"], a["nb"], a["n_blk"], a["K"], a["idx"], a["tsc"],
-        a["sc"], a["bi"], a["si"], a["bo"], a["so"], a["step"], a["cap"], a["pred"], a["cnt"],
+        a["sc"], a["bi"], a["si"], a["bo"], a["so"], a["step"], a["cap"], a["pred"], a["ins"],
+        a["cnt"],
         a["src"], a["dst"], a["ev"], a["kt"], a["vt"], a["tbl"], a["n_sel"], a["stride"],
         a["tt"], a["tl"], a["scale"], a["out"], a["lse"], a["opts"], a["ws"], a["wsb"], None)
 

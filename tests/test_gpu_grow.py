@@ -1,0 +1,103 @@
+"""GPU parity of decode with growing contexts: one token per request per step.
+
+Each step appends a synthetic key/value row to every request's active block
+(the model's KV write), builds the summaries of blocks that have become full,
+and runs the fused step with n_blk = full blocks before the active one, the
+active block as the always-attended tail, and ins_blk = the block the new token
+completed (it joins every KV head's resident set through the plan for the next
+step).  Lengths are staggered so requests complete blocks on different steps.
+Every step is checked against the oracle: scores, top-K, plan with the
+insertion, slot tables, and attention over resident blocks plus the tail.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_block_quest_amd import ops, synth
+from test_gpu_step import check_step, small
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+
+
+def run_grow(cuda, wl, L0, steps, opts=None, units=None):
+    dev = cuda
+    R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
+    nb = wl.n_blk  # store capacity in blocks
+    qf = synth.queries(wl, dev)
+    keys = synth.keys(wl, qf[:, 0], dev)
+    vt = synth.v_tiles(synth.values(wl, dev), B)
+    kt = keys.view(R, H, nb, B, D)
+    _, kt, vt = synth.interleave_kv(kt, vt)  # the interleaved store the bench uses
+    del keys
+    L = torch.tensor(L0, dtype=torch.int64, device=dev)
+    assert int(L.max()) + steps <= nb * B
+    summ = torch.zeros((R, H, nb, 2, D), dtype=wl.dtype, device=dev)
+    n_blk = (L // B).to(torch.int32)  # L0 tokens; the next token opens/extends a block
+    ops.build_summaries(kt, B, seq_len=(n_blk * B).to(torch.int32), out=summ)
+    q = qf.to(wl.dtype)
+    # seed from the prompt: full blocks only
+    idx, _, _ = ops.score_topk(q, summ, K, n_blk=n_blk)
+    blk = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    stamp = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+    ops.select_plan(idx, blk[0], stamp[0], 0, wl.cap, pred_row=0)
+    gen = synth.generator(wl.seed + 7, synth.S_MISC, dev)
+    gq = synth.generator(wl.seed + 8, synth.S_DRIFT, dev)
+    cur = qf
+    bufs = {}
+    ar = torch.arange(R, device=dev)
+    if units is None:
+        units = [(r, g) for r in range(R) for g in range(H)]
+    inserted = 0
+    for t in range(steps):
+        a, b = t % 2, 1 - t % 2
+        # the model's KV write: one token per request at position L
+        pos = L
+        bi, ti = (pos // B), (pos % B)
+        knew = torch.randn((R, H, D), generator=gen, device=dev).to(wl.dtype)
+        vnew = torch.randn((R, H, D), generator=gen, device=dev).to(wl.dtype)
+        kt[ar, :, bi, ti, :] = knew
+        vt[ar, :, bi, :, ti] = vnew
+        L = L + 1
+        act = ((L - 1) // B).to(torch.int32)
+        tail_len = (L - act.long() * B).to(torch.int32)
+        n_blk = act.clone()
+        ins = torch.where(tail_len == B, act, torch.full_like(act, -1))
+        inserted += int((ins >= 0).sum())
+        # summaries of blocks that became full since the last build
+        lo = max(int(n_blk.min()) - 1, 0)
+        ops.build_summaries(kt, B, seq_len=(n_blk * B).to(torch.int32), blk_begin=lo,
+                            blk_end=int(n_blk.max()), out=summ)
+        tt = act[:, None].expand(R, H).contiguous()
+        qs = cur.to(wl.dtype)
+        say(f"  grow step {t}: L={L.tolist()} ins={ins.tolist()}")
+        res = ops.lookahead_step(qs, summ, K, blk[a], stamp[a], blk[b], stamp[b], t + 1, wl.cap,
+                                 kt, vt, blk[a], nb, B, pred_row=1, n_blk=n_blk, ins_blk=ins,
+                                 tail_tile=tt, tail_len=tail_len, want_scores=True, opts=opts,
+                                 bufs=bufs)
+        torch.cuda.synchronize()
+        check_step(wl, qs, summ, kt, vt, blk[a], stamp[a], blk[b], stamp[b], res, t + 1,
+                   n_blk.cpu().numpy(), tt, tail_len, units, ins=ins)
+        # the completed block is resident for every head of its request
+        for r in range(R):
+            if int(ins[r]) >= 0:
+                assert bool((blk[b][r] == ins[r]).any(dim=1).all())
+        cur = synth.drift(cur[:, 0], wl.rho, gq)
+    assert inserted > 0, "the run completed no block"
+
+
+@pytest.mark.parametrize("case", [
+    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[700, 713, 725], steps=24, opts=None),
+    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[704, 719, 735], steps=18,
+         opts=(2, 2, 0)),
+])
+def test_grow_chain(cuda, case):
+    wl = small("qwen3-8b-1layer", **case["wl"])
+    say(f"growing contexts {case}")
+    o = None if case["opts"] is None else ops.step_opts(*case["opts"])
+    run_grow(cuda, wl, case["L0"], case["steps"], opts=o)

@@ -200,8 +200,9 @@ def test_score_topk_full_size(cuda, name, units):
 
 
 # ------------------------------------------------------------------ plan
-def test_plan_bitwise_over_history(cuda):
-    say("select_plan 12-step history, R=4 H=8 K=32 cap=4")
+@pytest.mark.parametrize("insert", [False, True])
+def test_plan_bitwise_over_history(cuda, insert):
+    say(f"select_plan 12-step history, R=4 H=8 K=32 cap=4, insertion={insert}")
     R, H, K, nb, cap = 4, 8, 32, 300, 4
     rng = np.random.default_rng(17)
     blk = torch.full((R, H, K), -1, dtype=torch.int32, device=cuda)
@@ -221,9 +222,16 @@ def test_plan_bitwise_over_history(cuda):
                 topk[r, 1, h, :len(row)] = row[::-1]
         pred_row = 0 if step == 0 else 1
         t = torch.from_numpy(topk).to(cuda)
-        plan = ops.select_plan(t, blk, stamp, step, cap, pred_row=pred_row)
+        ins = None
+        if insert:  # a fresh block for most requests; now and then one already resident
+            ins = np.where(rng.random(R) < 0.7, nb + step * R + np.arange(R), -1).astype(np.int32)
+            if step % 4 == 3:
+                ins[1] = blk_ref[1, 0, 0]
+        plan = ops.select_plan(t, blk, stamp, step, cap, pred_row=pred_row,
+                               ins_blk=None if ins is None else torch.from_numpy(ins).to(cuda))
         torch.cuda.synchronize()
-        ref = oracle.select_plan(topk, blk_ref, stamp_ref, step, cap, pred_row=pred_row)
+        ref = oracle.select_plan(topk, blk_ref, stamp_ref, step, cap, pred_row=pred_row,
+                                 ins_blk=ins)
         for key in ("plan_count", "plan_src", "plan_dst", "plan_evicted"):
             np.testing.assert_array_equal(plan[key].cpu().numpy(), ref[key], err_msg=key)
         np.testing.assert_array_equal(blk.cpu().numpy(), ref["slot_block"])

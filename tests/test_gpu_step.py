@@ -101,7 +101,7 @@ def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0
 
 
 def check_step(wl, q, summ, kt, vt, blk_in, stamp_in, blk_out, stamp_out, res, step, n_valid,
-               tt, tl, units):
+               tt, tl, units, ins=None):
     R, H, K, G = wl.R, wl.H, wl.K, wl.G
     q64 = np64(q)
     blk_in_np = blk_in.cpu().numpy()
@@ -123,7 +123,8 @@ def check_step(wl, q, summ, kt, vt, blk_in, stamp_in, blk_out, stamp_out, res, s
     np.testing.assert_array_equal(res["topk_score"].cpu().double().numpy(), v_ref)
     # plan on the kernel's top-K
     p_ref = oracle.select_plan(res["topk_idx"].cpu().numpy(), blk_in_np, stamp_in.cpu().numpy(),
-                               step, wl.cap, pred_row=1)
+                               step, wl.cap, pred_row=1,
+                               ins_blk=None if ins is None else ins.cpu().numpy())
     np.testing.assert_array_equal(blk_out.cpu().numpy(), p_ref["slot_block"])
     np.testing.assert_array_equal(stamp_out.cpu().numpy(), p_ref["slot_stamp"])
     for key in ("plan_count", "plan_src", "plan_dst", "plan_evicted"):

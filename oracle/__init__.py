@@ -37,6 +37,7 @@ def _load():
     lib = ctypes.CDLL(_LIB_PATH)
     lib.oro_build_summaries.argtypes = [ctypes.c_int] * 5 + [_f64p, _i32p, ctypes.c_int,
                                                                ctypes.c_int, _f64p]
+    lib.oro_append_kv.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p, _f64p, _i32p, _f64p]
     lib.oro_block_scores.argtypes = [ctypes.c_int] * 6 + [_f64p, _f64p, _i32p, _f64p]
     lib.oro_topk.argtypes = [ctypes.c_int] * 4 + [_f64p, _i32p, ctypes.c_int, _i32p, _f64p]
     lib.oro_select_plan.argtypes = [ctypes.c_int] * 5 + [_i32p, _i32p, _i32p, ctypes.c_int,
@@ -49,7 +50,8 @@ def _load():
                                                           _i32p, _i32p, ctypes.c_double,
                                                           _f64p, _f64p])
     lib.oro_num_threads.argtypes = []
-    for name in ("oro_build_summaries", "oro_block_scores", "oro_topk", "oro_select_plan",
+    for name in ("oro_build_summaries", "oro_append_kv", "oro_block_scores", "oro_topk",
+                 "oro_select_plan",
                  "oro_copy_blocks", "oro_sparse_attn", "oro_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -98,6 +100,25 @@ def build_summaries(keys, block_size: int, seq_len=None, blk_begin: int = 0,
                                        int(blk_begin), end, _p(summ, _f64p)),
            "build_summaries")
     return summ
+
+
+def append_kv(keys, values, k_new, v_new, pos, block_size: int, summ=None):
+    """Write each request's new token (position pos[r], -1 = none) for every KV
+    head; rebuild the summary of a block the token completes.
+
+    keys / values [R][H][L_max][D] token-major, k_new / v_new [R][H][D],
+    summ [R][H][L_max/B][2][D] or None.  Returns new (keys, values, summ).
+    """
+    keys, values = _f64(keys).copy(), _f64(values).copy()
+    R, H, Lmax, D = keys.shape
+    B = int(block_size)
+    if Lmax % B or values.shape != keys.shape:
+        raise ValueError("keys / values must be [R][H][L_max][D] with L_max a multiple of B")
+    s = None if summ is None else _f64(summ).copy()
+    _check(_load().oro_append_kv(R, H, D, B, Lmax // B, _p(keys, _f64p), _p(values, _f64p),
+                                 _p(_f64(k_new), _f64p), _p(_f64(v_new), _f64p),
+                                 _p(_i32(pos), _i32p), _p(s, _f64p)), "append_kv")
+    return keys, values, s
 
 
 def block_scores(q, summ, n_blk=None) -> np.ndarray:

@@ -82,6 +82,55 @@ int oro_build_summaries(int R, int H, int D, int B, int n_blk_max,
 }
 
 /*
+ * Token append of a growing context: request r's new token (position pos[r],
+ * skipped if negative) is written for every KV head into keys / values
+ * ([R][H][n_blk_max*B][D], token-major here).  When the token is the last of
+ * its block (pos % B == B - 1) and summ is given, that block's summary rows
+ * are rebuilt from its B keys (coordinate-wise min and max, as in
+ * oro_build_summaries).  [v2] §3.2.1 (newly generated blocks join the
+ * working set) and Fig. 6 (per-block min/max key summaries kept in HBM);
+ * [reader] paragraph on compressed-key updates.
+ */
+int oro_append_kv(int R, int H, int D, int B, int n_blk_max, double* keys, double* values,
+                  const double* k_new, const double* v_new, const int32_t* pos, double* summ) {
+    if (R <= 0 || H <= 0 || D <= 0 || B <= 0 || n_blk_max <= 0 || !keys || !values || !k_new ||
+        !v_new || !pos)
+        return -1;
+    for (int r = 0; r < R; ++r)
+        if (pos[r] >= (long)n_blk_max * B) return -1;
+    for (int r = 0; r < R; ++r) {
+        const long p = pos[r];
+        if (p < 0) continue;
+        const long b = p / B;
+        for (int g = 0; g < H; ++g) {
+            const size_t u = (size_t)r * H + g;
+            double* krow = keys + (u * (size_t)n_blk_max * B + (size_t)p) * D;
+            double* vrow = values + (u * (size_t)n_blk_max * B + (size_t)p) * D;
+            for (int d = 0; d < D; ++d) {
+                krow[d] = k_new[u * D + d];
+                vrow[d] = v_new[u * D + d];
+            }
+            if (summ && p % B == B - 1) {
+                const double* blk = keys + (u * (size_t)n_blk_max + (size_t)b) * (size_t)B * D;
+                double* mn = summ + ((u * (size_t)n_blk_max + (size_t)b) * 2 + 0) * D;
+                double* mx = summ + ((u * (size_t)n_blk_max + (size_t)b) * 2 + 1) * D;
+                for (int d = 0; d < D; ++d) {
+                    double lo = blk[d], hi = blk[d];
+                    for (int i = 1; i < B; ++i) {
+                        double v = blk[(size_t)i * D + d];
+                        if (v < lo) lo = v;
+                        if (v > hi) hi = v;
+                    }
+                    mn[d] = lo;
+                    mx[d] = hi;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
  * Upper-bound block score, per KV head g and query row j:
  *   s_b = sum over the query heads h of group g, sum over d, of
  *         max(q_hd * max_bd, q_hd * min_bd).

@@ -40,6 +40,9 @@ int oro_build_summaries(int R, int H, int D, int B, int n_blk_max,
                         const double* keys, const int32_t* seq_len,
                         int blk_begin, int blk_end, double* summ);
 
+int oro_append_kv(int R, int H, int D, int B, int n_blk_max, double* keys, double* values,
+                  const double* k_new, const double* v_new, const int32_t* pos, double* summ);
+
 int oro_block_scores(int R, int n_q, int Hq, int H, int D, int n_blk_max,
                      const double* q, const double* summ, const int32_t* n_blk,
                      double* scores);

@@ -156,3 +156,47 @@ def test_scores_past_n_blk_are_minus_inf():
     assert np.all(np.isneginf(sc[0, :, :, 3:]))
     assert np.all(np.isfinite(sc[0, :, :, :3]))
     assert np.all(np.isfinite(sc[1]))
+
+
+# ---------------------------------------------------------------- token append
+def test_append_fills_blocks_and_builds_their_summaries():
+    """Appending a context token by token writes each token in place, leaves a
+    block's summary alone until its last token arrives, then sets it to the
+    coordinate-wise min / max of the block's keys (numpy's reductions)."""
+    rng = np.random.default_rng(21)
+    R, H, D, B, nb = 2, 3, 8, 4, 5
+    keys = np.zeros((R, H, nb * B, D))
+    vals = np.zeros((R, H, nb * B, D))
+    summ = np.full((R, H, nb, 2, D), 7.0)
+    L = np.array([3, 9], np.int32)  # tokens already present
+    keys[:, :, :12] = rng.standard_normal((R, H, 12, D))
+    for _ in range(9):
+        kn, vn = rng.standard_normal((R, H, D)), rng.standard_normal((R, H, D))
+        pos = L.copy()
+        pos[1] = -1 if _ % 4 == 3 else pos[1]  # request 1 skips some steps
+        before = summ.copy()
+        keys, vals, summ = oracle.append_kv(keys, vals, kn, vn, pos, B, summ)
+        for r in range(R):
+            if pos[r] < 0:
+                np.testing.assert_array_equal(summ[r], before[r])
+                continue
+            np.testing.assert_array_equal(keys[r, :, pos[r]], kn[r])
+            np.testing.assert_array_equal(vals[r, :, pos[r]], vn[r])
+            b = pos[r] // B
+            if pos[r] % B == B - 1:
+                blk = keys[r, :, b * B:(b + 1) * B]
+                np.testing.assert_array_equal(summ[r, :, b, 0], blk.min(axis=1))
+                np.testing.assert_array_equal(summ[r, :, b, 1], blk.max(axis=1))
+            else:
+                np.testing.assert_array_equal(summ[r, :, b], before[r, :, b])
+            L[r] += 1
+
+
+def test_append_without_summaries_and_bad_position():
+    keys = np.zeros((1, 1, 8, 2))
+    k, v, s = oracle.append_kv(keys, keys, np.ones((1, 1, 2)), np.full((1, 1, 2), 2.0),
+                               np.array([3], np.int32), 4)
+    assert s is None and k[0, 0, 3].tolist() == [1.0, 1.0] and v[0, 0, 3].tolist() == [2.0, 2.0]
+    with pytest.raises(ValueError):
+        oracle.append_kv(keys, keys, np.ones((1, 1, 2)), np.ones((1, 1, 2)),
+                         np.array([8], np.int32), 4)

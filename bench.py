@@ -53,6 +53,8 @@ def parse_args(argv=None):
                         "oasis_sparse_attn + oasis_score_topk + oasis_select_plan")
     p.add_argument("--pipeline", action="store_true",
                    help="pinned-host pipeline (use with --workload qwen3-8b-pipeline)")
+    p.add_argument("--grow", action="store_true",
+                   help="growing contexts: one token per request per step")
     p.add_argument("--kv-layout", choices=("interleaved", "split"), default="interleaved",
                    help="one K|V record per block-head, or separate K and V stores")
     p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
@@ -281,6 +283,123 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     return res
 
 
+# ----------------------------------------------------------------- growing contexts
+def run_grow(args, wl, torch, synth, ops):
+    """Decode with growing contexts: every layer-step appends one new token's key
+    and value per request to the layer's store with oasis_append_kv (which also
+    rebuilds the summaries of a block the token completes), then runs the fused
+    step with the active block as the always-attended tail and the
+    just-completed block inserted into every KV head's resident set.  Lengths
+    start staggered below the store's capacity (wl.L tokens) and grow by one
+    per step."""
+    dev = torch.device("cuda:0")
+    n_layers = wl.layers
+    impl = {"auto": ops.IMPL_AUTO, "valu": ops.IMPL_VALU, "mfma": ops.IMPL_MFMA}[args.impl]
+    layers, _ = setup_layers(wl, dev, n_layers, args.kv_layout == "interleaved", torch, synth,
+                             ops)
+    R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
+    T = args.warmup + args.steps
+    qseq = query_sequence(wl, dev, n_layers, T, torch, synth)
+    L0_host = [wl.L - 64 + (5 * r) % B for r in range(R)]
+    L0 = torch.tensor(L0_host, dtype=torch.int64, device=dev)
+    assert int(L0.max()) + T <= wl.L
+    # New tokens' keys and values, drawn before timing: [T][layers][R][H][D].
+    g = synth.generator(wl.seed + 99, synth.S_MISC, dev)
+    knew = torch.randn((T, n_layers, R, H, D), generator=g, device=dev).to(wl.dtype)
+    vnew = torch.randn((T, n_layers, R, H, D), generator=g, device=dev).to(wl.dtype)
+    # Per-step bookkeeping, shared by the layers (device buffers the prepared
+    # calls point at, rewritten in place).
+    n_blk = (L0 // B).to(torch.int32)
+    tail_tile = torch.zeros((R, H), dtype=torch.int32, device=dev)
+    tail_len = torch.zeros(R, dtype=torch.int32, device=dev)
+    ins = torch.full((R,), -1, dtype=torch.int32, device=dev)
+    idx = torch.empty((R, wl.n_q, H, K), dtype=torch.int32, device=dev)
+    blk = [[torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+           for _ in range(n_layers)]
+    stamp = [[torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
+             for _ in range(n_layers)]
+    for l in range(n_layers):
+        ops.score_topk(qseq[0, l], layers[l]["summ"], K, n_blk=n_blk,
+                       out=(idx, torch.empty((R, wl.n_q, H, K), device=dev), None,
+                            torch.zeros(1 << 20, dtype=torch.uint8, device=dev)))
+        ops.select_plan(idx, blk[l][0], stamp[l][0], 0, wl.cap, pred_row=0)
+    opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
+    bufs = {}
+    calls = [[ops.prepare_lookahead_step(
+        qseq[0, l], layers[l]["summ"], K, blk[l][p], stamp[l][p], blk[l][1 - p], stamp[l][1 - p],
+        0, wl.cap, layers[l]["keys"], layers[l]["vt"], blk[l][p], wl.n_blk, B, pred_row=1,
+        n_blk=n_blk, ins_blk=ins, tail_tile=tail_tile, tail_len=tail_len, want_evicted=False,
+        opts=opts, bufs=bufs) for p in range(2)] for l in range(n_layers)]
+    L = L0.clone()
+    pos = torch.zeros(R, dtype=torch.int32, device=dev)
+    # One prepared append per (step, layer): the token write and, for a token
+    # that completes its block, that block's summaries, in one launch.
+    appends = [[ops.prepare_append_kv(knew[t, l], vnew[t, l], pos, layers[l]["keys"],
+                                      layers[l]["vt"], B, summaries=layers[l]["summ"])
+                for l in range(n_layers)] for t in range(T)]
+    inserted = torch.zeros((), dtype=torch.int64, device=dev)
+
+    def step(t):
+        nonlocal L
+        pos.copy_(L)
+        L = L + 1
+        act = (L - 1) // B
+        tl = L - act * B
+        n_blk.copy_(act)
+        tail_len.copy_(tl)
+        tail_tile.copy_(act[:, None].expand(R, H))
+        ins.copy_(torch.where(tl == B, act, torch.full_like(act, -1)))
+        for l in range(n_layers):
+            appends[t][l]()
+            calls[l][t % 2](t + 1, qseq[t, l])
+        inserted.add_((ins >= 0).sum())
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    inserted.zero_()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record()
+    for t in range(args.warmup, T):
+        step(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    return {"total_ms": ev0.elapsed_time(ev1), "wall_s": time.perf_counter() - w0,
+            "inserted_per_step": float(inserted.item()) / args.steps,
+            "L_start": int(L0.min()), "L_end": int(L.max())}
+
+
+def report_grow(args, wl, g):
+    e = 2 if str(wl.dtype).endswith("bfloat16") else 4
+    n_ls = args.steps * wl.layers
+    units = wl.R * wl.H
+    per_ls = units * per_ls_alg(1, algo_bytes(wl, e))
+    ls_us = g["total_ms"] * 1000.0 / n_ls
+    line = {
+        "metric": "layer-steps/s (growing contexts: token append with summary update, "
+                  "scan+top-K+plan with insertion, sparse attn incl. active block)",
+        "value": round(n_ls / (g["total_ms"] / 1000.0), 2), "unit": "layer-steps/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(g["total_ms"] / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if e == 2 else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}, "
+                               f"contexts {g['L_start']}..{g['L_end']} tokens growing one per step",
+                   "batch": wl.R, "store_capacity": wl.L, "block": wl.B, "top_k_blocks": wl.K,
+                   "layers": wl.layers, "cap": wl.cap, "kv_layout": args.kv_layout},
+        "layer_step": {"us": round(ls_us, 2), "algo_bytes_fused": per_ls,
+                       "GBps_fused_bytes": round(per_ls / (ls_us * 1e-6) / 1e9, 1),
+                       "frac": round(per_ls / (ls_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "blocks_completed_per_step": round(g["inserted_per_step"], 3),
+        "host_issue_us_per_layer_step": round(g["wall_s"] * 1e6 / n_ls, 2),
+        "kernel_sources": kernel_source_hash(),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ----------------------------------------------------------------- pipeline leg
 PEAK_PCIE_GBS = 64.0  # PCIe Gen5 x16, one direction, nominal
 
@@ -505,6 +624,8 @@ def main(argv=None):
           file=sys.stderr, flush=True)
     if args.pipeline:
         return report_pipeline(args, wl, run_pipeline(args, wl, torch, synth, ops))
+    if args.grow:
+        return report_grow(args, wl, run_grow(args, wl, torch, synth, ops))
     g = run_gpu(args, wl, torch, synth, ops, _lib)
     print(f"# gpu timed region {g['total_ms']:.2f} ms", file=sys.stderr, flush=True)
 

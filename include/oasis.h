@@ -107,6 +107,30 @@ int oasis_build_summaries(const oasis_shape* s, const void* keys, int32_t n_blk_
                           void* summaries, hipStream_t stream);
 
 /*
+ * Append one token per request to a growing context: for every KV head, the
+ * new key row goes into row t of the K tile and the new value into column t
+ * of the V tile of block b, where b = pos[r] / B and t = pos[r] % B.  A token
+ * that completes its block (t == B - 1) also rebuilds that block's summary
+ * rows (coordinate-wise min and max of its B keys, exactly as
+ * oasis_build_summaries) when `summaries` is not NULL.  [v2] §3.2.1 (newly
+ * generated blocks join each KV head's working set) and Fig. 6 (per-block
+ * min/max key summaries kept in HBM); [reader] paragraph on compressed-key
+ * updates.  The context's other tokens must already be in the tiles.
+ *   s          shape; uses batch, n_kv_heads, head_dim, block_size, dtype,
+ *              tile_stride
+ *   k_new, v_new  [R][H][D] (dtype) the new token's key and value per KV head
+ *   pos        [R] int32 token position (< n_blk_max*B), or -1 to skip
+ *   k_tiles, v_tiles  the tile stores (as oasis_sparse_attn: K tiles [B][D],
+ *              V tiles [D][B]), tile (u*n_blk_max + b) for unit u; device
+ *              memory or mapped pinned host memory
+ *   summaries  [R][H][n_blk_max][2][D] (dtype) or NULL
+ * Errors: EINVAL, EUNSUPPORTED, EHIP.
+ */
+int oasis_append_kv(const oasis_shape* s, const void* k_new, const void* v_new,
+                    const int32_t* pos, void* k_tiles, void* v_tiles, int32_t n_blk_max,
+                    void* summaries, hipStream_t stream);
+
+/*
  * Workspaces.  When a unit's work is split over several workgroups (small
  * batches, long contexts), the partial results (block scores, attention
  * partials) go through a caller-owned scratch buffer and a second, small

@@ -32,6 +32,7 @@ EXPORTS = (
     "oasis_score_topk_workspace",
     "oasis_score_topk",
     "oasis_select_plan",
+    "oasis_append_kv",
     "oasis_copy_blocks",
     "oasis_sparse_attn_workspace",
     "oasis_sparse_attn",
@@ -97,6 +98,7 @@ def load() -> ctypes.CDLL:
     lib.oasis_select_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.oasis_copy_blocks.argtypes = [_shp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
+    lib.oasis_append_kv.argtypes = [_shp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]
     lib.oasis_sparse_attn_workspace.argtypes = [_shp, _i32]
     lib.oasis_sparse_attn_workspace.restype = _sz
     lib.oasis_sparse_attn.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp,
@@ -111,7 +113,7 @@ def load() -> ctypes.CDLL:
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
-    for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan",
+    for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan", "oasis_append_kv",
                  "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl",
                  "oasis_lookahead_step"):
         getattr(lib, name).restype = ctypes.c_int

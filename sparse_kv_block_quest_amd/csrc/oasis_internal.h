@@ -14,10 +14,12 @@ struct Elem;
 template <>
 struct Elem<OASIS_F32> {
     static constexpr int bytes = 4;
+    using type = uint32_t;  // raw bits of one element
 };
 template <>
 struct Elem<OASIS_BF16> {
     static constexpr int bytes = 2;
+    using type = uint16_t;
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

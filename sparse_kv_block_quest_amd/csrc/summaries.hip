@@ -128,3 +128,64 @@ extern "C" int oasis_build_summaries(const oasis_shape* s, const void* keys, int
     }
     return launch_status();
 }
+
+// ------------------------------------------------------------ token append
+// Growing contexts: request r's new token (position pos[r], skipped if
+// negative) goes into the K tile row and the V tile column of its block, for
+// every KV head; a token that completes its block also rebuilds that block's
+// summary rows (the same min / max as build_summaries_kernel).  Sources:
+// OasisKV paperpeel v2 text, §3.2.1 (newly generated blocks join each head's
+// working set) and Fig. 6 (per-block min / max key summaries in HBM).
+// One thread per (unit, dim): the K writes of a unit are one contiguous row;
+// the block's other B-1 keys of the column were written by earlier launches.
+template <int DT>
+__global__ void __launch_bounds__(256)
+append_kv_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
+                 const int32_t* __restrict__ pos, void* __restrict__ kt, void* __restrict__ vt,
+                 void* __restrict__ summ, int H, int D, int B, int n_blk_max, long long stride,
+                 long long total) {
+    using E = typename Elem<DT>::type;
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const long long u = i / D;
+    const int d = (int)(i - u * D);
+    const int r = (int)(u / H);
+    const int p = pos[r];
+    if (p < 0) return;
+    const int b = p / B, t = p - b * B;
+    const size_t tile = ((size_t)u * n_blk_max + b) * (size_t)stride;
+    const E kx = reinterpret_cast<const E*>(k_new)[i];
+    reinterpret_cast<E*>(kt)[tile + (size_t)t * D + d] = kx;
+    reinterpret_cast<E*>(vt)[tile + (size_t)d * B + t] = reinterpret_cast<const E*>(v_new)[i];
+    if (summ && t == B - 1) {
+        float lo = load_elem<DT>(&kx, 0), hi = lo;
+        for (int j = 0; j < B - 1; ++j) {
+            const float x = load_elem<DT>(kt, tile + (size_t)j * D + d);
+            lo = fminf(lo, x);
+            hi = fmaxf(hi, x);
+        }
+        const size_t so = ((size_t)u * n_blk_max + b) * 2 * D + d;
+        store_elem<DT>(summ, so, lo);
+        store_elem<DT>(summ, so + D, hi);
+    }
+}
+
+extern "C" int oasis_append_kv(const oasis_shape* s, const void* k_new, const void* v_new,
+                               const int32_t* pos, void* k_tiles, void* v_tiles,
+                               int32_t n_blk_max, void* summaries, hipStream_t stream) {
+    int st = check_shape(s);
+    if (st != OASIS_OK) return st;
+    if (!k_new || !v_new || !pos || !k_tiles || !v_tiles || n_blk_max <= 0) return OASIS_EINVAL;
+    const long long total = (long long)s->batch * s->n_kv_heads * s->head_dim;
+    const dim3 grid((unsigned)((total + 255) / 256));
+    const long long stride = tile_stride_of(s);
+    if (s->dtype == OASIS_F32)
+        hipLaunchKernelGGL(append_kv_kernel<OASIS_F32>, grid, dim3(256), 0, stream, k_new, v_new,
+                           pos, k_tiles, v_tiles, summaries, s->n_kv_heads, s->head_dim,
+                           s->block_size, n_blk_max, stride, total);
+    else
+        hipLaunchKernelGGL(append_kv_kernel<OASIS_BF16>, grid, dim3(256), 0, stream, k_new, v_new,
+                           pos, k_tiles, v_tiles, summaries, s->n_kv_heads, s->head_dim,
+                           s->block_size, n_blk_max, stride, total);
+    return launch_status();
+}

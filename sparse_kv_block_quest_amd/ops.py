@@ -134,6 +134,65 @@ def build_summaries(keys: torch.Tensor, block_size: int, seq_len: torch.Tensor |
     return out
 
 
+class PreparedAppend:
+    """A validated oasis_append_kv call; calling it appends the tokens held in
+    the prepared k_new / v_new / pos buffers (rewrite them in place between
+    calls)."""
+
+    def __init__(self, args, keep, lib):
+        self.args = args
+        self._keep = keep
+        self._fn = lib.oasis_append_kv
+
+    def __call__(self, stream=None) -> None:
+        a = self.args
+        if stream is not None:
+            a = a[:-1] + [_stream(stream)]
+        st = self._fn(*a)
+        if st != 0:
+            check("oasis_append_kv", st)
+
+
+def prepare_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor,
+                      k_tiles: torch.Tensor, v_tiles: torch.Tensor, block_size: int,
+                      summaries: torch.Tensor | None = None, stream=None) -> PreparedAppend:
+    """``append_kv`` with the argument checks done once."""
+    lib = _lib.load()
+    R, H, D = k_new.shape
+    B = int(block_size)
+    if v_new.shape != k_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must match")
+    _i32(pos, "pos")
+    if pos.shape != (R,):
+        raise ValueError("pos must be [R]")
+    if k_tiles.dim() < 4 or k_tiles.shape[:2] != (R, H):
+        raise ValueError("tile stores must be [R][H][n_blk_max][..tile..]")
+    nb = k_tiles.shape[2]
+    if v_tiles.shape[:3] != k_tiles.shape[:3] or k_tiles.dtype != k_new.dtype or \
+            v_tiles.dtype != k_new.dtype:
+        raise ValueError("k_tiles / v_tiles do not match the new tokens")
+    kptr, ks = _tile_store(k_tiles, "k_tiles", B * D)
+    vptr, vs = _tile_store(v_tiles, "v_tiles", B * D)
+    if ks != vs:
+        raise ValueError("k_tiles and v_tiles must share one tile stride")
+    if summaries is not None and (summaries.shape != (R, H, nb, 2, D) or
+                                  summaries.dtype != k_new.dtype):
+        raise ValueError("summaries must be [R][H][n_blk_max][2][D] in the tiles' dtype")
+    shp = _shape(R, 1, H, H, D, B, _dt(k_new), ks)
+    args = [ctypes.byref(shp), _ptr(k_new), _ptr(v_new), _ptr(pos), ctypes.c_void_p(kptr),
+            ctypes.c_void_p(vptr), nb, _ptr(summaries), _stream(stream)]
+    return PreparedAppend(args, (shp, k_new, v_new, pos, k_tiles, v_tiles, summaries), lib)
+
+
+def append_kv(k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor, k_tiles: torch.Tensor,
+              v_tiles: torch.Tensor, block_size: int, summaries: torch.Tensor | None = None,
+              stream=None) -> None:
+    """Write each request's new token (k_new / v_new [R][H][D], position pos [R],
+    -1 = skip) into the tile stores; a token completing its block rebuilds that
+    block's summary rows when ``summaries`` is given."""
+    prepare_append_kv(k_new, v_new, pos, k_tiles, v_tiles, block_size, summaries, stream)()
+
+
 def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                n_blk: torch.Tensor | None = None, want_scores: bool = False,
                stream=None, out=None):

@@ -169,3 +169,15 @@ def test_lookahead_step_validation(lib):
     assert _step(lib, s, wsb=0, **big) == _lib.OASIS_EWORKSPACE
     assert _step(lib, s, ws=None, **big) == _lib.OASIS_EWORKSPACE
     assert lib.oasis_lookahead_step_workspace(ctypes.byref(_shape(batch=0)), 8, 4, 4, None) == 0
+
+
+def test_append_kv_validation(lib):
+    s = _shape()
+    E = _lib.OASIS_EINVAL
+    assert lib.oasis_append_kv(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None, None) == E
+    assert lib.oasis_append_kv(ctypes.byref(s), None, FAKE, FAKE, FAKE, FAKE, 4, None, None) == E
+    assert lib.oasis_append_kv(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, 4, None, None) == E
+    assert lib.oasis_append_kv(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == E
+    bad = _shape(head_dim=96)
+    assert lib.oasis_append_kv(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None,
+                               None) == _lib.OASIS_EUNSUPPORTED

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from sparse_kv_block_quest_amd import ops, synth
 from test_gpu_step import check_step, small
 
@@ -23,9 +24,13 @@ def say(msg):
     print(msg, flush=True)
 
 
+def np64(t):
+    return t.detach().float().cpu().double().numpy()
 
 
-def run_grow(cuda, wl, L0, steps, opts=None, units=None):
+
+
+def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
     dev = cuda
     R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
     nb = wl.n_blk  # store capacity in blocks
@@ -61,18 +66,21 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None):
         bi, ti = (pos // B), (pos % B)
         knew = torch.randn((R, H, D), generator=gen, device=dev).to(wl.dtype)
         vnew = torch.randn((R, H, D), generator=gen, device=dev).to(wl.dtype)
-        kt[ar, :, bi, ti, :] = knew
-        vt[ar, :, bi, :, ti] = vnew
+        if kv_write == "append":  # the library's append (summary of a completed block included)
+            ops.append_kv(knew, vnew, pos.to(torch.int32), kt, vt, B, summaries=summ)
+        else:
+            kt[ar, :, bi, ti, :] = knew
+            vt[ar, :, bi, :, ti] = vnew
         L = L + 1
         act = ((L - 1) // B).to(torch.int32)
         tail_len = (L - act.long() * B).to(torch.int32)
         n_blk = act.clone()
         ins = torch.where(tail_len == B, act, torch.full_like(act, -1))
         inserted += int((ins >= 0).sum())
-        # summaries of blocks that became full since the last build
-        lo = max(int(n_blk.min()) - 1, 0)
-        ops.build_summaries(kt, B, seq_len=(n_blk * B).to(torch.int32), blk_begin=lo,
-                            blk_end=int(n_blk.max()), out=summ)
+        if kv_write != "append":  # summaries of blocks that became full since the last build
+            lo = max(int(n_blk.min()) - 1, 0)
+            ops.build_summaries(kt, B, seq_len=(n_blk * B).to(torch.int32), blk_begin=lo,
+                                blk_end=int(n_blk.max()), out=summ)
         tt = act[:, None].expand(R, H).contiguous()
         qs = cur.to(wl.dtype)
         say(f"  grow step {t}: L={L.tolist()} ins={ins.tolist()}")
@@ -92,12 +100,49 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None):
 
 
 @pytest.mark.parametrize("case", [
-    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[700, 713, 725], steps=24, opts=None),
+    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[700, 713, 725], steps=24, opts=None,
+         kv_write="append"),
     dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[704, 719, 735], steps=18,
-         opts=(2, 2, 0)),
+         opts=(2, 2, 0), kv_write="torch"),
 ])
 def test_grow_chain(cuda, case):
     wl = small("qwen3-8b-1layer", **case["wl"])
     say(f"growing contexts {case}")
     o = None if case["opts"] is None else ops.step_opts(*case["opts"])
-    run_grow(cuda, wl, case["L0"], case["steps"], opts=o)
+    run_grow(cuda, wl, case["L0"], case["steps"], opts=o, kv_write=case["kv_write"])
+
+
+@pytest.mark.parametrize("dtype,D,B,interleaved", [(torch.float32, 64, 16, False),
+                                                   (torch.bfloat16, 128, 16, True),
+                                                   (torch.bfloat16, 128, 8, False),
+                                                   (torch.float32, 128, 4, True)])
+def test_append_kv_bitwise(cuda, dtype, D, B, interleaved):
+    """oasis_append_kv against the oracle, token by token: the tiles hold every
+    token, and a block's summary is rebuilt exactly when its last token lands."""
+    say(f"append_kv dtype={dtype} D={D} B={B} interleaved={interleaved}")
+    R, H, nb = 3, 2, 6
+    gen = synth.generator(5, synth.S_MISC, cuda)
+    kt = synth.normal((R, H, nb, B, D), gen, cuda, dtype)
+    vt = synth.normal((R, H, nb, D, B), gen, cuda, dtype)
+    if interleaved:
+        _, kt, vt = synth.interleave_kv(kt, vt)
+    summ = synth.normal((R, H, nb, 2, D), gen, cuda, dtype)
+    keys64 = np64(kt).reshape(R, H, nb * B, D)
+    vals64 = np64(synth.v_tiles_to_tokens(vt))
+    summ64 = np64(summ)
+    pos = np.array([B - 3, 2 * B - 1, -1], np.int32)
+    for step in range(2 * B + 2):
+        kn = synth.normal((R, H, D), gen, cuda, dtype)
+        vn = synth.normal((R, H, D), gen, cuda, dtype)
+        p = pos.copy()
+        if step % 5 == 4:
+            p[0] = -1  # request 0 skips this step
+        ops.append_kv(kn, vn, torch.from_numpy(p).to(cuda), kt, vt, B, summaries=summ)
+        torch.cuda.synchronize()
+        keys64, vals64, summ64 = oracle.append_kv(keys64, vals64, np64(kn), np64(vn), p, B, summ64)
+        np.testing.assert_array_equal(np64(kt).reshape(R, H, nb * B, D), keys64)
+        np.testing.assert_array_equal(np64(synth.v_tiles_to_tokens(vt)), vals64)
+        np.testing.assert_array_equal(np64(summ), summ64)
+        pos = np.where(p >= 0, p + 1, pos)
+        pos[2] = -1 if step < 3 else (pos[2] + 1 if pos[2] >= 0 else 0)
+        pos = np.minimum(pos, nb * B - 1)

@@ -39,6 +39,9 @@ def _load():
                                                                ctypes.c_int, _f64p]
     lib.oro_append_kv.argtypes = [ctypes.c_int] * 5 + [_f64p, _f64p, _f64p, _f64p, _i32p, _f64p]
     lib.oro_block_scores.argtypes = [ctypes.c_int] * 6 + [_f64p, _f64p, _i32p, _f64p]
+    lib.oro_block_scores_variant.argtypes = ([ctypes.c_int] * 6 + [_f64p, _f64p, _i32p,
+                                                                  ctypes.c_double, ctypes.c_int,
+                                                                  _f64p])
     lib.oro_topk.argtypes = [ctypes.c_int] * 4 + [_f64p, _i32p, ctypes.c_int, _i32p, _f64p]
     lib.oro_select_plan.argtypes = [ctypes.c_int] * 5 + [_i32p, _i32p, _i32p, ctypes.c_int,
                                                            ctypes.c_int, _i32p, _i32p, _i32p,
@@ -50,7 +53,8 @@ def _load():
                                                           _i32p, _i32p, ctypes.c_double,
                                                           _f64p, _f64p])
     lib.oro_num_threads.argtypes = []
-    for name in ("oro_build_summaries", "oro_append_kv", "oro_block_scores", "oro_topk",
+    for name in ("oro_build_summaries", "oro_append_kv", "oro_block_scores",
+                 "oro_block_scores_variant", "oro_topk",
                  "oro_select_plan",
                  "oro_copy_blocks", "oro_sparse_attn", "oro_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
@@ -121,17 +125,28 @@ def append_kv(keys, values, k_new, v_new, pos, block_size: int, summ=None):
     return keys, values, s
 
 
-def block_scores(q, summ, n_blk=None) -> np.ndarray:
-    """q [R][n_q][Hq][D], summaries [R][H][n_blk_max][2][D] -> scores [R][n_q][H][n_blk_max]."""
+def block_scores(q, summ, n_blk=None, alpha: float = 1.0, draft_avg: bool = False) -> np.ndarray:
+    """q [R][n_q][Hq][D], summaries [R][H][n_blk_max][2][D] -> scores [R][n_s][H][n_blk_max].
+
+    alpha: the s_b(alpha) weight of the radius term (1 = the exact bound).
+    draft_avg: q has 3 rows (normal, draft a, draft b); the two drafts are
+    averaged before scoring, so n_s = 2.  Otherwise n_s = n_q.
+    """
     q = _f64(q)
     summ = _f64(summ)
     R, nq, Hq, D = q.shape
     _, H, nb, two, D2 = summ.shape
     assert two == 2 and D2 == D and summ.shape[0] == R
     nbk = None if n_blk is None else _i32(n_blk)
-    out = np.empty((R, nq, H, nb))
-    _check(_load().oro_block_scores(R, nq, Hq, H, D, nb, _p(q, _f64p), _p(summ, _f64p),
-                                    _p(nbk, _i32p), _p(out, _f64p)), "block_scores")
+    if alpha == 1.0 and not draft_avg:
+        out = np.empty((R, nq, H, nb))
+        _check(_load().oro_block_scores(R, nq, Hq, H, D, nb, _p(q, _f64p), _p(summ, _f64p),
+                                        _p(nbk, _i32p), _p(out, _f64p)), "block_scores")
+        return out
+    out = np.empty((R, 2 if draft_avg else nq, H, nb))
+    _check(_load().oro_block_scores_variant(R, nq, Hq, H, D, nb, _p(q, _f64p), _p(summ, _f64p),
+                                            _p(nbk, _i32p), float(alpha), int(bool(draft_avg)),
+                                            _p(out, _f64p)), "block_scores")
     return out
 
 

@@ -178,6 +178,75 @@ int oro_block_scores(int R, int n_q, int Hq, int H, int D, int n_blk_max,
     return 0;
 }
 
+/*
+ * Scoring variants ([v2] §3.1 equation s_b(alpha); §4.2.3 on the composition
+ * with speculative decoding):
+ *   s_b(alpha) = sum over the query heads h of group g of
+ *                q_h . c_b + alpha * |q_h| . r_b,
+ *   c_b = (max_b + min_b) / 2, r_b = (max_b - min_b) / 2  (coordinate-wise),
+ * with alpha = 1 taken in the per-coordinate max form of oro_block_scores.
+ * draft_avg: q holds n_q_in = 3 rows (normal, draft a, draft b); the scored
+ * rows are row 0 and the element-wise mean of rows 1 and 2 (the two draft
+ * queries averaged before scoring), so scores has 2 rows.
+ */
+int oro_block_scores_variant(int R, int n_q_in, int Hq, int H, int D, int n_blk_max,
+                             const double* q, const double* summ, const int32_t* n_blk,
+                             double alpha, int draft_avg, double* scores) {
+    if (R <= 0 || n_q_in <= 0 || Hq <= 0 || H <= 0 || D <= 0 || n_blk_max <= 0 ||
+        Hq % H != 0 || !q || !summ || !scores || (draft_avg && n_q_in != 3))
+        return -1;
+    const int G = Hq / H;
+    const int n_s = draft_avg ? 2 : n_q_in;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int r = 0; r < R; ++r) {
+        for (int j = 0; j < n_s; ++j) {
+            for (int g = 0; g < H; ++g) {
+                int n_r = n_blk ? n_blk[r] : n_blk_max;
+                if (n_r > n_blk_max) n_r = n_blk_max;
+                double* qs = (double*)malloc(sizeof(double) * (size_t)G * D);
+                for (int h = 0; h < G; ++h)
+                    for (int d = 0; d < D; ++d) {
+                        const size_t hh = (size_t)g * G + h;
+                        if (draft_avg && j == 1) {
+                            const double a = q[(((size_t)r * n_q_in + 1) * Hq + hh) * D + d];
+                            const double b = q[(((size_t)r * n_q_in + 2) * Hq + hh) * D + d];
+                            qs[(size_t)h * D + d] = (a + b) / 2.0;
+                        } else {
+                            qs[(size_t)h * D + d] = q[(((size_t)r * n_q_in + j) * Hq + hh) * D + d];
+                        }
+                    }
+                double* out = scores + (((size_t)r * n_s + j) * H + g) * n_blk_max;
+                for (int b = 0; b < n_blk_max; ++b) {
+                    if (b >= n_r) {
+                        out[b] = -INFINITY;
+                        continue;
+                    }
+                    const double* mn = summ + ((((size_t)r * H + g) * n_blk_max + b) * 2 + 0) * D;
+                    const double* mx = summ + ((((size_t)r * H + g) * n_blk_max + b) * 2 + 1) * D;
+                    double s = 0.0;
+                    for (int h = 0; h < G; ++h) {
+                        const double* qh = qs + (size_t)h * D;
+                        for (int d = 0; d < D; ++d) {
+                            if (alpha == 1.0) {
+                                const double a = qh[d] * mx[d];
+                                const double c = qh[d] * mn[d];
+                                s += (a > c) ? a : c;
+                            } else {
+                                const double cen = (mx[d] + mn[d]) / 2.0;
+                                const double rad = (mx[d] - mn[d]) / 2.0;
+                                s += qh[d] * cen + alpha * fabs(qh[d]) * rad;
+                            }
+                        }
+                    }
+                    out[b] = s;
+                }
+                free(qs);
+            }
+        }
+    }
+    return 0;
+}
+
 typedef struct {
     double s;
     int32_t b;

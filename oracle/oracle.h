@@ -47,6 +47,10 @@ int oro_block_scores(int R, int n_q, int Hq, int H, int D, int n_blk_max,
                      const double* q, const double* summ, const int32_t* n_blk,
                      double* scores);
 
+int oro_block_scores_variant(int R, int n_q_in, int Hq, int H, int D, int n_blk_max,
+                             const double* q, const double* summ, const int32_t* n_blk,
+                             double alpha, int draft_avg, double* scores);
+
 int oro_topk(int R, int n_q, int H, int n_blk_max, const double* scores,
              const int32_t* n_blk, int K, int32_t* topk_idx, double* topk_score);
 

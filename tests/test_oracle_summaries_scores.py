@@ -200,3 +200,57 @@ def test_append_without_summaries_and_bad_position():
     with pytest.raises(ValueError):
         oracle.append_kv(keys, keys, np.ones((1, 1, 2)), np.ones((1, 1, 2)),
                          np.array([8], np.int32), 4)
+
+
+# ---------------------------------------------------------------- scoring variants
+def _variant_inputs(seed, G=4, B=8, nq=2):
+    rng = np.random.default_rng(seed)
+    R, H, nb, D = 2, 2, 9, 16
+    keys = rng.standard_normal((R, H, nb * B, D))
+    summ = oracle.build_summaries(keys, B)
+    q = rng.standard_normal((R, nq, H * G, D))
+    return keys, summ, q, G, B
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.3, 0.5, 2.0])
+def test_scores_alpha_is_affine_between_centre_and_bound(alpha):
+    """s(alpha) = s(0) + alpha * (s(1) - s(0)), with s(1) from the max form and
+    s(0) = sum_h q_h . c (numpy): OasisKV v2 text, 3.1, equation s_b(alpha)."""
+    _, summ, q, G, _ = _variant_inputs(31)
+    R, nq, Hq, D = q.shape
+    H = summ.shape[1]
+    s1 = oracle.block_scores(q, summ)
+    centre = (summ[:, :, :, 0] + summ[:, :, :, 1]) / 2
+    s0 = np.einsum("rjhd,rhbd->rjhb", q.reshape(R, nq, H, G, D).sum(axis=3), centre)
+    np.testing.assert_allclose(oracle.block_scores(q, summ, alpha=0.0), s0, rtol=1e-12, atol=1e-12)
+    got = oracle.block_scores(q, summ, alpha=alpha)
+    np.testing.assert_allclose(got, s0 + alpha * (s1 - s0), rtol=1e-11, atol=1e-11)
+
+
+def test_scores_alpha_above_one_still_bounds_every_key():
+    keys, summ, q, G, B = _variant_inputs(32)
+    R, nq, Hq, D = q.shape
+    H, nb = summ.shape[1], summ.shape[2]
+    best = np.einsum("rjhd,rhld->rjhl", q.reshape(R, nq, H, G, D).sum(axis=3), keys)
+    best = best.reshape(R, nq, H, nb, B).max(axis=-1)
+    assert np.all(oracle.block_scores(q, summ, alpha=1.5) >= best - 1e-12 * (1 + np.abs(best)))
+
+
+@pytest.mark.parametrize("alpha", [1.0, 0.4])
+def test_scores_draft_average_equals_scoring_the_mean_query(alpha):
+    """Two drafts averaged before scoring (v2 text, 4.2.3) = scoring the row
+    [normal, (draft a + draft b) / 2] formed in numpy."""
+    _, summ, q3, G, _ = _variant_inputs(33, nq=3)
+    got = oracle.block_scores(q3, summ, alpha=alpha, draft_avg=True)
+    mean = np.stack([q3[:, 0], (q3[:, 1] + q3[:, 2]) / 2], axis=1)
+    ref = oracle.block_scores(mean, summ, alpha=alpha)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    assert got.shape[1] == 2
+
+
+def test_scores_centre_form_is_linear_in_the_query():
+    """At alpha = 0 the averaged-draft score is the mean of the two drafts' scores."""
+    _, summ, q3, _, _ = _variant_inputs(34, nq=3)
+    avg = oracle.block_scores(q3, summ, alpha=0.0, draft_avg=True)[:, 1]
+    each = oracle.block_scores(q3, summ, alpha=0.0)
+    np.testing.assert_allclose(avg, (each[:, 1] + each[:, 2]) / 2, rtol=1e-12, atol=1e-12)

@@ -168,7 +168,7 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     val = torch.empty((R, nq, H, K), dtype=torch.float32, device=dev)
     lib = _lib.load()
     shp = ops._shape(R, nq, wl.Hq, H, wl.D, 1, ops._dt(qseq))
-    ws_sc = torch.zeros(int(lib.oasis_score_topk_workspace(ctypes.byref(shp), wl.n_blk, K)),
+    ws_sc = torch.zeros(int(lib.oasis_score_topk_workspace(ctypes.byref(shp), wl.n_blk, K, None)),
                         dtype=torch.uint8, device=dev)
     ws_at = torch.zeros(max(1, ops.sparse_attn_workspace_bytes((R, nq, wl.Hq, wl.D), H, wl.B, K,
                                                                wl.dtype)),

@@ -30,7 +30,9 @@
  *    behaviour: tile / block ids within range, distinct ids in one table row,
  *    finite inputs, buffers at least as large as stated.
  *  - Notation: R batch, n_q stacked query rows (1 or 2; row 0 = normal query
- *    of step t, row 1 = draft query of step t+1), Hq query heads, H KV heads,
+ *    of step t, row 1 = draft query of step t+1; 3 with two drafts, see
+ *    oasis_step_opts), n_s scored rows (n_q, or 2 when the two drafts are
+ *    averaged), Hq query heads, H KV heads,
  *    G = Hq / H (query head h reads KV head h / G), D head dim, B block size,
  *    K top-K = resident slots per KV head, unit = one (request r, KV head g)
  *    pair with index u = r*H + g.
@@ -61,7 +63,7 @@ typedef enum { OASIS_F32 = 0, OASIS_BF16 = 1 } oasis_dtype;
 
 typedef struct oasis_shape {
     int32_t batch;       /* R >= 1 */
-    int32_t n_q;         /* stacked query rows, 1 or 2 */
+    int32_t n_q;         /* stacked query rows: 1, 2, or 3 (see oasis_step_opts.draft_avg) */
     int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
     int32_t n_kv_heads;  /* H >= 1 */
     int32_t head_dim;    /* D: 64 or 128 */
@@ -73,6 +75,30 @@ typedef struct oasis_shape {
                             the attention gathers as one contiguous piece.  Otherwise
                             >= B*D and a multiple of 16 bytes. */
 } oasis_shape;
+
+/*
+ * Tuning and scoring variants of oasis_score_topk and oasis_lookahead_step.  A
+ * NULL pointer or zero fields mean: automatic tuning, the exact bound, no
+ * draft averaging.
+ *   use_alpha, alpha  score s_b(alpha) = sum_h q_h.c_b + alpha*|q_h|.r_b with
+ *                     c_b, r_b the block's centre and radius ([v2] §3.1,
+ *                     equation s_b(alpha)); alpha = 1 is the exact bound used
+ *                     otherwise; 0 <= alpha < 1e30
+ *   draft_avg         q holds three rows (normal, draft a, draft b; n_q = 3):
+ *                     the two draft queries are averaged element-wise before
+ *                     scoring ([v2] §4.2.3, composition with speculative
+ *                     decoding), so the scored rows are row 0 and the mean
+ *                     (top-K and scores have 2 rows; attention still covers
+ *                     all three rows).  Required exactly when n_q = 3.
+ */
+typedef struct oasis_step_opts {
+    int32_t scan_chunks; /* workgroups that share one unit's summary scan (0 = auto) */
+    int32_t attn_splits; /* workgroups that share one unit's attention (0 = auto) */
+    int32_t attn_impl;   /* 0 automatic, 1 VALU, 2 MFMA (as oasis_sparse_attn_impl) */
+    int32_t use_alpha;   /* 1: score s_b(alpha) with the alpha below */
+    float alpha;
+    int32_t draft_avg;   /* 1: three query rows, drafts averaged before scoring */
+} oasis_step_opts;
 
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* oasis_status_string(int status);
@@ -141,7 +167,8 @@ int oasis_append_kv(const oasis_shape* s, const void* k_new, const void* v_new,
  *
  * Workspace bytes oasis_score_topk needs.
  */
-size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k);
+size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k,
+                                  const oasis_step_opts* opts);
 
 /*
  * Score every full block with every stacked query row and keep the top-K per
@@ -162,10 +189,12 @@ size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32
  *   summaries   [R][H][n_blk_max][2][D] (dtype)
  *   n_blk       [R] int32 full-block counts (0..n_blk_max), or NULL = n_blk_max
  *   top_k       K, 1..1024
- *   topk_idx    [R][n_q][H][K] int32 output
- *   topk_score  [R][n_q][H][K] fp32 output, or NULL
- *   scores      [R][n_q][H][n_blk_max] fp32 output of every block score
+ *   topk_idx    [R][n_s][H][K] int32 output
+ *   topk_score  [R][n_s][H][K] fp32 output, or NULL
+ *   scores      [R][n_s][H][n_blk_max] fp32 output of every block score
  *               (-inf past n_r), or NULL (then the workspace holds them)
+ *   opts        scoring variants (alpha, draft averaging) and scan tuning, or
+ *               NULL (see oasis_step_opts)
  *   workspace   device buffer of at least oasis_score_topk_workspace() bytes
  *               (NULL when that is 0; see Workspaces above)
  * Limits: n_blk_max <= 32768.
@@ -174,7 +203,8 @@ size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max, int32
 int oasis_score_topk(const oasis_shape* s, const void* q, const void* summaries,
                      int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
                      int32_t* topk_idx, float* topk_score, float* scores,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+                     const oasis_step_opts* opts, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /*
  * Capped least-recently-selected selection and transfer plan, per unit:
@@ -289,13 +319,6 @@ int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const void* k_ti
                            void* workspace, size_t workspace_bytes, int32_t impl,
                            hipStream_t stream);
 
-/* Tuning of oasis_lookahead_step; a NULL pointer or zero fields mean automatic. */
-typedef struct oasis_step_opts {
-    int32_t scan_chunks; /* workgroups that share one unit's summary scan (0 = auto) */
-    int32_t attn_splits; /* workgroups that share one unit's attention (0 = auto) */
-    int32_t attn_impl;   /* 0 automatic, 1 VALU, 2 MFMA (as oasis_sparse_attn_impl) */
-} oasis_step_opts;
-
 /* Workspace bytes of oasis_lookahead_step (see Workspaces above). */
 size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max, int32_t top_k,
                                       int32_t n_sel, const oasis_step_opts* opts);
@@ -315,8 +338,8 @@ size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max, i
  *   oasis_sparse_attn(q, k_tiles, v_tiles, tile_table, n_sel, unit_stride,
  *                     tail_tile, tail_len, scale, out, lse)
  *   oasis_score_topk(q, summaries, n_blk_max, n_blk, top_k,
- *                    topk_idx, topk_score, scores)
- *   oasis_select_plan(R, H, n_q, pred_row, top_k, topk_idx, slot_block_in,
+ *                    topk_idx, topk_score, scores, opts)
+ *   oasis_select_plan(R, H, n_s, pred_row, top_k, topk_idx, slot_block_in,
  *                     slot_stamp_in, slot_block_out, slot_stamp_out, step,
  *                     cap, ins_blk, plan_count, plan_src, plan_dst, plan_evicted)
  * run in that order (arguments as documented there; the resident set holds

@@ -60,6 +60,9 @@ class OasisStepOpts(ctypes.Structure):
         ("scan_chunks", ctypes.c_int32),
         ("attn_splits", ctypes.c_int32),
         ("attn_impl", ctypes.c_int32),
+        ("use_alpha", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("draft_avg", ctypes.c_int32),
     ]
 
 
@@ -92,9 +95,11 @@ def load() -> ctypes.CDLL:
     lib.oasis_version.argtypes = []
     lib.oasis_version.restype = ctypes.c_int
     lib.oasis_build_summaries.argtypes = [_shp, _vp, _i32, _vp, _i32, _i32, _vp, _vp]
-    lib.oasis_score_topk_workspace.argtypes = [_shp, _i32, _i32]
+    _opts = ctypes.POINTER(OasisStepOpts)
+    lib.oasis_score_topk_workspace.argtypes = [_shp, _i32, _i32, _opts]
     lib.oasis_score_topk_workspace.restype = _sz
-    lib.oasis_score_topk.argtypes = [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
+    lib.oasis_score_topk.argtypes = [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _opts, _vp,
+                                     _sz, _vp]
     lib.oasis_select_plan.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                       _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.oasis_copy_blocks.argtypes = [_shp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
@@ -105,7 +110,6 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, _vp, _vp, _vp, _sz, _vp]
     lib.oasis_sparse_attn_impl.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp,
                                            _vp, ctypes.c_float, _vp, _vp, _vp, _sz, _i32, _vp]
-    _opts = ctypes.POINTER(OasisStepOpts)
     lib.oasis_lookahead_step_workspace.argtypes = [_shp, _i32, _i32, _i32, _opts]
     lib.oasis_lookahead_step_workspace.restype = _sz
     lib.oasis_lookahead_step.argtypes = (

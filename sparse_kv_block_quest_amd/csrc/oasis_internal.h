@@ -108,7 +108,7 @@ inline int check_shape(const oasis_shape* s) {
     if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
         s->block_size <= 0)
         return OASIS_EINVAL;
-    if (s->n_q != 1 && s->n_q != 2) return OASIS_EINVAL;
+    if (s->n_q < 1 || s->n_q > 3) return OASIS_EINVAL;
     if (s->n_q_heads % s->n_kv_heads != 0) return OASIS_EINVAL;
     if (s->dtype != OASIS_F32 && s->dtype != OASIS_BF16) return OASIS_EUNSUPPORTED;
     if (s->head_dim != 64 && s->head_dim != 128) return OASIS_EUNSUPPORTED;

@@ -140,19 +140,25 @@ struct WsLayout {
 // Scratch of one call: global scores when a unit's scan is split or its scores
 // do not fit in LDS (and the caller passed no scores buffer), and attention
 // partials when units are split.
-static bool scores_in_lds(const oasis_shape* s, int n_blk_max, const StepPlan& p) {
-    return p.NC == 1 && (size_t)s->n_q * n_blk_max * 4 <= kScoreLdsMax;
+static bool scores_in_lds(const oasis_shape* s, int n_blk_max, const StepPlan& p, int NS) {
+    (void)s;
+    return p.NC == 1 && (size_t)NS * n_blk_max * 4 <= kScoreLdsMax;
+}
+
+// Scored rows: the query rows, or 2 when three rows average their two drafts.
+static int scored_rows(const oasis_shape* s, const oasis_step_opts* o) {
+    return (o && o->draft_avg) ? 2 : s->n_q;
 }
 
 static WsLayout ws_layout(const oasis_shape* s, int n_blk_max, bool scan, bool own_scores,
-                          bool attn, const StepPlan& p) {
+                          bool attn, const StepPlan& p, int NS) {
     WsLayout L{0, 0, 0, 0};
     const size_t U = (size_t)s->batch * s->n_kv_heads;
     const int NR = s->n_q * (s->n_q_heads / s->n_kv_heads);
     size_t off = 0;
-    if (scan && own_scores && !scores_in_lds(s, n_blk_max, p)) {
+    if (scan && own_scores && !scores_in_lds(s, n_blk_max, p, NS)) {
         L.scores = off;
-        off += align_up((size_t)s->batch * s->n_q * s->n_kv_heads * n_blk_max * 4, 256);
+        off += align_up((size_t)s->batch * NS * s->n_kv_heads * n_blk_max * 4, 256);
     }
     if (attn && p.S > 1) {
         L.part_ml = off;
@@ -166,12 +172,24 @@ static WsLayout ws_layout(const oasis_shape* s, int n_blk_max, bool scan, bool o
 
 static int elem_bytes(const oasis_shape* s) { return s->dtype == OASIS_F32 ? 4 : 2; }
 
-static int scan_check(const oasis_shape* s, int32_t n_blk_max, int32_t top_k) {
+static int scan_check(const oasis_shape* s, int32_t n_blk_max, int32_t top_k,
+                      const oasis_step_opts* o) {
     int st = check_shape(s);
     if (st != OASIS_OK) return st;
     if (n_blk_max <= 0 || top_k <= 0 || top_k > kMaxTopK) return OASIS_EINVAL;
+    // Three query rows only as (normal, draft a, draft b) with the drafts averaged.
+    const bool avg = o && o->draft_avg;
+    if (avg != (s->n_q == 3)) return OASIS_EINVAL;
+    if (o && o->use_alpha && !(o->alpha >= 0.f && o->alpha < 1e30f)) return OASIS_EINVAL;
     if (n_blk_max > 32768) return OASIS_EUNSUPPORTED;
     return OASIS_OK;
+}
+
+static void fill_variant(StepArgs& a, const oasis_shape* s, const oasis_step_opts* o) {
+    a.NS = scored_rows(s, o);
+    a.draft_avg = (o && o->draft_avg) ? 1 : 0;
+    a.use_alpha = (o && o->use_alpha) ? 1 : 0;
+    a.alpha = a.use_alpha ? o->alpha : 1.f;
 }
 
 static int attn_check(const oasis_shape* s, int32_t n_sel) {
@@ -202,6 +220,8 @@ static void fill_shape(StepArgs& a, const oasis_shape* s) {
     a.D = s->head_dim;
     a.B = s->block_size;
     a.U = s->batch * s->n_kv_heads;
+    a.NS = s->n_q;
+    a.alpha = 1.f;
     a.pred_row = -1;
 }
 
@@ -243,7 +263,7 @@ static void fill_scan(StepArgs& a, const oasis_shape* s, const void* q, const vo
     a.K = top_k;
     a.topk_idx = topk_idx;
     a.topk_score = topk_score;
-    a.scores_lds = scores_in_lds(s, n_blk_max, p) ? 1 : 0;
+    a.scores_lds = scores_in_lds(s, n_blk_max, p, a.NS) ? 1 : 0;
     a.scores = scores ? scores : (a.scores_lds ? nullptr : reinterpret_cast<float*>(ws + L.scores));
     a.NC = p.NC;
     a.chunk = p.chunk;
@@ -253,7 +273,7 @@ static void fill_scan(StepArgs& a, const oasis_shape* s, const void* q, const vo
 static size_t lds_for(const StepArgs& a, Role role, int att) {
     size_t b = 0;
     if (role != Role::kAttn)
-        b = scan_lds_bytes(a.NQ, a.D, a.K, a.scores_lds ? a.NQ * a.n_blk_max : 0);
+        b = scan_lds_bytes(a.NS, a.D, a.K, a.scores_lds ? a.NS * a.n_blk_max : 0);
     if (role != Role::kScan) {
         const size_t t = attn_lds_bytes(att, a.NR, a.D, a.per_split > 0 ? a.per_split : 1);
         b = t > b ? t : b;
@@ -272,29 +292,35 @@ using namespace oasis;
 
 // ================================================================ score + top-K
 extern "C" size_t oasis_score_topk_workspace(const oasis_shape* s, int32_t n_blk_max,
-                                             int32_t top_k) {
-    if (scan_check(s, n_blk_max, top_k) != OASIS_OK) return 0;
+                                             int32_t top_k, const oasis_step_opts* opts) {
+    if (scan_check(s, n_blk_max, top_k, opts) != OASIS_OK) return 0;
     const StepPlan p = plan_items(s->batch * s->n_kv_heads, n_blk_max, 0, s->head_dim,
-                                  s->block_size, elem_bytes(s), true, false, 0, 0);
-    return ws_layout(s, n_blk_max, true, true, false, p).total;
+                                  s->block_size, elem_bytes(s), true, false,
+                                  opts ? opts->scan_chunks : 0, 0);
+    return ws_layout(s, n_blk_max, true, true, false, p, scored_rows(s, opts)).total;
 }
 
 extern "C" int oasis_score_topk(const oasis_shape* s, const void* q, const void* summaries,
                                 int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
                                 int32_t* topk_idx, float* topk_score, float* scores,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int st = scan_check(s, n_blk_max, top_k);
+                                const oasis_step_opts* opts, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    int st = scan_check(s, n_blk_max, top_k, opts);
     if (st != OASIS_OK) return st;
     if (!q || !summaries || !topk_idx) return OASIS_EINVAL;
+    if (opts && opts->scan_chunks < 0) return OASIS_EINVAL;
     const StepPlan p = plan_items(s->batch * s->n_kv_heads, n_blk_max, 0, s->head_dim,
-                                  s->block_size, elem_bytes(s), true, false, 0, 0);
-    const WsLayout L = ws_layout(s, n_blk_max, true, scores == nullptr, false, p);
+                                  s->block_size, elem_bytes(s), true, false,
+                                  opts ? opts->scan_chunks : 0, 0);
+    const int NS = scored_rows(s, opts);
+    const WsLayout L = ws_layout(s, n_blk_max, true, scores == nullptr, false, p, NS);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return OASIS_EWORKSPACE;
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
     StepArgs a;
     fill_shape(a, s);
+    fill_variant(a, s, opts);
     fill_scan(a, s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores, p, ws, L);
-    return dispatch(a, s->dtype, s->head_dim, s->n_q, kAttnNone, Role::kScan,
+    return dispatch(a, s->dtype, s->head_dim, NS, kAttnNone, Role::kScan,
                     lds_for(a, Role::kScan, kAttnNone), stream);
 }
 
@@ -303,7 +329,7 @@ extern "C" size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_se
     if (attn_check(s, n_sel) != OASIS_OK) return 0;
     const StepPlan p = plan_items(s->batch * s->n_kv_heads, 0, n_sel, s->head_dim, s->block_size,
                                   elem_bytes(s), false, true, 0, 0);
-    return ws_layout(s, 0, false, false, true, p).total;
+    return ws_layout(s, 0, false, false, true, p, s->n_q).total;
 }
 
 extern "C" int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const void* k_tiles,
@@ -320,7 +346,7 @@ extern "C" int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const
     if ((st = pick_attn(s, impl, &att)) != OASIS_OK) return st;
     const StepPlan p = plan_items(s->batch * s->n_kv_heads, 0, n_sel, s->head_dim, s->block_size,
                                   elem_bytes(s), false, true, 0, 0);
-    const WsLayout L = ws_layout(s, 0, false, false, true, p);
+    const WsLayout L = ws_layout(s, 0, false, false, true, p, s->n_q);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return OASIS_EWORKSPACE;
     StepArgs a;
     fill_shape(a, s);
@@ -363,8 +389,9 @@ extern "C" int oasis_select_plan(int32_t batch, int32_t n_kv_heads, int32_t n_q,
 }
 
 // ================================================================ fused step
-static int step_check(const oasis_shape* s, int32_t n_blk_max, int32_t top_k, int32_t n_sel) {
-    int st = scan_check(s, n_blk_max, top_k);
+static int step_check(const oasis_shape* s, int32_t n_blk_max, int32_t top_k, int32_t n_sel,
+                      const oasis_step_opts* o) {
+    int st = scan_check(s, n_blk_max, top_k, o);
     if (st != OASIS_OK) return st;
     return attn_check(s, n_sel);
 }
@@ -378,8 +405,9 @@ static StepPlan step_plan(const oasis_shape* s, int32_t n_blk_max, int32_t n_sel
 extern "C" size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max,
                                                  int32_t top_k, int32_t n_sel,
                                                  const oasis_step_opts* opts) {
-    if (step_check(s, n_blk_max, top_k, n_sel) != OASIS_OK) return 0;
-    return ws_layout(s, n_blk_max, true, true, true, step_plan(s, n_blk_max, n_sel, opts)).total;
+    if (step_check(s, n_blk_max, top_k, n_sel, opts) != OASIS_OK) return 0;
+    return ws_layout(s, n_blk_max, true, true, true, step_plan(s, n_blk_max, n_sel, opts),
+                     scored_rows(s, opts)).total;
 }
 
 extern "C" int oasis_lookahead_step(
@@ -392,13 +420,14 @@ extern "C" int oasis_lookahead_step(
     const void* v_tiles, const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
     const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out, float* lse,
     const oasis_step_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    int st = step_check(s, n_blk_max, top_k, n_sel);
+    int st = step_check(s, n_blk_max, top_k, n_sel, opts);
     if (st != OASIS_OK) return st;
+    const int NS = scored_rows(s, opts);
     if (!q || !summaries || !topk_idx || !slot_block_in || !slot_stamp_in || !slot_block_out ||
         !slot_stamp_out || !plan_count || !plan_src || !plan_dst || !k_tiles || !v_tiles || !out)
         return OASIS_EINVAL;
     if (n_sel > 0 && !tile_table) return OASIS_EINVAL;
-    if (pred_row < 0 || pred_row >= s->n_q || cap < 0 || unit_stride < 0) return OASIS_EINVAL;
+    if (pred_row < 0 || pred_row >= NS || cap < 0 || unit_stride < 0) return OASIS_EINVAL;
     if (opts && (opts->scan_chunks < 0 || opts->attn_splits < 0)) return OASIS_EINVAL;
     // The plan rewrites slots while attention reads the tile table: the
     // new slot tables must not overlap it.
@@ -409,11 +438,12 @@ extern "C" int oasis_lookahead_step(
     int att;
     if ((st = pick_attn(s, opts ? opts->attn_impl : 0, &att)) != OASIS_OK) return st;
     const StepPlan p = step_plan(s, n_blk_max, n_sel, opts);
-    const WsLayout L = ws_layout(s, n_blk_max, true, scores == nullptr, true, p);
+    const WsLayout L = ws_layout(s, n_blk_max, true, scores == nullptr, true, p, NS);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return OASIS_EWORKSPACE;
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
     StepArgs a;
     fill_shape(a, s);
+    fill_variant(a, s, opts);
     fill_scan(a, s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores, p, ws, L);
     fill_attn(a, s, q, k_tiles, v_tiles, tile_table, n_sel, unit_stride, tail_tile, tail_len, scale,
               out, lse, p, ws, L);
@@ -430,6 +460,6 @@ extern "C" int oasis_lookahead_step(
     a.plan_src = plan_src;
     a.plan_dst = plan_dst;
     a.plan_evicted = plan_evicted;
-    return dispatch(a, s->dtype, s->head_dim, s->n_q, att, Role::kFused,
+    return dispatch(a, s->dtype, s->head_dim, NS, att, Role::kFused,
                     lds_for(a, Role::kFused, att), stream);
 }

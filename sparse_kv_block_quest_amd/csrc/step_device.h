@@ -56,20 +56,24 @@ enum { kAttnNone = 0, kAttnMfma = 1, kAttnValu = 2 };
 struct StepArgs {
     // shape
     int R, NQ, Hq, H, G, NR, D, B, U;
+    int NS;            // scored rows (NQ, or 2 when three query rows average their drafts)
     const uint8_t* q;  // [R][NQ][Hq][D]
     // scan + top-K
     const uint8_t* summ;  // [R][H][n_blk_max][2][D]
     int n_blk_max;
     const int32_t* n_blk;  // [R] or null
     int K;
-    int32_t* topk_idx;   // [R][NQ][H][K]
-    float* topk_score;   // [R][NQ][H][K] or null
-    float* scores;       // [R][NQ][H][n_blk_max] global scores, or null (NC = 1 only)
+    int32_t* topk_idx;   // [R][NS][H][K]
+    float* topk_score;   // [R][NS][H][K] or null
+    float* scores;       // [R][NS][H][n_blk_max] global scores, or null (NC = 1 only)
     int NC, chunk;       // scan items per unit, blocks per item
     int scores_lds;      // NC = 1 and the unit's scores fit in LDS
     // plan
     int do_plan, pred_row, step, cap;
     const int32_t* ins_blk;  // [R] newly completed block per request (-1 none) or null
+    int draft_avg;           // q rows: normal, draft a, draft b; scored: row 0, mean of 1 and 2
+    int use_alpha;           // score s_b(alpha) instead of the exact bound (alpha = 1)
+    float alpha;
     const int32_t* slot_blk_in;
     const int32_t* slot_stamp_in;
     int32_t* slot_blk_out;
@@ -211,15 +215,25 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
     // group's P/N vectors are formed.
     uint4 mnA[UNR], mxA[UNR], mnB[UNR], mxB[UNR];
     load(b_begin, mnA, mxA);
-    // P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0) over the group's heads.
+    // P_g = sum_h max(q_h, 0), N_g = sum_h min(q_h, 0) over the group's heads
+    // (scored row j; with draft averaging row 1 is the mean of query rows 1
+    // and 2).  s_b(alpha) = P'.max + N'.min with P' = ((1+alpha)P + (1-alpha)N)/2
+    // and N' = ((1-alpha)P + (1+alpha)N)/2, the centre/radius form rewritten.
     for (int idx = tid; idx < NQ * D; idx += kNT) {
         const int j = idx / D, d = idx - (idx / D) * D;
+        const bool avg = a.draft_avg && j == 1;
         float p = 0.f, n = 0.f;
         for (int h = 0; h < a.G; ++h) {
-            const float x =
-                load_elem<DT>(a.q, (((size_t)r * NQ + j) * a.Hq + (size_t)g * a.G + h) * D + d);
+            const size_t hd = ((size_t)g * a.G + h) * D + d;
+            float x = load_elem<DT>(a.q, ((size_t)r * a.NQ + j) * a.Hq * D + hd);
+            if (avg) x = 0.5f * (x + load_elem<DT>(a.q, ((size_t)r * a.NQ + 2) * a.Hq * D + hd));
             p += x > 0.f ? x : 0.f;
             n += x < 0.f ? x : 0.f;
+        }
+        if (a.use_alpha) {
+            const float pp = 0.5f * ((1.f + a.alpha) * p + (1.f - a.alpha) * n);
+            n = 0.5f * ((1.f - a.alpha) * p + (1.f + a.alpha) * n);
+            p = pp;
         }
         pn[(j * 2) * D + d] = p;
         pn[(j * 2 + 1) * D + d] = n;

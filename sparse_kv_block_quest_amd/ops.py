@@ -193,14 +193,24 @@ def append_kv(k_new: torch.Tensor, v_new: torch.Tensor, pos: torch.Tensor, k_til
     prepare_append_kv(k_new, v_new, pos, k_tiles, v_tiles, block_size, summaries, stream)()
 
 
+def _opts_ref(opts):
+    return ctypes.byref(opts) if opts is not None else None
+
+
+def scored_rows(n_q: int, opts: OasisStepOpts | None) -> int:
+    """Rows of the top-K and score outputs: n_q, or 2 when the drafts are averaged."""
+    return 2 if (opts is not None and opts.draft_avg) else int(n_q)
+
+
 def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                n_blk: torch.Tensor | None = None, want_scores: bool = False,
-               stream=None, out=None):
+               stream=None, out=None, opts: OasisStepOpts | None = None):
     """q [R][n_q][Hq][D], summaries [R][H][n_blk_max][2][D].
 
     Returns (topk_idx int32, topk_score fp32, scores fp32 or None), top-K tensors
-    shaped [R][n_q][H][top_k], scores [R][n_q][H][n_blk_max].  ``out`` may pass
-    preallocated (topk_idx, topk_score, scores, workspace).
+    shaped [R][n_s][H][top_k], scores [R][n_s][H][n_blk_max], n_s the scored rows
+    (``scored_rows``).  ``opts`` selects the scoring variant (``step_opts``).
+    ``out`` may pass preallocated (topk_idx, topk_score, scores, workspace).
     """
     lib = _lib.load()
     R, n_q, Hq, D = q.shape
@@ -208,21 +218,22 @@ def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
     if R2 != R or two != 2 or D2 != D or summaries.dtype != q.dtype:
         raise ValueError("summaries do not match q")
     shp = _shape(R, n_q, Hq, H, D, 1, _dt(q))
+    ns = scored_rows(n_q, opts)
     dev = q.device
     if out is not None:
         idx, val, sc, ws = out
     else:
-        idx = torch.empty((R, n_q, H, top_k), dtype=torch.int32, device=dev)
-        val = torch.empty((R, n_q, H, top_k), dtype=torch.float32, device=dev)
-        sc = torch.empty((R, n_q, H, nb), dtype=torch.float32, device=dev) if want_scores else None
-        wsb = lib.oasis_score_topk_workspace(ctypes.byref(shp), nb, int(top_k))
+        idx = torch.empty((R, ns, H, top_k), dtype=torch.int32, device=dev)
+        val = torch.empty((R, ns, H, top_k), dtype=torch.float32, device=dev)
+        sc = torch.empty((R, ns, H, nb), dtype=torch.float32, device=dev) if want_scores else None
+        wsb = lib.oasis_score_topk_workspace(ctypes.byref(shp), nb, int(top_k), _opts_ref(opts))
         ws = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
     if n_blk is not None:
         _i32(n_blk, "n_blk")
     check("oasis_score_topk",
           lib.oasis_score_topk(ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk),
-                               int(top_k), _ptr(idx), _ptr(val), _ptr(sc), _ptr(ws),
-                               ws.numel(), _stream(stream)))
+                               int(top_k), _ptr(idx), _ptr(val), _ptr(sc), _opts_ref(opts),
+                               _ptr(ws), ws.numel(), _stream(stream)))
     return idx, val, sc
 
 
@@ -384,8 +395,14 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
     return out, (lse if want_lse else None)
 
 
-def step_opts(scan_chunks: int = 0, attn_splits: int = 0, impl: int = IMPL_AUTO) -> OasisStepOpts:
-    return OasisStepOpts(int(scan_chunks), int(attn_splits), int(impl))
+def step_opts(scan_chunks: int = 0, attn_splits: int = 0, impl: int = IMPL_AUTO,
+              alpha: float | None = None, draft_avg: bool = False) -> OasisStepOpts:
+    """Tuning (0 = automatic) and scoring variants: ``alpha`` scores s_b(alpha)
+    (None = the exact bound), ``draft_avg`` takes three query rows and averages
+    the two drafts before scoring."""
+    return OasisStepOpts(int(scan_chunks), int(attn_splits), int(impl),
+                         0 if alpha is None else 1, 1.0 if alpha is None else float(alpha),
+                         1 if draft_avg else 0)
 
 
 def lookahead_step_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_blk_max: int,
@@ -484,12 +501,13 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             b[key] = t
         return t
 
+    ns = scored_rows(n_q, opts)
     res = {
         "out": get("out", q.shape, q.dtype),
         "lse": get("lse", (R, n_q, Hq), torch.float32) if want_lse else None,
-        "topk_idx": get("topk_idx", (R, n_q, H, K), torch.int32),
-        "topk_score": get("topk_score", (R, n_q, H, K), torch.float32),
-        "scores": get("scores", (R, n_q, H, nb), torch.float32) if want_scores else None,
+        "topk_idx": get("topk_idx", (R, ns, H, K), torch.int32),
+        "topk_score": get("topk_score", (R, ns, H, K), torch.float32),
+        "scores": get("scores", (R, ns, H, nb), torch.float32) if want_scores else None,
         "plan_count": get("plan_count", (R, H), torch.int32),
         "plan_src": get("plan_src", (R, H, K), torch.int32),
         "plan_dst": get("plan_dst", (R, H, K), torch.int32),

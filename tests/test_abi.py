@@ -50,7 +50,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), _lib.OASIS_EINVAL),
-    (dict(n_q=3), _lib.OASIS_EINVAL),
+    (dict(n_q=4), _lib.OASIS_EINVAL),
     (dict(n_q_heads=5), _lib.OASIS_EINVAL),
     (dict(dtype=7), _lib.OASIS_EUNSUPPORTED),
     (dict(head_dim=96), _lib.OASIS_EUNSUPPORTED),
@@ -63,11 +63,11 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails val
 def test_shape_validation(lib, kw, code):
     s = _shape(**kw)
     assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 0, 4, FAKE, None) == code
-    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 2, FAKE, None, FAKE, None, 0,
-                                None) == code
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 2, FAKE, None, FAKE, None,
+                                None, 0, None) == code
     assert lib.oasis_sparse_attn(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 2, 4, None, None, 0.0,
                                  FAKE, None, FAKE, 1 << 20, None) == code
-    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4, 2) == 0
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4, 2, None) == 0
     assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 2) == 0
 
 
@@ -78,16 +78,16 @@ def test_argument_validation(lib):
     assert lib.oasis_build_summaries(ctypes.byref(s), None, 4, None, 0, 4, FAKE, None) == E
     assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 3, 2, FAKE, None) == E
     assert lib.oasis_build_summaries(ctypes.byref(s), FAKE, 4, None, 2, 2, FAKE, None) == 0  # empty
-    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 0, FAKE, None, FAKE, None, 0,
-                                None) == E
+    assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 0, FAKE, None, FAKE, None,
+                                None, 0, None) == E
     assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4, None, 1025, FAKE, None, FAKE, None,
-                                0, None) == E
+                                None, 0, None) == E
     assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 40000, None, 8, FAKE, None, FAKE,
-                                None, 0, None) == _lib.OASIS_EUNSUPPORTED
+                                None, None, 0, None) == _lib.OASIS_EUNSUPPORTED
     # scores NULL and no workspace, at a shape whose units are split (needs scratch)
-    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4096, 2) > 0
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 4096, 2, None) > 0
     assert lib.oasis_score_topk(ctypes.byref(s), FAKE, FAKE, 4096, None, 2, FAKE, None, None, None,
-                                0, None) == _lib.OASIS_EWORKSPACE
+                                None, 0, None) == _lib.OASIS_EWORKSPACE
     # plan: pred_row out of range, negative cap, K too large
     args = [FAKE] * 5
     assert lib.oasis_select_plan(1, 2, 2, 2, 8, *args, 0, 1, None, FAKE, FAKE, FAKE, None,
@@ -116,15 +116,15 @@ def test_argument_validation(lib):
 def test_workspace_queries(lib):
     # 256 units: one workgroup per unit and role, scores in LDS, no scratch
     s = _shape(batch=32, n_q_heads=32, n_kv_heads=8)
-    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 2048, 128) == 0
+    assert lib.oasis_score_topk_workspace(ctypes.byref(s), 2048, 128, None) == 0
     assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 128) == 0
     assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), 2048, 128, 128, None) == 0
     # split units: global scores and attention partials
     small = _shape(batch=1, n_q_heads=32, n_kv_heads=8)
-    assert lib.oasis_score_topk_workspace(ctypes.byref(small), 2048, 128) >= 2 * 8 * 2048 * 4
+    assert lib.oasis_score_topk_workspace(ctypes.byref(small), 2048, 128, None) >= 2 * 8 * 2048 * 4
     assert lib.oasis_sparse_attn_workspace(ctypes.byref(small), 128) >= 8 * 2 * 8 * 2 * 128 * 4
     # forced splits at 256 units need scratch too
-    o = _lib.OasisStepOpts(2, 2, 0)
+    o = _lib.OasisStepOpts(2, 2, 0, 0, 1.0, 0)
     assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), 2048, 128, 128,
                                               ctypes.byref(o)) >= 32 * 2 * 8 * 2048 * 4
 
@@ -159,9 +159,9 @@ def test_lookahead_step_validation(lib):
     # new slot table overlapping the tile table the attention reads
     assert _step(lib, s, bo=ctypes.c_void_p(0x100000 + 8)) == E
     assert _step(lib, s, so=ctypes.c_void_p(0x100000 - 8)) == E
-    bad = _lib.OasisStepOpts(-1, 0, 0)
+    bad = _lib.OasisStepOpts(-1, 0, 0, 0, 1.0, 0)
     assert _step(lib, s, opts=ctypes.byref(bad)) == E
-    mf = _lib.OasisStepOpts(0, 0, 2)
+    mf = _lib.OasisStepOpts(0, 0, 2, 0, 1.0, 0)
     assert _step(lib, _shape(dtype=0), opts=ctypes.byref(mf)) == _lib.OASIS_EUNSUPPORTED
     assert _step(lib, _shape(head_dim=96)) == _lib.OASIS_EUNSUPPORTED
     big = dict(nb=2048, K=64, n_sel=64)  # one request: split units need scratch
@@ -181,3 +181,23 @@ def test_append_kv_validation(lib):
     bad = _shape(head_dim=96)
     assert lib.oasis_append_kv(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None,
                                None) == _lib.OASIS_EUNSUPPORTED
+
+
+def test_scoring_variant_validation(lib):
+    """Three query rows only with draft averaging, averaging only with three rows,
+    and alpha finite and non-negative (all rejected before any launch)."""
+    E = _lib.OASIS_EINVAL
+    three = _shape(n_q=3)
+    avg = _lib.OasisStepOpts(0, 0, 0, 0, 1.0, 1)
+    assert lib.oasis_score_topk(ctypes.byref(three), FAKE, FAKE, 4, None, 2, FAKE, None, FAKE,
+                                None, None, 0, None) == E
+    assert lib.oasis_score_topk(ctypes.byref(_shape()), FAKE, FAKE, 4, None, 2, FAKE, None, FAKE,
+                                ctypes.byref(avg), None, 0, None) == E
+    assert lib.oasis_score_topk_workspace(ctypes.byref(three), 4, 2, None) == 0
+    for alpha in (-0.5, float("inf"), float("nan")):
+        bad = _lib.OasisStepOpts(0, 0, 0, 1, alpha, 0)
+        assert lib.oasis_score_topk(ctypes.byref(_shape()), FAKE, FAKE, 4, None, 2, FAKE, None,
+                                    FAKE, ctypes.byref(bad), None, 0, None) == E
+    # the fused step: pred_row must be a scored row (2 rows with averaging)
+    assert _step(lib, three, pred=2, opts=ctypes.byref(avg)) == E
+    assert _step(lib, three, opts=None) == E

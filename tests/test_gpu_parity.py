@@ -359,6 +359,30 @@ def test_attn_parity(cuda, dtype, G, B, nb, n_sel, tail):
             assert torch.equal(o1, out[:, j:j + 1]) and torch.equal(l1, lse[:, j:j + 1])
 
 
+@pytest.mark.parametrize("G,impl", [(4, None), (8, None), (10, None), (4, "valu")])
+def test_attn_three_rows(cuda, G, impl):
+    """Three stacked rows (normal + two drafts) attend the same tiles; each row
+    equals its own single-row call bit for bit."""
+    say(f"attn three rows G={G} impl={impl}")
+    R, H, D, B, nb, n_sel = 2, 2, 128, 16, 40, 13
+    dtype = torch.bfloat16
+    gen = synth.generator(41 + G, synth.S_MISC, cuda)
+    q = synth.normal((R, 3, H * G, D), gen, cuda, dtype)
+    k = synth.normal((R, H, nb, B, D), gen, cuda, dtype)
+    vt = synth.normal((R, H, nb, D, B), gen, cuda, dtype)
+    table = synth.random_tile_table(R, H, n_sel, nb - 1, gen, cuda)
+    tt = torch.full((R, H), nb - 1, dtype=torch.int32, device=cuda)
+    tl = torch.tensor([9, 16], dtype=torch.int32, device=cuda)
+    im = ops.IMPL_VALU if impl == "valu" else ops.IMPL_AUTO
+    out, lse = ops.sparse_attn(q, k, vt, table, nb, B, tail_tile=tt, tail_len=tl, impl=im)
+    torch.cuda.synchronize()
+    check_attn(out, lse, attn_reference(q, k, vt, table, nb, B, tt, tl), dtype)
+    for j in range(3):
+        o1, l1 = ops.sparse_attn(q[:, j:j + 1].contiguous(), k, vt, table, nb, B, tail_tile=tt,
+                                 tail_len=tl, impl=im)
+        assert torch.equal(o1, out[:, j:j + 1]) and torch.equal(l1, lse[:, j:j + 1])
+
+
 def test_attn_empty_and_custom_scale(cuda):
     say("attn empty units + explicit scale")
     R, H, G, D, B, nb = 2, 2, 4, 128, 16, 10

@@ -41,6 +41,13 @@ def score_scale(q64, summ64, G):
     return np.einsum("rjhd,rhbd->rjhb", qa, amax)
 
 
+def three_rows(cur, gen):
+    """[normal, draft a, draft b]: a second draft beside synth's [normal, draft]."""
+    extra = 0.98 * cur[:, 0] + 0.2 * torch.randn(cur[:, 0].shape, generator=gen,
+                                                 device=cur.device)
+    return torch.cat([cur, extra[:, None]], dim=1)
+
+
 def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0,
               interleaved=False):
     """Seed the resident set, then run `steps` fused steps, checking each.  With
@@ -68,9 +75,14 @@ def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0
         # the active block: the last block of the store, `tail` valid tokens
         tt = torch.full((R, H), wl.n_blk - 1, dtype=torch.int32, device=dev)
         tl = torch.tensor([max(1, tail - (r % 3)) for r in range(R)], dtype=torch.int32, device=dev)
+    alpha = opts.alpha if (opts is not None and opts.use_alpha) else None
+    avg = bool(opts is not None and opts.draft_avg)
+    g3 = synth.generator(wl.seed + 5, synth.S_MISC, dev)
+    if avg:
+        qf = three_rows(qf, g3)
     # seeding from row 0 of the first queries
     q = qf.to(wl.dtype)
-    idx, _, _ = ops.score_topk(q, summ, K, n_blk=nbk)
+    idx, _, _ = ops.score_topk(q, summ, K, n_blk=nbk, opts=opts)
     slots = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
     stamps = [torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
     ops.select_plan(idx, slots[0], stamps[0], 0, wl.cap, pred_row=0)
@@ -89,32 +101,38 @@ def run_chain(cuda, wl, steps, opts=None, tail=0, n_blk=None, units=None, seed=0
                                  opts=opts, bufs=bufs)
         torch.cuda.synchronize()
         # standalone scan + top-K: identical fp32 scores and selection
-        i2, v2, s2 = ops.score_topk(q, summ, K, n_blk=nbk, want_scores=True)
+        i2, v2, s2 = ops.score_topk(q, summ, K, n_blk=nbk, want_scores=True, opts=opts)
         torch.cuda.synchronize()
         assert torch.equal(res["scores"], s2)
         assert torch.equal(res["topk_idx"], i2)
         assert torch.equal(res["topk_score"], v2)
         check_step(wl, q, summ, kt, vt, slots[a], stamps[a], slots[b], stamps[b], res, t + 1,
-                   n_valid, tt, tl, units)
+                   n_valid, tt, tl, units, alpha=alpha, draft_avg=avg)
         cur = synth.drift(cur[:, 0], wl.rho, gen)
+        if avg:
+            cur = three_rows(cur, g3)
     return res
 
 
 def check_step(wl, q, summ, kt, vt, blk_in, stamp_in, blk_out, stamp_out, res, step, n_valid,
-               tt, tl, units, ins=None):
+               tt, tl, units, ins=None, alpha=None, draft_avg=False):
     R, H, K, G = wl.R, wl.H, wl.K, wl.G
     q64 = np64(q)
+    # the rows that are scored: [normal, mean of the drafts] when averaging
+    qsc = np.stack([q64[:, 0], (q64[:, 1] + q64[:, 2]) / 2], axis=1) if draft_avg else q64
     blk_in_np = blk_in.cpu().numpy()
     # scores against the fp64 oracle, on the sampled units
     sc = res["scores"].cpu().double().numpy()
     for r, g in units:
         s_sub = np64(summ[r:r + 1, g:g + 1])
         qs = q64[r:r + 1, :, g * G:(g + 1) * G]
-        ref = oracle.block_scores(qs, s_sub, n_blk=n_valid[r:r + 1])
+        ref = oracle.block_scores(qs, s_sub, n_blk=n_valid[r:r + 1],
+                                  alpha=1.0 if alpha is None else alpha, draft_avg=draft_avg)
         got = sc[r:r + 1, :, g:g + 1]
         fin = np.isfinite(ref)
         assert np.array_equal(np.isfinite(got), fin)
-        scale = score_scale(qs, s_sub, G)
+        scale = score_scale(qsc[r:r + 1, :, g * G:(g + 1) * G], s_sub, G)
+        scale = scale * max(1.0, 1.0 if alpha is None else alpha)
         err = np.abs(got[fin] - ref[fin])
         assert np.all(err <= SCORE_RTOL * np.maximum(np.abs(ref[fin]), scale[fin]))
     # top-K: the oracle's selection on the kernel's scores
@@ -163,6 +181,20 @@ def test_step_tiny_fp32(cuda, case):
     o = None if case["opts"] is None else ops.step_opts(*case["opts"])
     say(f"fused step tiny fp32 {case}")
     run_chain(cuda, wl, 4, opts=o, tail=case.get("tail", 0))
+
+
+@pytest.mark.parametrize("G,D,B,K,opts", [
+    (4, 128, 16, 32, dict(alpha=0.5)),
+    (4, 128, 16, 32, dict(alpha=2.0, scan_chunks=2, attn_splits=2)),
+    (4, 128, 16, 32, dict(draft_avg=True)),
+    (4, 128, 16, 24, dict(draft_avg=True, alpha=0.25, scan_chunks=3, attn_splits=2)),
+    (8, 64, 16, 16, dict(draft_avg=True, impl=1)),  # 24 rows, VALU attention
+])
+def test_step_scoring_variants(cuda, G, D, B, K, opts):
+    """s_b(alpha) and two drafts averaged before scoring (three query rows)."""
+    wl = small("qwen3-8b-1layer", R=3, H=2, Hq=2 * G, D=D, B=B, L=2064, K=K, cap=5)
+    say(f"fused step variants G={G} D={D} K={K} {opts}")
+    run_chain(cuda, wl, 3, opts=ops.step_opts(**opts), tail=7)
 
 
 @pytest.mark.parametrize("G,D,B,L,K,nq_opts", [

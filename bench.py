@@ -55,6 +55,10 @@ def parse_args(argv=None):
                    help="pinned-host pipeline (use with --workload qwen3-8b-pipeline)")
     p.add_argument("--grow", action="store_true",
                    help="growing contexts: one token per request per step")
+    p.add_argument("--alpha", type=float, default=None,
+                   help="score s_b(alpha) instead of the exact bound")
+    p.add_argument("--draft-avg", action="store_true",
+                   help="three query rows; the two drafts are averaged before scoring")
     p.add_argument("--kv-layout", choices=("interleaved", "split"), default="interleaved",
                    help="one K|V record per block-head, or separate K and V stores")
     p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
@@ -140,14 +144,19 @@ def setup_layers(wl, dev, n_layers, interleaved, torch, synth, ops):
     return layers, ms
 
 
-def query_sequence(wl, dev, n_layers, n_steps, torch, synth):
-    """Stacked queries per (step, layer): [T][layers][R][2][Hq][D] in wl.dtype, AR(1) drift."""
-    out = torch.empty((n_steps, n_layers, wl.R, 2, wl.Hq, wl.D), dtype=wl.dtype, device=dev)
+def query_sequence(wl, dev, n_layers, n_steps, torch, synth, rows=2):
+    """Stacked queries per (step, layer): [T][layers][R][rows][Hq][D] in wl.dtype, AR(1)
+    drift; rows = 3 adds a second draft (0.98 q + 0.2 N(0, 1), its own stream)."""
+    out = torch.empty((n_steps, n_layers, wl.R, rows, wl.Hq, wl.D), dtype=wl.dtype, device=dev)
     for l in range(n_layers):
         g = synth.generator(wl.seed + 1000 * l, synth.S_DRIFT, dev)
+        g2 = synth.generator(wl.seed + 1000 * l + 500, synth.S_DRIFT, dev)
         cur = synth.queries(wl, dev, layer=l)
         for t in range(n_steps):
-            out[t, l] = cur.to(wl.dtype)
+            out[t, l, :, :2] = cur.to(wl.dtype)
+            if rows == 3:
+                out[t, l, :, 2] = (0.98 * cur[:, 0] + 0.2 * torch.randn(
+                    cur[:, 0].shape, generator=g2, device=dev)).to(wl.dtype)
             cur = synth.drift(cur[:, 0], wl.rho, g)
     return out
 
@@ -159,7 +168,9 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     layers, summ_ms = setup_layers(wl, dev, n_layers, args.kv_layout == "interleaved", torch,
                                    synth, ops)
     T = args.warmup + args.steps + 1
-    qseq = query_sequence(wl, dev, n_layers, T, torch, synth)
+    qseq = query_sequence(wl, dev, n_layers, T, torch, synth, rows=3 if args.draft_avg else 2)
+    vopts = ops.step_opts(args.scan_chunks, args.attn_splits, impl, alpha=args.alpha,
+                          draft_avg=args.draft_avg)
 
     R, H, K, nq = wl.R, wl.H, wl.K, wl.n_q
     # Preallocated outputs, workspaces and per-layer resident state (slot
@@ -168,7 +179,9 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     val = torch.empty((R, nq, H, K), dtype=torch.float32, device=dev)
     lib = _lib.load()
     shp = ops._shape(R, nq, wl.Hq, H, wl.D, 1, ops._dt(qseq))
-    ws_sc = torch.zeros(int(lib.oasis_score_topk_workspace(ctypes.byref(shp), wl.n_blk, K, None)),
+    shp3 = ops._shape(R, qseq.shape[3], wl.Hq, H, wl.D, 1, ops._dt(qseq))
+    ws_sc = torch.zeros(max(1, int(lib.oasis_score_topk_workspace(ctypes.byref(shp3), wl.n_blk, K,
+                                                                  ctypes.byref(vopts)))),
                         dtype=torch.uint8, device=dev)
     ws_at = torch.zeros(max(1, ops.sparse_attn_workspace_bytes((R, nq, wl.Hq, wl.D), H, wl.B, K,
                                                                wl.dtype)),
@@ -186,14 +199,14 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
 
     # Seeding: the first working set comes from the first normal query (row 0).
     for l in range(n_layers):
-        ops.score_topk(qseq[0, l], layers[l]["summ"], K, out=(idx, val, None, ws_sc))
+        ops.score_topk(qseq[0, l], layers[l]["summ"], K, out=(idx, val, None, ws_sc), opts=vopts)
         ops.select_plan(idx, blk[l][0], stamp[l][0], 0, wl.cap, pred_row=0, plan=plan)
     torch.cuda.synchronize()
 
     fused = args.path == "fused"
     calls = None
     if fused:
-        opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
+        opts = vopts
         bufs = {}
         calls = [[ops.prepare_lookahead_step(
             qseq[0, l], layers[l]["summ"], K, blk[l][p], stamp[l][p], blk[l][1 - p],
@@ -568,7 +581,9 @@ def run_cpu_baseline(args, wl, g, torch, synth):
     done = 0
     t0 = time.perf_counter()
     while True:
-        sc = oracle.block_scores(inp["q"], inp["summ"])
+        sc = oracle.block_scores(inp["q"], inp["summ"],
+                                 alpha=1.0 if args.alpha is None else args.alpha,
+                                 draft_avg=args.draft_avg)
         ti, _ = oracle.topk(sc, wl.K)
         oracle.select_plan(ti, inp["blk"], inp["stamp"], t + 1, wl.cap, pred_row=1)
         oracle.sparse_attn(inp["q"], inp["kt"], inp["vt"], table, wl.K)
@@ -622,6 +637,10 @@ def main(argv=None):
     print(f"# workload {wl.name}: R={wl.R} Hq={wl.Hq} H={wl.H} D={wl.D} L={wl.L} B={wl.B} "
           f"K={wl.K} layers={wl.layers} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
+    if (args.alpha is not None or args.draft_avg) and (args.path != "fused" or args.pipeline or
+                                                        args.grow):
+        print("--alpha / --draft-avg apply to the fused default leg only", file=sys.stderr)
+        return 2
     if args.pipeline:
         return report_pipeline(args, wl, run_pipeline(args, wl, torch, synth, ops))
     if args.grow:
@@ -679,7 +698,10 @@ def main(argv=None):
                                f"{wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}",
                    "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
                    "budget_tokens": wl.K * wl.B, "layers": wl.layers, "cap": wl.cap,
-                   "stacked_queries": wl.n_q, "impl": args.impl, "path": args.path,
+                   "stacked_queries": 3 if args.draft_avg else wl.n_q,
+                   "scoring": ("exact bound" if args.alpha is None else f"s_b(alpha={args.alpha})")
+                              + (", drafts averaged" if args.draft_avg else ""),
+                   "impl": args.impl, "path": args.path,
                    "kv_layout": args.kv_layout},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",

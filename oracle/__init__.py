@@ -18,6 +18,8 @@ import os
 
 import numpy as np
 
+from .host_tier import HostTierModel  # noqa: F401  (decode-host cache reference)
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboasis_oracle.so")
 _lib = None

@@ -269,6 +269,80 @@ int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const void* src_v
                       const int32_t* plan_count, const int32_t* plan_src,
                       const int32_t* plan_dst, hipStream_t stream);
 
+/*
+ * Decode-host block cache (the one stateful object of this library; created
+ * and destroyed by the caller, one per layer).  [v2] §3.2.1 (ii) (the decode
+ * host fetches whole blocks, every KV head's entries, for the union of the
+ * heads' selections), §3.2.2 (union block mapping: remote block -> decode-host
+ * block, per request) and §3.2.3 (per-request budget f_Host*P + F blocks; least
+ * recently used prompt blocks are evicted while generated blocks and the
+ * current working set are kept; evicted blocks are fetched again when
+ * selected).  Policy: a request's union is its planned source blocks in
+ * (head, entry) order, each once; an absent block takes the lowest free slot,
+ * else evicts the slot with the smallest (last use, slot) among blocks that are
+ * not generated, not in the request's HBM working set and not in the union.
+ * Memory (caller-owned, alive until destroy):
+ *   remote    [R][n_blk][block_bytes] whole blocks: H interleaved K|V records
+ *   cache     [R][cap_max][block_bytes] pinned host memory (the GPU reads it)
+ *   map       [R][n_blk] int32 pinned host memory: cache slot of each remote
+ *             block, -1 if absent (written by the tier, read by the gather)
+ *   capacity  [R] slots per request (<= cap_max)
+ * Returns NULL on a bad argument.  Calls on one tier must not overlap.
+ */
+typedef struct oasis_host_tier oasis_host_tier;
+oasis_host_tier* oasis_host_tier_create(int32_t batch, int32_t n_kv_heads, int32_t top_k,
+                                        int32_t n_blk, const int32_t* capacity, int32_t cap_max,
+                                        size_t block_bytes, const void* remote, void* cache,
+                                        int32_t* map);
+void oasis_host_tier_destroy(oasis_host_tier* t);
+
+/* One layer-step on the CPU, now: fetch the absent blocks of every request's
+ * union of plan_src[r][g][i < plan_count[r][g]] (host arrays, [R][H] and
+ * [R][H][K]) and stamp the union with `step`; slot_block [R][H][K] (host, or
+ * NULL) is the HBM working set after the plan.  EINVAL if a request's budget
+ * held no evictable block (its blocks that did not fit are counted as failed). */
+int oasis_host_tier_fetch(oasis_host_tier* t, int64_t step, const int32_t* plan_count,
+                          const int32_t* plan_src, const int32_t* slot_block);
+
+/* The same in stream order: copies plan_count / plan_src / slot_block (device
+ * memory, as written by the plan) into the tier's pinned staging on `stream`,
+ * then runs the fetch as a host function on that stream, stamped with the
+ * tier's own step counter; work later on the stream (the mapped gather) sees
+ * the updated cache and map.  Errors: EINVAL, EHIP; fetch failures are
+ * counted (oasis_host_tier_state). */
+int oasis_host_tier_enqueue_fetch(oasis_host_tier* t, const int32_t* plan_count,
+                                  const int32_t* plan_src, const int32_t* slot_block,
+                                  hipStream_t stream);
+
+/* A block generated on the decode node (already written to the cache slot
+ * this returns through the map) joins request `req`'s cache, never evicted. */
+int oasis_host_tier_add_generated(oasis_host_tier* t, int32_t req, int32_t block, int64_t step,
+                                  const int32_t* slot_block);
+
+/* Periodic pass: evict, by the same order, until request r holds at most
+ * target[r] blocks (protected blocks stay, so fewer may go). */
+int oasis_host_tier_trim(oasis_host_tier* t, const int32_t* target, const int32_t* slot_block);
+
+/* Snapshot: slot_block_out [R][cap_max] (block per slot, -1 free) and
+ * last_out [R][cap_max] (either may be NULL); stats_out[4] = blocks fetched,
+ * blocks evicted, blocks that found no slot, stream-ordered steps run. */
+int oasis_host_tier_state(const oasis_host_tier* t, int32_t* slot_block_out, int64_t* last_out,
+                          int64_t* stats_out);
+
+/*
+ * oasis_copy_blocks reading its sources through the decode-host cache: the
+ * tile of unit u = (r, g) for block b is record g of cache slot map[r][b]
+ * (entries whose block is absent are skipped).  cache_k, cache_v: the cache's
+ * K and V tiles (v = k + B*D with tile_stride 2*B*D); map as above; res_*,
+ * top_k and plan_* as oasis_copy_blocks.  [v2] §3.2.2 (the gather copies each
+ * head's slice of the mapped decode-host block into the GPU page).
+ * Errors: EINVAL, EUNSUPPORTED, EHIP.
+ */
+int oasis_copy_blocks_mapped(const oasis_shape* s, const void* cache_k, const void* cache_v,
+                             int32_t cap_max, const int32_t* map, int32_t n_blk, void* res_k,
+                             void* res_v, int32_t top_k, const int32_t* plan_count,
+                             const int32_t* plan_src, const int32_t* plan_dst, hipStream_t stream);
+
 /* Workspace bytes oasis_sparse_attn needs for this shape (see Workspaces above). */
 size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel);
 

@@ -34,6 +34,14 @@ EXPORTS = (
     "oasis_select_plan",
     "oasis_append_kv",
     "oasis_copy_blocks",
+    "oasis_copy_blocks_mapped",
+    "oasis_host_tier_create",
+    "oasis_host_tier_destroy",
+    "oasis_host_tier_fetch",
+    "oasis_host_tier_enqueue_fetch",
+    "oasis_host_tier_add_generated",
+    "oasis_host_tier_trim",
+    "oasis_host_tier_state",
     "oasis_sparse_attn_workspace",
     "oasis_sparse_attn",
     "oasis_sparse_attn_impl",
@@ -104,6 +112,17 @@ def load() -> ctypes.CDLL:
                                       _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.oasis_copy_blocks.argtypes = [_shp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
     lib.oasis_append_kv.argtypes = [_shp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]
+    lib.oasis_copy_blocks_mapped.argtypes = [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
+                                             _vp, _vp, _vp, _vp]
+    lib.oasis_host_tier_create.argtypes = [_i32, _i32, _i32, _i32, _vp, _i32, _sz, _vp, _vp, _vp]
+    lib.oasis_host_tier_create.restype = _vp
+    lib.oasis_host_tier_destroy.argtypes = [_vp]
+    lib.oasis_host_tier_destroy.restype = None
+    lib.oasis_host_tier_fetch.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp]
+    lib.oasis_host_tier_enqueue_fetch.argtypes = [_vp, _vp, _vp, _vp, _vp]
+    lib.oasis_host_tier_add_generated.argtypes = [_vp, _i32, _i32, ctypes.c_int64, _vp]
+    lib.oasis_host_tier_trim.argtypes = [_vp, _vp, _vp]
+    lib.oasis_host_tier_state.argtypes = [_vp, _vp, _vp, _vp]
     lib.oasis_sparse_attn_workspace.argtypes = [_shp, _i32]
     lib.oasis_sparse_attn_workspace.restype = _sz
     lib.oasis_sparse_attn.argtypes = [_shp, _vp, _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp,
@@ -117,6 +136,10 @@ def load() -> ctypes.CDLL:
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
+    for name in ("oasis_copy_blocks_mapped", "oasis_host_tier_fetch",
+                 "oasis_host_tier_enqueue_fetch", "oasis_host_tier_add_generated",
+                 "oasis_host_tier_trim", "oasis_host_tier_state"):
+        getattr(lib, name).restype = ctypes.c_int
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan", "oasis_append_kv",
                  "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl",
                  "oasis_lookahead_step"):

@@ -286,10 +286,11 @@ class PreparedCopy:
     calling it enqueues the copy again (on the stream given at preparation, or
     on ``stream``)."""
 
-    def __init__(self, args, keep, lib):
+    def __init__(self, args, keep, lib, name: str = "oasis_copy_blocks"):
         self.args = args
         self._keep = keep
-        self._fn = lib.oasis_copy_blocks
+        self._name = name
+        self._fn = getattr(lib, name)
 
     def __call__(self, stream=None) -> None:
         a = self.args
@@ -297,7 +298,7 @@ class PreparedCopy:
             a = a[:-1] + [_stream(stream)]
         st = self._fn(*a)
         if st != 0:
-            check("oasis_copy_blocks", st)
+            check(self._name, st)
 
 
 def prepare_copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.Tensor,
@@ -342,6 +343,122 @@ def prepare_copy_blocks(src_k: torch.Tensor, src_v: torch.Tensor, res_k: torch.T
     keep = (shp, src_k, src_v, res_k, res_v, plan["plan_count"], plan["plan_src"],
             plan["plan_dst"])
     return PreparedCopy(args, keep, lib)
+
+
+# ------------------------------------------------------------ decode-host tier
+def _np_or_tensor_ptr(a):
+    """Host pointer of a numpy array or a CPU (pinned or not) tensor; None stays None."""
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        if a.is_cuda:
+            raise ValueError("expected host memory")
+        if not a.is_contiguous():
+            raise ValueError("host array must be contiguous")
+        return ctypes.c_void_p(a.data_ptr())
+    import numpy as np
+    if not (isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"]):
+        raise ValueError("host array must be a contiguous numpy array or tensor")
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class HostTier:
+    """The decode-host block cache of one layer (oasis_host_tier_*): whole
+    blocks of ``remote`` [R][n_blk][block] cached in ``cache`` [R][cap_max][block]
+    (pinned, as the GPU gather reads it), with the union map ``map`` [R][n_blk]
+    int32 (pinned).  The arrays must outlive the tier."""
+
+    def __init__(self, batch: int, n_kv_heads: int, top_k: int, n_blk: int, capacity,
+                 remote, cache, map_, block_bytes: int):
+        import numpy as np
+        self._lib = _lib.load()
+        self.R, self.H, self.K, self.n_blk = int(batch), int(n_kv_heads), int(top_k), int(n_blk)
+        self.capacity = np.ascontiguousarray(np.asarray(capacity, np.int32))
+        self.cap_max = int(self.capacity.max()) if cache is None else int(cache.shape[1])
+        self._keep = (remote, cache, map_, self.capacity)
+        h = self._lib.oasis_host_tier_create(
+            self.R, self.H, self.K, self.n_blk, _np_or_tensor_ptr(self.capacity), self.cap_max,
+            int(block_bytes), _np_or_tensor_ptr(remote), _np_or_tensor_ptr(cache),
+            _np_or_tensor_ptr(map_))
+        if not h:
+            raise ValueError("oasis_host_tier_create rejected its arguments")
+        self._h = ctypes.c_void_p(h)
+
+    def fetch(self, step: int, plan_count, plan_src, slot_block=None) -> int:
+        return int(self._lib.oasis_host_tier_fetch(self._h, int(step), _np_or_tensor_ptr(plan_count),
+                                                   _np_or_tensor_ptr(plan_src),
+                                                   _np_or_tensor_ptr(slot_block)))
+
+    def enqueue_fetch(self, plan_count: torch.Tensor, plan_src: torch.Tensor,
+                      slot_block: torch.Tensor, stream=None) -> None:
+        check("oasis_host_tier_enqueue_fetch",
+              self._lib.oasis_host_tier_enqueue_fetch(self._h, _ptr(plan_count), _ptr(plan_src),
+                                                      _ptr(slot_block), _stream(stream)))
+
+    def add_generated(self, req: int, block: int, step: int, slot_block=None) -> int:
+        return int(self._lib.oasis_host_tier_add_generated(self._h, int(req), int(block), int(step),
+                                                           _np_or_tensor_ptr(slot_block)))
+
+    def trim(self, target, slot_block=None) -> None:
+        import numpy as np
+        t = np.ascontiguousarray(np.asarray(target, np.int32))
+        check("oasis_host_tier_trim",
+              self._lib.oasis_host_tier_trim(self._h, _np_or_tensor_ptr(t),
+                                             _np_or_tensor_ptr(slot_block)))
+
+    def state(self):
+        """(slot_block [R][cap_max], last [R][cap_max], stats dict)."""
+        import numpy as np
+        sb = np.empty((self.R, self.cap_max), np.int32)
+        last = np.empty((self.R, self.cap_max), np.int64)
+        st = np.empty(4, np.int64)
+        check("oasis_host_tier_state",
+              self._lib.oasis_host_tier_state(self._h, _np_or_tensor_ptr(sb),
+                                              _np_or_tensor_ptr(last), _np_or_tensor_ptr(st)))
+        return sb, last, {"fetched": int(st[0]), "evicted": int(st[1]), "failed": int(st[2]),
+                          "steps": int(st[3])}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.oasis_host_tier_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # interpreter shutdown
+            pass
+
+
+def prepare_copy_blocks_mapped(cache: torch.Tensor, map_: torch.Tensor, res_k: torch.Tensor,
+                               res_v: torch.Tensor, plan: dict, block_size: int,
+                               stream=None) -> PreparedCopy:
+    """The gather of planned blocks from the decode-host cache (pinned,
+    [R][cap_max][H][2][B][D]) through the union map (pinned [R][n_blk] int32)
+    into the resident slots (res_* as ``copy_blocks``)."""
+    lib = _lib.load()
+    if cache.dim() != 6 or cache.shape[3] != 2 or not cache.is_pinned():
+        raise ValueError("cache must be pinned [R][cap_max][H][2][B][D]")
+    R, cap_max, H, _, B, D = cache.shape
+    if int(block_size) != B:
+        raise ValueError("block_size does not match the cache")
+    if map_.dtype != torch.int32 or map_.dim() != 2 or map_.shape[0] != R or not map_.is_pinned():
+        raise ValueError("map must be pinned int32 [R][n_blk]")
+    K = res_k.shape[2]
+    rptr_k, rs = _tile_store(res_k, "res_k", B * D)
+    rptr_v, rs2 = _tile_store(res_v, "res_v", B * D)
+    if rs != 2 * B * D or rs2 != rs:
+        raise ValueError("the resident store must be interleaved (tile stride 2*B*D)")
+    ck, cv = interleaved_kv(cache.view(R, cap_max * H, 2, B, D))
+    shp = _shape(R, 1, H, H, D, B, _dt(cache), rs)
+    for k in ("plan_count", "plan_src", "plan_dst"):
+        _i32(plan[k], k)
+    args = [ctypes.byref(shp), ctypes.c_void_p(ck.data_ptr()), ctypes.c_void_p(cv.data_ptr()),
+            cap_max, ctypes.c_void_p(map_.data_ptr()), map_.shape[1], ctypes.c_void_p(rptr_k),
+            ctypes.c_void_p(rptr_v), K, _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
+            _ptr(plan["plan_dst"]), _stream(stream)]
+    return PreparedCopy(args, (shp, cache, map_, res_k, res_v, plan), lib,
+                        "oasis_copy_blocks_mapped")
 
 
 def sparse_attn_workspace_bytes(q_shape, n_kv_heads: int, block_size: int, n_sel: int,

@@ -16,6 +16,11 @@ it is ordered after the copy.  Other layers run meanwhile.  This is the
 pipelined transfer of the OasisKV paper (Section 4, the pinned-host path with a
 background copy stream and events that keep each layer's order); the steps
 themselves are the library's kernels, called through ``ops``.
+
+With a decode-host cache (Section 3.2: remote memory holds the full prompt KV,
+decode-host memory a bounded cache of whole blocks), the copy stream first
+copies the plan back and runs the cache's fetch of absent blocks as a host
+function, then gathers through the cache's union map.
 """
 from __future__ import annotations
 
@@ -29,14 +34,33 @@ class PipelineLayer:
     (double-buffered: step t reads buffer t % 2 and plans into the other),
     per-layer plan buffers and the prepared calls."""
 
-    def __init__(self, wl, host_store: torch.Tensor, summaries: torch.Tensor,
-                 q0: torch.Tensor, device, opts=None, want_scores=False):
+    def __init__(self, wl, host_store: torch.Tensor | None, summaries: torch.Tensor,
+                 q0: torch.Tensor, device, opts=None, want_scores=False,
+                 remote_store: torch.Tensor | None = None, host_capacity: int | None = None):
+        """host_store: pinned [R][H][n_blk][2][B][D], the full store the copies
+        read.  Or, with a decode-host cache: remote_store pinned
+        [R][n_blk][H][2][B][D] (whole blocks, standing in for remote memory) and
+        host_capacity blocks per request cached in decode-host memory."""
         R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
-        if not host_store.is_pinned():
-            raise ValueError("the host store must be pinned")
         self.wl = wl
-        self.host = host_store
-        self.host_k, self.host_v = ops.interleaved_kv(host_store)
+        self.tier = None
+        if remote_store is not None:
+            if not remote_store.is_pinned() or remote_store.shape[:1] != (R,) or \
+                    remote_store.shape[2:] != (H, 2, B, D):
+                raise ValueError("remote_store must be pinned [R][n_blk][H][2][B][D]")
+            n_blk = remote_store.shape[1]
+            cap = int(host_capacity)
+            self.remote = remote_store
+            self.cache = torch.empty((R, cap, H, 2, B, D), dtype=wl.dtype, pin_memory=True)
+            self.map = torch.empty((R, n_blk), dtype=torch.int32, pin_memory=True)
+            block_bytes = H * 2 * B * D * remote_store.element_size()
+            self.tier = ops.HostTier(R, H, K, n_blk, [cap] * R, remote_store, self.cache,
+                                     self.map, block_bytes)
+        else:
+            if host_store is None or not host_store.is_pinned():
+                raise ValueError("the host store must be pinned")
+            self.host = host_store
+            self.host_k, self.host_v = ops.interleaved_kv(host_store)
         self.res = torch.empty((R, H, K, 2, B, D), dtype=wl.dtype, device=device)
         self.res_k, self.res_v = ops.interleaved_kv(self.res)
         self.summ = summaries
@@ -50,8 +74,12 @@ class PipelineLayer:
             wl.cap, self.res_k, self.res_v, self.ident, K, B, pred_row=1, want_scores=want_scores,
             want_evicted=False, opts=opts, bufs=self.bufs) for p in range(2)]
         self.plan = {k: self.bufs[k] for k in ("plan_count", "plan_src", "plan_dst")}
-        self.copy_call = ops.prepare_copy_blocks(self.host_k, self.host_v, self.res_k,
-                                                 self.res_v, self.plan, B)
+        if self.tier is None:
+            self.copy_call = ops.prepare_copy_blocks(self.host_k, self.host_v, self.res_k,
+                                                     self.res_v, self.plan, B)
+        else:
+            self.copy_call = ops.prepare_copy_blocks_mapped(self.cache, self.map, self.res_k,
+                                                            self.res_v, self.plan, B)
         self.attn_done = torch.cuda.Event()
         self.copy_done = torch.cuda.Event()
 
@@ -64,8 +92,16 @@ class PipelineLayer:
                         plan=dict(self.plan, plan_evicted=None))
         self.attn_done.record()
         copy_stream.wait_event(self.attn_done)
-        self.copy_call(copy_stream)
+        self.copy(copy_stream, self.blk[0])
         self.copy_done.record(copy_stream)
+
+    def copy(self, stream, slot_block: torch.Tensor) -> None:
+        """The planned blocks into their slots, on `stream`; through the
+        decode-host cache (fetch of absent whole blocks first) when there is one."""
+        if self.tier is not None:
+            self.tier.enqueue_fetch(self.plan["plan_count"], self.plan["plan_src"], slot_block,
+                                    stream)
+        self.copy_call(stream)
 
 
 class Pipeline:
@@ -89,7 +125,7 @@ class Pipeline:
         res = L.step_calls[t % 2](t + 1, q)
         L.attn_done.record(main)
         self.copy_stream.wait_event(L.attn_done)
-        L.copy_call(self.copy_stream)
+        L.copy(self.copy_stream, L.blk[1 - t % 2])
         L.copy_done.record(self.copy_stream)
         return res
 

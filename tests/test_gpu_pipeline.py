@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from sparse_kv_block_quest_amd import ops, pipeline, synth
 from test_gpu_step import check_step, small
 
@@ -23,7 +24,7 @@ def say(msg):
     print(msg, flush=True)
 
 
-def build(wl, dev, n_layers, opts=None, want_scores=True):
+def build(wl, dev, n_layers, opts=None, want_scores=True, host_capacity=None):
     layers, q0s, full = [], [], []
     for l in range(n_layers):
         qf = synth.queries(wl, dev, layer=l)
@@ -32,11 +33,19 @@ def build(wl, dev, n_layers, opts=None, want_scores=True):
         kt = keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D)
         store, k, v = synth.interleave_kv(kt, vt)
         summ = ops.build_summaries(k, wl.B)
-        host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
-        host.copy_(store)
         q0 = qf.to(wl.dtype)
-        layers.append(pipeline.PipelineLayer(wl, host, summ, q0, dev, opts=opts,
-                                             want_scores=want_scores))
+        if host_capacity is None:
+            host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
+            host.copy_(store)
+            layers.append(pipeline.PipelineLayer(wl, host, summ, q0, dev, opts=opts,
+                                                 want_scores=want_scores))
+        else:  # remote memory holds whole blocks [R][n_blk][H][2][B][D]
+            whole = store.permute(0, 2, 1, 3, 4, 5).contiguous()
+            remote = torch.empty(whole.shape, dtype=whole.dtype, pin_memory=True)
+            remote.copy_(whole)
+            layers.append(pipeline.PipelineLayer(wl, None, summ, q0, dev, opts=opts,
+                                                 want_scores=want_scores, remote_store=remote,
+                                                 host_capacity=host_capacity))
         q0s.append(q0)
         full.append((k, v, store))
     return pipeline.Pipeline(layers), q0s, full
@@ -55,18 +64,21 @@ def query_steps(wl, dev, n_layers, n_steps):
 
 
 def resident_matches_host(layer, blk):
-    """Every filled slot holds the host tiles of the block its slot table names."""
+    """Every filled slot holds the host tiles of the block its slot table names
+    (from the full host store, or from remote memory through the cache)."""
     R, H, K = blk.shape
     b = blk.long()
     assert bool((b >= 0).all()), "pipeline slots are all filled after seeding"
     r = torch.arange(R, device=b.device)[:, None, None]
     g = torch.arange(H, device=b.device)[None, :, None]
-    host_dev = layer.host.to(b.device)
-    want = host_dev[r, g, b]
+    if layer.tier is None:
+        want = layer.host.to(b.device)[r, g, b]
+    else:
+        want = layer.remote.to(b.device)[r, b, g]
     assert torch.equal(layer.res.view(torch.int16), want.view(torch.int16))
 
 
-def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None):
+def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_capacity=None):
     dev = cuda
     qs = query_steps(wl, dev, n_layers, n_steps)
     n_valid = np.full(wl.R, wl.n_blk, np.int32)
@@ -74,10 +86,17 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None):
         units = [(r, g) for r in range(wl.R) for g in range(wl.H)]
 
     # run A: checked step by step
-    pa, q0s, full = build(wl, dev, n_layers, opts)
+    pa, q0s, full = build(wl, dev, n_layers, opts, host_capacity=host_capacity)
     pa.seed(q0s)
     torch.cuda.synchronize()
     outs_a = []
+    models = None
+    if host_capacity is not None:  # replay the GPU's plans through the reference cache
+        nb = wl.n_blk
+        models = [oracle.HostTierModel([host_capacity] * wl.R, nb) for _ in range(n_layers)]
+        for l, L in enumerate(pa.layers):
+            models[l].fetch(1, L.plan["plan_count"].cpu().numpy(), L.plan["plan_src"].cpu().numpy(),
+                            L.blk[0].cpu().numpy())
     for l, layer in enumerate(pa.layers):
         resident_matches_host(layer, pa.resident_blocks(l, 0))
     for t in range(n_steps):
@@ -92,10 +111,15 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None):
                        res, t + 1, n_valid, None, None, units)
             outs_a.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
             resident_matches_host(L, L.blk[b])
+            if models is not None:
+                models[l].fetch(t + 2, L.plan["plan_count"].cpu().numpy(),
+                                L.plan["plan_src"].cpu().numpy(), L.blk[b].cpu().numpy())
+                np.testing.assert_array_equal(L.map.numpy(), models[l].map)
+                assert L.tier.state()[2]["failed"] == 0
     del pa
 
     # run B: free-running, events only
-    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False)
+    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False, host_capacity=host_capacity)
     pb.seed(q0s)
     outs_b = []
     for t in range(n_steps):
@@ -122,3 +146,13 @@ def test_pipeline_full_shape(cuda):
     wl = synth.workload("qwen3-8b-pipeline", layers=2)
     say("pipeline qwen3-8b shape, 2 layers x 2 steps")
     run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)])
+
+
+@pytest.mark.parametrize("cap", [40, 36])
+def test_pipeline_with_decode_host_cache(cuda, cap):
+    """Remote memory holds whole blocks; a bounded decode-host cache (2 heads x
+    16 slots = at most 32 working-set blocks per request) feeds the gather
+    through its union map; the cache evicts and refetches as the sets drift."""
+    wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=2048, K=16, cap=4)
+    say(f"pipeline with decode-host cache, capacity {cap}")
+    run_pipeline_case(cuda, wl, 2, 5, host_capacity=cap)

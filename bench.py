@@ -63,6 +63,12 @@ def parse_args(argv=None):
                    help="score s_b(alpha) instead of the exact bound")
     p.add_argument("--draft-avg", action="store_true",
                    help="three query rows; the two drafts are averaged before scoring")
+    p.add_argument("--host-frac", type=float, default=None,
+                   help="--pipeline: decode-host cache of this fraction of each request's "
+                        "blocks in front of a remote store (default: the full store in host "
+                        "memory)")
+    p.add_argument("--host-workers", type=int, default=4,
+                   help="--pipeline --host-frac: host threads per remote fetch")
     p.add_argument("--kv-layout", choices=("interleaved", "split"), default="interleaved",
                    help="one K|V record per block-head, or separate K and V stores")
     p.add_argument("--scan-chunks", type=int, default=0, help="fused path: 0 = automatic")
@@ -529,6 +535,7 @@ def run_pipeline(args, wl, torch, synth, ops):
     n_layers = wl.layers
     impl = {"auto": ops.IMPL_AUTO, "valu": ops.IMPL_VALU, "mfma": ops.IMPL_MFMA}[args.impl]
     opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
+    cap = None if args.host_frac is None else max(1, int(math.ceil(args.host_frac * wl.n_blk)))
     layers = []
     t0 = time.perf_counter()
     for l in range(n_layers):
@@ -538,10 +545,21 @@ def run_pipeline(args, wl, torch, synth, ops):
         store, k, _ = synth.interleave_kv(keys.view(wl.R, wl.H, wl.n_blk, wl.B, wl.D), vt)
         del keys, vt
         summ = ops.build_summaries(k, wl.B)
-        host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
-        host.copy_(store)
-        del store, k
-        layers.append(pipeline.PipelineLayer(wl, host, summ, qf.to(wl.dtype), dev, opts=opts))
+        del k
+        if cap is None:
+            host = torch.empty(store.shape, dtype=store.dtype, pin_memory=True)
+            host.copy_(store)
+            del store
+            layers.append(pipeline.PipelineLayer(wl, host, summ, qf.to(wl.dtype), dev, opts=opts))
+        else:  # remote memory: whole blocks; a bounded decode-host cache in front
+            whole = store.permute(0, 2, 1, 3, 4, 5).contiguous()
+            del store
+            remote = torch.empty(whole.shape, dtype=whole.dtype, pin_memory=True)
+            remote.copy_(whole.cpu())  # written by the host: its pages are mapped for host reads
+            del whole
+            layers.append(pipeline.PipelineLayer(wl, None, summ, qf.to(wl.dtype), dev, opts=opts,
+                                                 remote_store=remote, host_capacity=cap,
+                                                 host_workers=args.host_workers))
         if (l + 1) % 6 == 0 or l + 1 == n_layers:
             print(f"# layer {l + 1}/{n_layers} in pinned host memory "
                   f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
@@ -550,55 +568,71 @@ def run_pipeline(args, wl, torch, synth, ops):
     pipe = pipeline.Pipeline(layers)
     main = torch.cuda.current_stream()
     pipe.seed([qseq[0, l] for l in range(n_layers)])
+    pipe.drain()
     torch.cuda.synchronize()
     for t in range(args.warmup):
         for l in range(n_layers):
             pipe.layer_step(t, l, qseq[t, l])
+    pipe.drain()
     torch.cuda.synchronize()
 
     # Timed region: free-running, no markers between launches; the end waits
-    # for the copy stream, so every copy is inside it.
+    # (host) until every copy is issued, then for the copy stream, so every
+    # copy is inside it.
+    def tier_stats():
+        if cap is None:
+            return None
+        st = [L.tier.state()[2] for L in layers]
+        return {k: sum(x[k] for x in st) for k in st[0]}
+
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    st0 = tier_stats()
     w0 = time.perf_counter()
     ev0.record()
     for t in range(args.warmup, args.warmup + args.steps):
         for l in range(n_layers):
             pipe.layer_step(t, l, qseq[t, l])
+    pipe.drain()
     main.wait_stream(pipe.copy_stream)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     total_ms = ev0.elapsed_time(ev1)
+    st1 = tier_stats()
 
     # Breakdown replay on the following steps: events around every fused step
-    # (main stream) and every copy (copy stream), and the admitted blocks.
+    # (main stream) and every copy (copy stream; with a cache, from submit to
+    # the end of the gather), and the admitted blocks.
     admitted = torch.zeros((), dtype=torch.int64, device=dev)
     ev_step, ev_copy = [], []
-    cs = pipe.copy_stream
     for t in range(args.warmup + args.steps, T):
         for l in range(n_layers):
-            L = layers[l]
             a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            main.wait_event(L.copy_done)
-            a0.record(main)
-            res = L.step_calls[t % 2](t + 1, qseq[t, l])
-            a1.record(main)
+            res = pipe.layer_step(t, l, qseq[t, l], step_events=(a0, a1), copy_events=(c0, c1))
             admitted.add_(res["plan_count"].sum())
-            L.attn_done.record(main)
-            cs.wait_event(L.attn_done)
-            c0.record(cs)
-            L.copy_call(cs)
-            c1.record(cs)
-            L.copy_done.record(cs)
             ev_step.append((a0, a1))
             ev_copy.append((c0, c1))
+    pipe.drain()
     torch.cuda.synchronize()
 
     def avg_us(evs):
         return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
-    return {"total_ms": total_ms, "wall_s": wall, "step_us": avg_us(ev_step),
+    tier = None
+    if cap is not None:  # counts over the timed steps, all layers and requests
+        d = {k: st1[k] - st0[k] for k in st1}
+        n_ls = args.steps * n_layers
+        tier = {"capacity_blocks_per_request": cap, "host_frac": args.host_frac,
+                "host_workers": args.host_workers,
+                "fetch_host_us_per_layer_step": round(d["fetch_ns"] / 1000.0 / n_ls, 2),
+                "remote_fetched_blocks": d["fetched"], "evicted_blocks": d["evicted"],
+                "failed_blocks": d["failed"], "fetch_calls": d["steps"],
+                "remote_blocks_per_request_layer_step": round(d["fetched"] / (n_ls * wl.R), 4),
+                "remote_bytes_per_layer_step": round(
+                    d["fetched"] * wl.H * 2 * wl.B * wl.D * (2 if str(wl.dtype).endswith(
+                        "bfloat16") else 4) / n_ls)}
+    return {"total_ms": total_ms, "wall_s": wall, "step_us": avg_us(ev_step), "tier": tier,
             "copy_us": avg_us(ev_copy),
             "admitted_per_head_step": float(admitted.item()) / (args.steps * n_layers * wl.R * wl.H),
             "setup_s": time.perf_counter() - t0}
@@ -615,6 +649,16 @@ def report_pipeline(args, wl, g):
     ls_us = g["total_ms"] * 1000.0 / n_ls
     step_gbs = per_ls / (g["step_us"] * 1e-6) / 1e9
     pcie_gbs = copied / (g["copy_us"] * 1e-6) / 1e9
+    wall_gbs = copied / (ls_us * 1e-6) / 1e9
+    cached = g["tier"] is not None
+    if cached:  # the copy events span fetch + gather: rate the link by the interval
+        roof = {"bound": "pcie", "kernel": "copy_mapped_kernel (over the pipeline interval)",
+                "achieved": round(wall_gbs, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                "frac": round(wall_gbs / PEAK_PCIE_GBS, 4), "traffic": None}
+    else:
+        roof = {"bound": "pcie", "kernel": "oasis_copy_blocks", "achieved": round(pcie_gbs, 2),
+                "peak": PEAK_PCIE_GBS, "unit": "GB/s", "frac": round(pcie_gbs / PEAK_PCIE_GBS, 4),
+                "traffic": None}
     line = {
         "metric": "layer-steps/s (pinned-host pipeline: scan+top-K+plan+sparse attn, "
                   "block copies overlapped)",
@@ -625,23 +669,28 @@ def report_pipeline(args, wl, g):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if e == 2 else "f32", "data": "synthetic",
         "config": {"workload": f"{wl.name}: Qwen3-8B attention shape, {wl.Hq} q / {wl.H} KV "
-                               f"heads, head_dim {wl.D}; full K|V in pinned host memory",
+                               f"heads, head_dim {wl.D}; " + (
+                                   "full K|V in pinned host memory" if g["tier"] is None else
+                                   f"full K|V in a pinned remote store, decode-host cache of "
+                                   f"{g['tier']['capacity_blocks_per_request']} blocks per "
+                                   f"request"),
                    "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
                    "layers": wl.layers, "cap": wl.cap, "stacked_queries": wl.n_q,
                    "host_store_GiB": round(wl.layers * units * wl.n_blk * tile_bytes / 2**30, 2)},
-        "roofline": {"bound": "pcie", "kernel": "oasis_copy_blocks", "achieved": round(pcie_gbs, 2),
-                     "peak": PEAK_PCIE_GBS, "unit": "GB/s",
-                     "frac": round(pcie_gbs / PEAK_PCIE_GBS, 4), "traffic": None},
+        "roofline": roof,
         "stages_us_per_layer_step": {
-            "fused_step": round(g["step_us"], 2), "copy": round(g["copy_us"], 2),
+            "fused_step": round(g["step_us"], 2),
+            ("fetch_and_gather" if cached else "copy"): round(g["copy_us"], 2),
             "pipeline_interval": round(ls_us, 2),
             "stall": round(max(0.0, ls_us - g["step_us"]), 2)},
         "fused_step": {"algo_bytes": per_ls, "GBps": round(step_gbs, 1),
                        "frac": round(step_gbs / PEAK_HBM_GBS, 4)},
-        "pcie": {"bytes_per_layer_step": round(copied), "copy_kernel_GBps": round(pcie_gbs, 2),
-                 "wall_GBps": round(copied / (ls_us * 1e-6) / 1e9, 2)},
+        "pcie": {"bytes_per_layer_step": round(copied),
+                 "copy_kernel_GBps": None if cached else round(pcie_gbs, 2),
+                 "wall_GBps": round(wall_gbs, 2)},
         "admitted_blocks_per_head_step": round(g["admitted_per_head_step"], 3),
         "host_issue_us_per_layer_step": round(g["wall_s"] * 1e6 / n_ls, 2),
+        "decode_host_cache": g["tier"],
         "kernel_sources": kernel_source_hash(),
         "cpu_baseline": None,
     }

@@ -283,11 +283,15 @@ int oasis_copy_blocks(const oasis_shape* s, const void* src_k, const void* src_v
  * not generated, not in the request's HBM working set and not in the union.
  * Memory (caller-owned, alive until destroy):
  *   remote    [R][n_blk][block_bytes] whole blocks: H interleaved K|V records
- *   cache     [R][cap_max][block_bytes] pinned host memory (the GPU reads it)
+ *             (read by the host; pinned pages the host has never touched
+ *             fault on first read, so fill it from the host)
+ *   cache     [R][cap_max][block_bytes] pinned host memory (the GPU reads it);
+ *             create zeroes it, which also maps every page for the host
  *   map       [R][n_blk] int32 pinned host memory: cache slot of each remote
  *             block, -1 if absent (written by the tier, read by the gather)
  *   capacity  [R] slots per request (<= cap_max)
- * Returns NULL on a bad argument.  Calls on one tier must not overlap.
+ * Returns NULL on a bad argument.  Calls on one tier must not overlap (a
+ * stream-ordered fetch counts as a call until its stream has passed it).
  */
 typedef struct oasis_host_tier oasis_host_tier;
 oasis_host_tier* oasis_host_tier_create(int32_t batch, int32_t n_kv_heads, int32_t top_k,
@@ -295,6 +299,13 @@ oasis_host_tier* oasis_host_tier_create(int32_t batch, int32_t n_kv_heads, int32
                                         size_t block_bytes, const void* remote, void* cache,
                                         int32_t* map);
 void oasis_host_tier_destroy(oasis_host_tier* t);
+
+/* Split each fetch's requests over n_workers host threads (1..64; 1, the
+ * default, runs on the calling thread).  Requests own disjoint state, so the
+ * result does not depend on n_workers.  [v2] §3.2.1 (ii) (remote fetch is CPU
+ * gather, transfer and scatter of whole blocks).  Errors: EINVAL, EHIP (a
+ * thread could not be started; the tier is left with one worker). */
+int oasis_host_tier_set_workers(oasis_host_tier* t, int32_t n_workers);
 
 /* One layer-step on the CPU, now: fetch the absent blocks of every request's
  * union of plan_src[r][g][i < plan_count[r][g]] (host arrays, [R][H] and
@@ -304,15 +315,40 @@ void oasis_host_tier_destroy(oasis_host_tier* t);
 int oasis_host_tier_fetch(oasis_host_tier* t, int64_t step, const int32_t* plan_count,
                           const int32_t* plan_src, const int32_t* slot_block);
 
-/* The same in stream order: copies plan_count / plan_src / slot_block (device
- * memory, as written by the plan) into the tier's pinned staging on `stream`,
- * then runs the fetch as a host function on that stream, stamped with the
- * tier's own step counter; work later on the stream (the mapped gather) sees
- * the updated cache and map.  Errors: EINVAL, EHIP; fetch failures are
- * counted (oasis_host_tier_state). */
-int oasis_host_tier_enqueue_fetch(oasis_host_tier* t, const int32_t* plan_count,
-                                  const int32_t* plan_src, const int32_t* slot_block,
-                                  hipStream_t stream);
+/*
+ * One layer-step's remote fetch and local gather, asynchronously (the
+ * remote-fetch and local-fetch stages of the per-layer prefetch pipeline,
+ * [v2] §3.3 and Fig. 8).  Queues a job for the tier's dispatcher thread and
+ * returns.  The dispatcher takes jobs in order: it waits on the host for
+ * `after` (recorded by the caller after the step that wrote the plan and last
+ * read the slots), copies plan_count / plan_src / slot_block back, fetches as
+ * oasis_host_tier_fetch (stamped with the tier's own step counter), launches
+ * oasis_copy_blocks_mapped(s, cache_k, cache_v, cap_max, map, ...) on
+ * copy_stream and records `done` on copy_stream after it.  No GPU queue waits
+ * on host memory.
+ *   s            shape of the resident store (batch = R, n_kv_heads = H; one
+ *                block is H records of tile_stride elements = block_bytes)
+ *   cache_k/_v   the cache's K and V tiles (pinned host memory)
+ *   res_k/_v     resident slots [R][H][top_k] (device memory)
+ *   plan_*       as written by oasis_select_plan; slot_block [R][H][top_k] is
+ *                the slot table after the plan (device memory)
+ *   after, done  caller events; `done` must not be waited on before
+ *                oasis_host_tier_wait_issued has returned for this job
+ * The plan, slot table and `after` must stay unchanged until `done` is
+ * issued.  Host calls that change the tier (fetch, add_generated, trim,
+ * set_workers) or read it (state) wait until every submitted job is issued.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP (setting up the dispatcher); errors of
+ * a dispatched job are returned by oasis_host_tier_wait_issued.
+ */
+int oasis_host_tier_submit(oasis_host_tier* t, const oasis_shape* s, const void* cache_k,
+                           const void* cache_v, void* res_k, void* res_v,
+                           const int32_t* plan_count, const int32_t* plan_src,
+                           const int32_t* plan_dst, const int32_t* slot_block, hipEvent_t after,
+                           hipStream_t copy_stream, hipEvent_t done);
+
+/* Host wait until every submitted job has been issued (its `done` recorded).
+ * Returns OASIS_OK or the first error of a dispatched job (sticky). */
+int oasis_host_tier_wait_issued(oasis_host_tier* t);
 
 /* A block generated on the decode node (already written to the cache slot
  * this returns through the map) joins request `req`'s cache, never evicted. */
@@ -324,8 +360,9 @@ int oasis_host_tier_add_generated(oasis_host_tier* t, int32_t req, int32_t block
 int oasis_host_tier_trim(oasis_host_tier* t, const int32_t* target, const int32_t* slot_block);
 
 /* Snapshot: slot_block_out [R][cap_max] (block per slot, -1 free) and
- * last_out [R][cap_max] (either may be NULL); stats_out[4] = blocks fetched,
- * blocks evicted, blocks that found no slot, stream-ordered steps run. */
+ * last_out [R][cap_max] (either may be NULL); stats_out[5] = blocks fetched,
+ * blocks evicted, blocks that found no slot, stream-ordered steps run, host
+ * nanoseconds spent inside fetches. */
 int oasis_host_tier_state(const oasis_host_tier* t, int32_t* slot_block_out, int64_t* last_out,
                           int64_t* stats_out);
 

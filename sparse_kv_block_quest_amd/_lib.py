@@ -37,8 +37,10 @@ EXPORTS = (
     "oasis_copy_blocks_mapped",
     "oasis_host_tier_create",
     "oasis_host_tier_destroy",
+    "oasis_host_tier_set_workers",
     "oasis_host_tier_fetch",
-    "oasis_host_tier_enqueue_fetch",
+    "oasis_host_tier_submit",
+    "oasis_host_tier_wait_issued",
     "oasis_host_tier_add_generated",
     "oasis_host_tier_trim",
     "oasis_host_tier_state",
@@ -118,8 +120,11 @@ def load() -> ctypes.CDLL:
     lib.oasis_host_tier_create.restype = _vp
     lib.oasis_host_tier_destroy.argtypes = [_vp]
     lib.oasis_host_tier_destroy.restype = None
+    lib.oasis_host_tier_set_workers.argtypes = [_vp, _i32]
     lib.oasis_host_tier_fetch.argtypes = [_vp, ctypes.c_int64, _vp, _vp, _vp]
-    lib.oasis_host_tier_enqueue_fetch.argtypes = [_vp, _vp, _vp, _vp, _vp]
+    lib.oasis_host_tier_submit.argtypes = [_vp, _shp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp]
+    lib.oasis_host_tier_wait_issued.argtypes = [_vp]
     lib.oasis_host_tier_add_generated.argtypes = [_vp, _i32, _i32, ctypes.c_int64, _vp]
     lib.oasis_host_tier_trim.argtypes = [_vp, _vp, _vp]
     lib.oasis_host_tier_state.argtypes = [_vp, _vp, _vp, _vp]
@@ -136,8 +141,9 @@ def load() -> ctypes.CDLL:
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
-    for name in ("oasis_copy_blocks_mapped", "oasis_host_tier_fetch",
-                 "oasis_host_tier_enqueue_fetch", "oasis_host_tier_add_generated",
+    for name in ("oasis_copy_blocks_mapped", "oasis_host_tier_fetch", "oasis_host_tier_set_workers",
+                 "oasis_host_tier_submit", "oasis_host_tier_wait_issued",
+                 "oasis_host_tier_add_generated",
                  "oasis_host_tier_trim", "oasis_host_tier_state"):
         getattr(lib, name).restype = ctypes.c_int
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan", "oasis_append_kv",

@@ -369,7 +369,7 @@ class HostTier:
     int32 (pinned).  The arrays must outlive the tier."""
 
     def __init__(self, batch: int, n_kv_heads: int, top_k: int, n_blk: int, capacity,
-                 remote, cache, map_, block_bytes: int):
+                 remote, cache, map_, block_bytes: int, workers: int = 1):
         import numpy as np
         self._lib = _lib.load()
         self.R, self.H, self.K, self.n_blk = int(batch), int(n_kv_heads), int(top_k), int(n_blk)
@@ -383,17 +383,56 @@ class HostTier:
         if not h:
             raise ValueError("oasis_host_tier_create rejected its arguments")
         self._h = ctypes.c_void_p(h)
+        if workers != 1:
+            self.set_workers(workers)
+
+    def set_workers(self, n: int) -> None:
+        """Host threads per fetch (no fetch may be in flight)."""
+        check("oasis_host_tier_set_workers", self._lib.oasis_host_tier_set_workers(self._h, int(n)))
 
     def fetch(self, step: int, plan_count, plan_src, slot_block=None) -> int:
         return int(self._lib.oasis_host_tier_fetch(self._h, int(step), _np_or_tensor_ptr(plan_count),
                                                    _np_or_tensor_ptr(plan_src),
                                                    _np_or_tensor_ptr(slot_block)))
 
-    def enqueue_fetch(self, plan_count: torch.Tensor, plan_src: torch.Tensor,
-                      slot_block: torch.Tensor, stream=None) -> None:
-        check("oasis_host_tier_enqueue_fetch",
-              self._lib.oasis_host_tier_enqueue_fetch(self._h, _ptr(plan_count), _ptr(plan_src),
-                                                      _ptr(slot_block), _stream(stream)))
+    def prepare_submit(self, cache: torch.Tensor, res_k: torch.Tensor, res_v: torch.Tensor,
+                       plan: dict, block_size: int):
+        """Prepared oasis_host_tier_submit for one layer: returns
+        ``submit(slot_block, after, copy_stream, done)`` (after / done: recorded
+        torch events).  cache: pinned [R][cap_max][H][2][B][D]; res_*: the
+        interleaved resident store; plan: the layer's plan buffers."""
+        if cache.dim() != 6 or cache.shape[3] != 2 or not cache.is_pinned():
+            raise ValueError("cache must be pinned [R][cap_max][H][2][B][D]")
+        R, cap_max, H, _, B, D = cache.shape
+        if int(block_size) != B or R != self.R or H != self.H:
+            raise ValueError("cache does not match the tier or block_size")
+        rptr_k, rs = _tile_store(res_k, "res_k", B * D)
+        rptr_v, rs2 = _tile_store(res_v, "res_v", B * D)
+        if rs != 2 * B * D or rs2 != rs:
+            raise ValueError("the resident store must be interleaved (tile stride 2*B*D)")
+        ck, cv = interleaved_kv(cache.view(R, cap_max * H, 2, B, D))
+        shp = _shape(R, 1, H, H, D, B, _dt(cache), rs)
+        for k in ("plan_count", "plan_src", "plan_dst"):
+            _i32(plan[k], k)
+        head = [self._h, ctypes.byref(shp), ctypes.c_void_p(ck.data_ptr()),
+                ctypes.c_void_p(cv.data_ptr()), ctypes.c_void_p(rptr_k), ctypes.c_void_p(rptr_v),
+                _ptr(plan["plan_count"]), _ptr(plan["plan_src"]), _ptr(plan["plan_dst"])]
+        keep = (shp, cache, res_k, res_v, plan)
+        fn = self._lib.oasis_host_tier_submit
+
+        def submit(slot_block: torch.Tensor, after, copy_stream, done) -> None:
+            if not after.cuda_event or not done.cuda_event:
+                raise ValueError("record both events once before submitting")
+            _ = keep
+            check("oasis_host_tier_submit",
+                  fn(*head, _ptr(_i32(slot_block, "slot_block")), ctypes.c_void_p(after.cuda_event),
+                     _stream(copy_stream), ctypes.c_void_p(done.cuda_event)))
+
+        return submit
+
+    def wait_issued(self) -> None:
+        """Host wait until every submitted job has been issued."""
+        check("oasis_host_tier_wait_issued", self._lib.oasis_host_tier_wait_issued(self._h))
 
     def add_generated(self, req: int, block: int, step: int, slot_block=None) -> int:
         return int(self._lib.oasis_host_tier_add_generated(self._h, int(req), int(block), int(step),
@@ -411,12 +450,12 @@ class HostTier:
         import numpy as np
         sb = np.empty((self.R, self.cap_max), np.int32)
         last = np.empty((self.R, self.cap_max), np.int64)
-        st = np.empty(4, np.int64)
+        st = np.empty(5, np.int64)
         check("oasis_host_tier_state",
               self._lib.oasis_host_tier_state(self._h, _np_or_tensor_ptr(sb),
                                               _np_or_tensor_ptr(last), _np_or_tensor_ptr(st)))
         return sb, last, {"fetched": int(st[0]), "evicted": int(st[1]), "failed": int(st[2]),
-                          "steps": int(st[3])}
+                          "steps": int(st[3]), "fetch_ns": int(st[4])}
 
     def close(self) -> None:
         if getattr(self, "_h", None):

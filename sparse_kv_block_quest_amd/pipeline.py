@@ -18,9 +18,17 @@ background copy stream and events that keep each layer's order); the steps
 themselves are the library's kernels, called through ``ops``.
 
 With a decode-host cache (Section 3.2: remote memory holds the full prompt KV,
-decode-host memory a bounded cache of whole blocks), the copy stream first
-copies the plan back and runs the cache's fetch of absent blocks as a host
-function, then gathers through the cache's union map.
+decode-host memory a bounded cache of whole blocks), each layer's cache has a
+dispatcher thread (oasis_host_tier_submit): once the step's attention is done
+it copies the plan back, fetches the absent whole blocks on the host, then
+launches the gather through the cache's union map on the copy stream and
+records the layer's copy event.  These are the remote-fetch and local-fetch
+stages of Section 3.3's per-layer pipeline; the dispatchers of different
+layers work side by side while the GPU runs other layers.  Before the main
+stream waits on a layer's copy event, the host waits until that layer's
+dispatcher has recorded it.  A layer's next fetch (which may evict cache
+slots) follows its next step, which waits for this gather, so a gather never
+reads a slot being replaced.
 """
 from __future__ import annotations
 
@@ -36,11 +44,14 @@ class PipelineLayer:
 
     def __init__(self, wl, host_store: torch.Tensor | None, summaries: torch.Tensor,
                  q0: torch.Tensor, device, opts=None, want_scores=False,
-                 remote_store: torch.Tensor | None = None, host_capacity: int | None = None):
+                 remote_store: torch.Tensor | None = None, host_capacity: int | None = None,
+                 host_workers: int = 1):
         """host_store: pinned [R][H][n_blk][2][B][D], the full store the copies
         read.  Or, with a decode-host cache: remote_store pinned
-        [R][n_blk][H][2][B][D] (whole blocks, standing in for remote memory) and
-        host_capacity blocks per request cached in decode-host memory."""
+        [R][n_blk][H][2][B][D] (whole blocks, standing in for remote memory;
+        filled from the host), host_capacity blocks per request cached in
+        decode-host memory, and host_workers threads per fetch (besides the
+        layer's dispatcher thread)."""
         R, H, K, B, D = wl.R, wl.H, wl.K, wl.B, wl.D
         self.wl = wl
         self.tier = None
@@ -55,7 +66,7 @@ class PipelineLayer:
             self.map = torch.empty((R, n_blk), dtype=torch.int32, pin_memory=True)
             block_bytes = H * 2 * B * D * remote_store.element_size()
             self.tier = ops.HostTier(R, H, K, n_blk, [cap] * R, remote_store, self.cache,
-                                     self.map, block_bytes)
+                                     self.map, block_bytes, workers=host_workers)
         else:
             if host_store is None or not host_store.is_pinned():
                 raise ValueError("the host store must be pinned")
@@ -78,10 +89,17 @@ class PipelineLayer:
             self.copy_call = ops.prepare_copy_blocks(self.host_k, self.host_v, self.res_k,
                                                      self.res_v, self.plan, B)
         else:
-            self.copy_call = ops.prepare_copy_blocks_mapped(self.cache, self.map, self.res_k,
-                                                            self.res_v, self.plan, B)
+            self.submit = self.tier.prepare_submit(self.cache, self.res_k, self.res_v, self.plan, B)
         self.attn_done = torch.cuda.Event()
         self.copy_done = torch.cuda.Event()
+        self.attn_done.record()  # created now: the dispatcher takes raw handles
+        self.copy_done.record()
+
+    def ready(self) -> None:
+        """Host wait until this layer's last copy event has been recorded (a
+        dispatcher records it; without a cache it already is)."""
+        if self.tier is not None:
+            self.tier.wait_issued()
 
     def seed(self, q0: torch.Tensor, copy_stream) -> None:
         """First working set from row 0 of the first queries (empty slots, no
@@ -91,17 +109,29 @@ class PipelineLayer:
         ops.select_plan(idx, self.blk[0], self.stamp[0], 0, wl.cap, pred_row=0,
                         plan=dict(self.plan, plan_evicted=None))
         self.attn_done.record()
-        copy_stream.wait_event(self.attn_done)
         self.copy(copy_stream, self.blk[0])
-        self.copy_done.record(copy_stream)
 
-    def copy(self, stream, slot_block: torch.Tensor) -> None:
-        """The planned blocks into their slots, on `stream`; through the
-        decode-host cache (fetch of absent whole blocks first) when there is one."""
+    def copy(self, stream, slot_block: torch.Tensor, events=None) -> None:
+        """The planned blocks into their slots on `stream` after this layer's
+        attn_done, then copy_done.  Through the decode-host cache when there is
+        one (fetch and gather by the dispatcher).  `events`: timing events
+        around the copy; with a cache they span submit to gather end, and the
+        host waits for the dispatcher in between (for timing runs only)."""
         if self.tier is not None:
-            self.tier.enqueue_fetch(self.plan["plan_count"], self.plan["plan_src"], slot_block,
-                                    stream)
+            if events:
+                events[0].record(stream)
+            self.submit(slot_block, self.attn_done, stream, self.copy_done)
+            if events:
+                self.tier.wait_issued()
+                events[1].record(stream)
+            return
+        stream.wait_event(self.attn_done)
+        if events:
+            events[0].record(stream)
         self.copy_call(stream)
+        if events:
+            events[1].record(stream)
+        self.copy_done.record(stream)
 
 
 class Pipeline:
@@ -116,18 +146,30 @@ class Pipeline:
         for layer, q0 in zip(self.layers, q0s):
             layer.seed(q0, self.copy_stream)
 
-    def layer_step(self, t: int, l: int, q: torch.Tensor) -> dict:
+    def layer_step(self, t: int, l: int, q: torch.Tensor, step_events=None,
+                   copy_events=None) -> dict:
         """Step t of layer l with stacked queries q; returns the fused call's
-        result dict (its buffers are reused by this layer's next step)."""
+        result dict (its buffers are reused by this layer's next step).
+        Optional timing events: around the fused step (main stream) and around
+        the direct copy (copy stream)."""
         L = self.layers[l]
         main = torch.cuda.current_stream()
+        L.ready()
         main.wait_event(L.copy_done)
+        if step_events:
+            step_events[0].record(main)
         res = L.step_calls[t % 2](t + 1, q)
+        if step_events:
+            step_events[1].record(main)
         L.attn_done.record(main)
-        self.copy_stream.wait_event(L.attn_done)
-        L.copy(self.copy_stream, L.blk[1 - t % 2])
-        L.copy_done.record(self.copy_stream)
+        L.copy(self.copy_stream, L.blk[1 - t % 2], copy_events)
         return res
+
+    def drain(self) -> None:
+        """Host wait until every submitted copy has been issued; after this,
+        waiting on the copy stream covers all of them."""
+        for L in self.layers:
+            L.ready()
 
     def resident_blocks(self, l: int, t: int) -> torch.Tensor:
         """Slot table that describes layer l's resident store during step t."""

@@ -201,3 +201,41 @@ def test_scoring_variant_validation(lib):
     # the fused step: pred_row must be a scored row (2 rows with averaging)
     assert _step(lib, three, pred=2, opts=ctypes.byref(avg)) == E
     assert _step(lib, three, opts=None) == E
+
+
+def test_host_tier_submit_validation(lib):
+    """oasis_host_tier_submit rejects bad calls before any HIP call; a tier with
+    nothing submitted reports every job issued."""
+    import numpy as np
+    R, H, K, n_blk, B, D = 1, 2, 4, 8, 16, 128
+    rec = 2 * B * D * 2                        # interleaved bf16 record
+    remote = np.zeros((R, n_blk, H * rec), np.uint8)
+    cache = np.zeros((R, 4, H * rec), np.uint8)
+    map_ = np.zeros((R, n_blk), np.int32)
+    cap = np.array([4], np.int32)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    t = lib.oasis_host_tier_create(R, H, K, n_blk, ptr(cap), 4, H * rec, ptr(remote), ptr(cache),
+                                   ptr(map_))
+    assert t
+    t = ctypes.c_void_p(t)
+    E = _lib.OASIS_EINVAL
+    try:
+        good = _shape(batch=R, n_q=1, n_q_heads=H, n_kv_heads=H, tile_stride=2 * B * D)
+        args = [FAKE] * 8 + [FAKE, None, FAKE]     # caches, res, plan x3, slots, after, stream, done
+        assert lib.oasis_host_tier_submit(None, ctypes.byref(good), *args) == E
+        assert lib.oasis_host_tier_submit(t, None, *args) == E
+        wrong_r = _shape(batch=2, n_q=1, n_q_heads=H, n_kv_heads=H, tile_stride=2 * B * D)
+        assert lib.oasis_host_tier_submit(t, ctypes.byref(wrong_r), *args) == E
+        # records of B*D elements: two per block do not fill block_bytes
+        narrow = _shape(batch=R, n_q=1, n_q_heads=H, n_kv_heads=H)
+        assert lib.oasis_host_tier_submit(t, ctypes.byref(narrow), *args) == E
+        no_after = [FAKE] * 8 + [None, None, FAKE]
+        assert lib.oasis_host_tier_submit(t, ctypes.byref(good), *no_after) == E
+        no_done = [FAKE] * 8 + [FAKE, None, None]
+        assert lib.oasis_host_tier_submit(t, ctypes.byref(good), *no_done) == E
+        assert lib.oasis_host_tier_wait_issued(t) == 0
+        assert lib.oasis_host_tier_wait_issued(None) == E
+        assert lib.oasis_host_tier_set_workers(t, 0) == E
+        assert lib.oasis_host_tier_set_workers(None, 2) == E
+    finally:
+        lib.oasis_host_tier_destroy(t)

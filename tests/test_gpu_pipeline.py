@@ -24,7 +24,7 @@ def say(msg):
     print(msg, flush=True)
 
 
-def build(wl, dev, n_layers, opts=None, want_scores=True, host_capacity=None):
+def build(wl, dev, n_layers, opts=None, want_scores=True, host_capacity=None, host_workers=1):
     layers, q0s, full = [], [], []
     for l in range(n_layers):
         qf = synth.queries(wl, dev, layer=l)
@@ -42,10 +42,11 @@ def build(wl, dev, n_layers, opts=None, want_scores=True, host_capacity=None):
         else:  # remote memory holds whole blocks [R][n_blk][H][2][B][D]
             whole = store.permute(0, 2, 1, 3, 4, 5).contiguous()
             remote = torch.empty(whole.shape, dtype=whole.dtype, pin_memory=True)
-            remote.copy_(whole)
+            remote.copy_(whole.cpu())
             layers.append(pipeline.PipelineLayer(wl, None, summ, q0, dev, opts=opts,
                                                  want_scores=want_scores, remote_store=remote,
-                                                 host_capacity=host_capacity))
+                                                 host_capacity=host_capacity,
+                                                 host_workers=host_workers))
         q0s.append(q0)
         full.append((k, v, store))
     return pipeline.Pipeline(layers), q0s, full
@@ -78,7 +79,8 @@ def resident_matches_host(layer, blk):
     assert torch.equal(layer.res.view(torch.int16), want.view(torch.int16))
 
 
-def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_capacity=None):
+def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_capacity=None,
+                      host_workers=1):
     dev = cuda
     qs = query_steps(wl, dev, n_layers, n_steps)
     n_valid = np.full(wl.R, wl.n_blk, np.int32)
@@ -86,8 +88,10 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_c
         units = [(r, g) for r in range(wl.R) for g in range(wl.H)]
 
     # run A: checked step by step
-    pa, q0s, full = build(wl, dev, n_layers, opts, host_capacity=host_capacity)
+    pa, q0s, full = build(wl, dev, n_layers, opts, host_capacity=host_capacity,
+                          host_workers=host_workers)
     pa.seed(q0s)
+    pa.drain()
     torch.cuda.synchronize()
     outs_a = []
     models = None
@@ -104,6 +108,7 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_c
             say(f"  pipeline A step {t} layer {l}")
             L = pa.layers[l]
             res = pa.layer_step(t, l, qs[t][l])
+            pa.drain()
             torch.cuda.synchronize()
             a, b = t % 2, 1 - t % 2
             k, v, _ = full[l]
@@ -119,13 +124,15 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_c
     del pa
 
     # run B: free-running, events only
-    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False, host_capacity=host_capacity)
+    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False, host_capacity=host_capacity,
+                       host_workers=host_workers)
     pb.seed(q0s)
     outs_b = []
     for t in range(n_steps):
         for l in range(n_layers):
             res = pb.layer_step(t, l, qs[t][l])
             outs_b.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
+    pb.drain()
     torch.cuda.synchronize()
     say("  pipeline B done")
     for i, (xa, xb) in enumerate(zip(outs_a, outs_b)):
@@ -148,11 +155,21 @@ def test_pipeline_full_shape(cuda):
     run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)])
 
 
-@pytest.mark.parametrize("cap", [40, 36])
-def test_pipeline_with_decode_host_cache(cuda, cap):
+@pytest.mark.parametrize("cap,workers", [(40, 1), (36, 1), (36, 3)])
+def test_pipeline_with_decode_host_cache(cuda, cap, workers):
     """Remote memory holds whole blocks; a bounded decode-host cache (2 heads x
     16 slots = at most 32 working-set blocks per request) feeds the gather
-    through its union map; the cache evicts and refetches as the sets drift."""
+    through its union map; the cache evicts and refetches as the sets drift.
+    The fetch runs on its own stream, on `workers` host threads."""
     wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=2048, K=16, cap=4)
-    say(f"pipeline with decode-host cache, capacity {cap}")
-    run_pipeline_case(cuda, wl, 2, 5, host_capacity=cap)
+    say(f"pipeline with decode-host cache, capacity {cap}, {workers} fetch workers")
+    run_pipeline_case(cuda, wl, 2, 5, host_capacity=cap, host_workers=workers)
+
+
+def test_pipeline_with_decode_host_cache_full_shape(cuda):
+    """The Qwen3-8B pipeline shape with f_Host = 0.6 (1229 cached blocks per
+    request of 2048), four fetch workers, two layers."""
+    wl = synth.workload("qwen3-8b-pipeline", layers=2)
+    say("pipeline qwen3-8b shape with decode-host cache 1229, 2 layers x 2 steps")
+    run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)], host_capacity=1229,
+                      host_workers=4)

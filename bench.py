@@ -96,11 +96,18 @@ def per_ls_alg(units, ab):
     return units * sum(ab.values())
 
 
-def kernel_source_hash():
+# What the fused layer-step kernel is compiled from (sources and build flags).
+FUSED_SOURCES = ("csrc/oasis_internal.h", "csrc/step.hip", "csrc/step_device.h", "build.py")
+
+
+def kernel_source_hash(files=FUSED_SOURCES):
+    """sha256[:16] over the named package files (None: every file in csrc/)."""
+    pkg = os.path.join(ROOT, "sparse_kv_block_quest_amd")
+    if files is None:
+        files = ["csrc/" + n for n in sorted(os.listdir(os.path.join(pkg, "csrc")))]
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_kv_block_quest_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in files:
+        with open(os.path.join(pkg, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -416,7 +423,7 @@ def report_grow(args, wl, g):
                        "frac": round(per_ls / (ls_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "blocks_completed_per_step": round(g["inserted_per_step"], 3),
         "host_issue_us_per_layer_step": round(g["wall_s"] * 1e6 / n_ls, 2),
-        "kernel_sources": kernel_source_hash(),
+        "kernel_sources": kernel_source_hash(None),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
@@ -514,7 +521,7 @@ def report_quality(args, wl, q):
         "quality": q,
         "note": "reported, not a target: the pages' 98.74% (draft) and 84% (previous token, "
                 "top-20) come from real models; these come from synthetic drift",
-        "kernel_sources": kernel_source_hash(),
+        "kernel_sources": kernel_source_hash(None),
     }
     print(json.dumps(line), flush=True)
     return 0
@@ -691,7 +698,7 @@ def report_pipeline(args, wl, g):
         "admitted_blocks_per_head_step": round(g["admitted_per_head_step"], 3),
         "host_issue_us_per_layer_step": round(g["wall_s"] * 1e6 / n_ls, 2),
         "decode_host_cache": g["tier"],
-        "kernel_sources": kernel_source_hash(),
+        "kernel_sources": kernel_source_hash(None),
         "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)

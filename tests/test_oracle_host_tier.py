@@ -63,8 +63,20 @@ def test_host_tier_invariants(seed, R, H, K, n_blk, cap):
                         union.append(int(src[r, g, i]))
             absent[r] = [b for b in union if m.map[r, b] < 0]
         before = [list(x) for x in m.slot_blk]
+        last_before = [list(x) for x in m.last]
         got = m.fetch(step, cnt, src, work)
         for r in range(R):
+            # least recently used first: every evicted block was used no later
+            # than every evictable block that stayed
+            union_r = {int(src[r, g, i]) for g in range(H) for i in range(cnt[r, g])}
+            keep = {int(x) for x in work[r].ravel()} | union_r | m.generated[r]
+            after = set(m.slot_blk[r])
+            ev_last = [last_before[r][s] for s, b in enumerate(before[r])
+                       if b >= 0 and b not in after]
+            stay_last = [last_before[r][s] for s, b in enumerate(before[r])
+                         if b >= 0 and b in after and b not in keep]
+            if ev_last and stay_last:
+                assert max(ev_last) <= min(stay_last)
             # exactly the absent blocks are fetched, in union order
             assert [b for rr, b, _ in got if rr == r] == absent[r]
             protected = {int(x) for x in work[r].ravel()}

@@ -322,13 +322,14 @@ static int device_view(const void* p, const void** out) {
     return OASIS_EINVAL;
 }
 
-static int launch_mapped(const oasis_host_tier* t, const TierJob& j) {
-    hipLaunchKernelGGL(copy_mapped_kernel, dim3(kMapCopySplit, (unsigned)(t->R * t->H)),
+// The gather of one layer-step: units = R*H (<= 65535, checked by callers).
+static int launch_mapped(int units, int H, int n_blk, int cap_max, int K, const TierJob& j) {
+    hipLaunchKernelGGL(copy_mapped_kernel, dim3(kMapCopySplit, (unsigned)units),
                        dim3(kMapCopyThreads), 0, j.copy_stream,
                        reinterpret_cast<const uint4*>(j.dev_k),
                        reinterpret_cast<const uint4*>(j.dev_v),
-                       reinterpret_cast<const int32_t*>(j.dev_map), t->H, t->n_blk, t->cap_max,
-                       reinterpret_cast<uint4*>(j.res_k), reinterpret_cast<uint4*>(j.res_v), t->K,
+                       reinterpret_cast<const int32_t*>(j.dev_map), H, n_blk, cap_max,
+                       reinterpret_cast<uint4*>(j.res_k), reinterpret_cast<uint4*>(j.res_v), K,
                        j.tile_u4, j.stride_u4, j.plan_count, j.plan_src, j.plan_dst);
     return launch_status();
 }
@@ -349,7 +350,7 @@ static int run_job(oasis_host_tier* t, const TierJob& j) {
         return OASIS_EHIP;
     }
     (void)tier_fetch(t, ++t->clock, t->st_count, t->st_src, t->st_slots);  // failures counted
-    const int st = launch_mapped(t, j);
+    const int st = launch_mapped(t->R * t->H, t->H, t->n_blk, t->cap_max, t->K, j);
     if (st != OASIS_OK) return st;
     if (hipEventRecord(j.done, j.copy_stream) != hipSuccess) {
         (void)hipGetLastError();
@@ -608,15 +609,17 @@ extern "C" int oasis_copy_blocks_mapped(const oasis_shape* s, const void* cache_
     if (tile_bytes % 16) return OASIS_EUNSUPPORTED;
     const long long units = (long long)s->batch * s->n_kv_heads;
     if (units > 65535) return OASIS_EUNSUPPORTED;
-    const void *dk = nullptr, *dv = nullptr, *dm = nullptr;
-    if (device_view(cache_k, &dk) != OASIS_OK || device_view(cache_v, &dv) != OASIS_OK ||
-        device_view(map, &dm) != OASIS_OK)
+    TierJob j{};
+    if (device_view(cache_k, &j.dev_k) != OASIS_OK || device_view(cache_v, &j.dev_v) != OASIS_OK ||
+        device_view(map, &j.dev_map) != OASIS_OK)
         return OASIS_EINVAL;
-    hipLaunchKernelGGL(copy_mapped_kernel, dim3(kMapCopySplit, (unsigned)units),
-                       dim3(kMapCopyThreads), 0, stream, reinterpret_cast<const uint4*>(dk),
-                       reinterpret_cast<const uint4*>(dv), reinterpret_cast<const int32_t*>(dm),
-                       s->n_kv_heads, n_blk, cap_max, reinterpret_cast<uint4*>(res_k),
-                       reinterpret_cast<uint4*>(res_v), top_k, int(tile_bytes / 16),
-                       tile_stride_of(s) * eb / 16, plan_count, plan_src, plan_dst);
-    return launch_status();
+    j.res_k = res_k;
+    j.res_v = res_v;
+    j.tile_u4 = int(tile_bytes / 16);
+    j.stride_u4 = tile_stride_of(s) * eb / 16;
+    j.plan_count = plan_count;
+    j.plan_src = plan_src;
+    j.plan_dst = plan_dst;
+    j.copy_stream = stream;
+    return launch_mapped((int)units, s->n_kv_heads, n_blk, cap_max, top_k, j);
 }

@@ -150,24 +150,31 @@ append_kv_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
     const long long u = i / D;
     const int d = (int)(i - u * D);
     const int r = (int)(u / H);
+    // The new token does not depend on pos: its loads go out with pos's, so a
+    // thread waits for one round trip before its stores (and, for a token that
+    // completes its block, for one more before the summary stores).
     const int p = pos[r];
+    const E kx = reinterpret_cast<const E*>(k_new)[i];
+    const E vx = reinterpret_cast<const E*>(v_new)[i];
     if (p < 0) return;
     const int b = p / B, t = p - b * B;
     const size_t tile = ((size_t)u * n_blk_max + b) * (size_t)stride;
-    const E kx = reinterpret_cast<const E*>(k_new)[i];
-    reinterpret_cast<E*>(kt)[tile + (size_t)t * D + d] = kx;
-    reinterpret_cast<E*>(vt)[tile + (size_t)d * B + t] = reinterpret_cast<const E*>(v_new)[i];
     if (summ && t == B - 1) {
         float lo = load_elem<DT>(&kx, 0), hi = lo;
-        for (int j = 0; j < B - 1; ++j) {
+        for (int j = 0; j < B - 1; ++j) {  // rows written by earlier launches
             const float x = load_elem<DT>(kt, tile + (size_t)j * D + d);
             lo = fminf(lo, x);
             hi = fmaxf(hi, x);
         }
+        reinterpret_cast<E*>(kt)[tile + (size_t)t * D + d] = kx;
+        reinterpret_cast<E*>(vt)[tile + (size_t)d * B + t] = vx;
         const size_t so = ((size_t)u * n_blk_max + b) * 2 * D + d;
         store_elem<DT>(summ, so, lo);
         store_elem<DT>(summ, so + D, hi);
+        return;
     }
+    reinterpret_cast<E*>(kt)[tile + (size_t)t * D + d] = kx;
+    reinterpret_cast<E*>(vt)[tile + (size_t)d * B + t] = vx;
 }
 
 extern "C" int oasis_append_kv(const oasis_shape* s, const void* k_new, const void* v_new,

@@ -291,6 +291,63 @@ def test_copy_blocks_bitwise(cuda, pinned, interleaved):
     np.testing.assert_array_equal(u8(rv), ev)
 
 
+@pytest.mark.parametrize("workers", [1, 3])
+def test_copy_blocks_mapped_bitwise(cuda, workers):
+    """Host fetch into the decode-host cache (oasis_host_tier_fetch), then the
+    gather through the union map (oasis_copy_blocks_mapped): the planned slots
+    hold the remote blocks' records, entries whose block is absent are skipped
+    (their slots keep what they held), over three rounds with evictions."""
+    say(f"copy_blocks_mapped workers={workers}")
+    R, H, nb, K, B, D, cap = 3, 4, 96, 8, 16, 128, 40
+    gen = synth.generator(29, synth.S_MISC, cuda)
+    rec = synth.normal((R, nb, H, 2, B, D), gen, cuda, torch.bfloat16)
+    remote = torch.empty(rec.shape, dtype=rec.dtype, pin_memory=True)
+    remote.copy_(rec.cpu())
+    cache = torch.empty((R, cap, H, 2, B, D), dtype=rec.dtype, pin_memory=True)
+    map_ = torch.empty((R, nb), dtype=torch.int32, pin_memory=True)
+    tier = ops.HostTier(R, H, K, nb, [cap] * R, remote, cache, map_, H * 2 * B * D * 2,
+                        workers=workers)
+    res = synth.normal((R, H, K, 2, B, D), gen, cuda, torch.bfloat16)
+    rk, rv = ops.interleaved_kv(res)
+    rng = np.random.default_rng(12)
+    u8 = lambda t: t.cpu().contiguous().view(torch.uint8).numpy().reshape(R, H, t.shape[2], -1)
+    src_store = remote.permute(0, 2, 1, 3, 4, 5).contiguous()     # [R][H][nb][2][B][D]
+    for step in range(1, 4):
+        cnt = rng.integers(1, K + 1, (R, H)).astype(np.int32)
+        src = np.stack([[rng.permutation(nb)[:K] for _ in range(H)] for _ in range(R)]).astype(np.int32)
+        dst = np.stack([[rng.permutation(K) for _ in range(H)] for _ in range(R)]).astype(np.int32)
+        # unit (r, 0)'s last planned block is left out of the fetch: absent unless cached
+        fcnt = cnt.copy()
+        fcnt[:, 0] -= 1
+        assert tier.fetch(step, fcnt, src, None) == 0
+        plan = {"plan_count": torch.from_numpy(cnt).to(cuda),
+                "plan_src": torch.from_numpy(src).to(cuda),
+                "plan_dst": torch.from_numpy(dst).to(cuda)}
+        present = map_.numpy()[np.arange(R)[:, None, None], src] >= 0      # [R][H][K]
+        ecnt = cnt.copy()
+        esrc, edst = src.copy(), dst.copy()
+        for r in range(R):       # the oracle copies exactly the present entries, in order
+            for g in range(H):
+                keep = [i for i in range(cnt[r, g]) if present[r, g, i]]
+                ecnt[r, g] = len(keep)
+                esrc[r, g, :len(keep)] = src[r, g, keep]
+                edst[r, g, :len(keep)] = dst[r, g, keep]
+        assert (ecnt <= cnt).all() and ecnt.sum() >= cnt.sum() - R
+        before = u8(res)
+        both = lambda t: t.reshape(R, H, t.shape[2], 2, -1)
+        ek, ev = oracle.copy_blocks(both(u8(src_store))[..., 0, :].copy(),
+                                    both(u8(src_store))[..., 1, :].copy(),
+                                    both(before)[..., 0, :].copy(), both(before)[..., 1, :].copy(),
+                                    ecnt, esrc, edst)
+        ops.prepare_copy_blocks_mapped(cache, map_, rk, rv, plan, B)(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        got = both(u8(res))
+        np.testing.assert_array_equal(got[..., 0, :], ek)
+        np.testing.assert_array_equal(got[..., 1, :], ev)
+    assert tier.state()[2]["evicted"] > 0
+    tier.close()
+
+
 # ------------------------------------------------------------------ attention
 def attn_reference(q, k, vt, table, unit_stride, B, tail_tile=None, tail_len=None, scale=0.0):
     D = q.shape[-1]

@@ -63,6 +63,9 @@ def parse_args(argv=None):
                    help="score s_b(alpha) instead of the exact bound")
     p.add_argument("--draft-avg", action="store_true",
                    help="three query rows; the two drafts are averaged before scoring")
+    p.add_argument("--grow-write", choices=("fused", "append"), default="fused",
+                   help="--grow: append the new token inside the fused step (one launch) or "
+                        "with oasis_append_kv before it")
     p.add_argument("--host-frac", type=float, default=None,
                    help="--pipeline: decode-host cache of this fraction of each request's "
                         "blocks in front of a remote store (default: the full store in host "
@@ -316,12 +319,14 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
 # ----------------------------------------------------------------- growing contexts
 def run_grow(args, wl, torch, synth, ops):
     """Decode with growing contexts: every layer-step appends one new token's key
-    and value per request to the layer's store with oasis_append_kv (which also
-    rebuilds the summaries of a block the token completes), then runs the fused
-    step with the active block as the always-attended tail and the
-    just-completed block inserted into every KV head's resident set.  Lengths
+    and value per request to the layer's store (and the summaries of a block
+    the token completes) and runs the fused step with the active block as the
+    always-attended tail and the just-completed block inserted into every KV
+    head's resident set.  --grow-write fused (default) does both in one launch
+    (oasis_lookahead_step_append); append runs oasis_append_kv first.  Lengths
     start staggered below the store's capacity (wl.L tokens) and grow by one
     per step."""
+    fused = args.grow_write == "fused"
     dev = torch.device("cuda:0")
     n_layers = wl.layers
     impl = {"auto": ops.IMPL_AUTO, "valu": ops.IMPL_VALU, "mfma": ops.IMPL_MFMA}[args.impl]
@@ -355,18 +360,21 @@ def run_grow(args, wl, torch, synth, ops):
         ops.select_plan(idx, blk[l][0], stamp[l][0], 0, wl.cap, pred_row=0)
     opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
     bufs = {}
+    L = L0.clone()
+    pos = torch.zeros(R, dtype=torch.int32, device=dev)
+    tail = (dict(new_token=(knew[0, 0], vnew[0, 0], pos)) if fused else
+            dict(tail_tile=tail_tile, tail_len=tail_len))
     calls = [[ops.prepare_lookahead_step(
         qseq[0, l], layers[l]["summ"], K, blk[l][p], stamp[l][p], blk[l][1 - p], stamp[l][1 - p],
         0, wl.cap, layers[l]["keys"], layers[l]["vt"], blk[l][p], wl.n_blk, B, pred_row=1,
-        n_blk=n_blk, ins_blk=ins, tail_tile=tail_tile, tail_len=tail_len, want_evicted=False,
-        opts=opts, bufs=bufs) for p in range(2)] for l in range(n_layers)]
-    L = L0.clone()
-    pos = torch.zeros(R, dtype=torch.int32, device=dev)
+        n_blk=n_blk, ins_blk=ins, want_evicted=False, opts=opts, bufs=bufs, **tail)
+        for p in range(2)] for l in range(n_layers)]
     # One prepared append per (step, layer): the token write and, for a token
     # that completes its block, that block's summaries, in one launch.
-    appends = [[ops.prepare_append_kv(knew[t, l], vnew[t, l], pos, layers[l]["keys"],
-                                      layers[l]["vt"], B, summaries=layers[l]["summ"])
-                for l in range(n_layers)] for t in range(T)]
+    appends = None if fused else [
+        [ops.prepare_append_kv(knew[t, l], vnew[t, l], pos, layers[l]["keys"], layers[l]["vt"], B,
+                               summaries=layers[l]["summ"])
+         for l in range(n_layers)] for t in range(T)]
     inserted = torch.zeros((), dtype=torch.int64, device=dev)
 
     def step(t):
@@ -380,8 +388,11 @@ def run_grow(args, wl, torch, synth, ops):
         tail_tile.copy_(act[:, None].expand(R, H))
         ins.copy_(torch.where(tl == B, act, torch.full_like(act, -1)))
         for l in range(n_layers):
-            appends[t][l]()
-            calls[l][t % 2](t + 1, qseq[t, l])
+            if fused:
+                calls[l][t % 2](t + 1, qseq[t, l], token=(knew[t, l], vnew[t, l], pos))
+            else:
+                appends[t][l]()
+                calls[l][t % 2](t + 1, qseq[t, l])
         inserted.add_((ins >= 0).sum())
 
     for t in range(args.warmup):
@@ -417,7 +428,11 @@ def report_grow(args, wl, g):
         "config": {"workload": f"{wl.name}: {wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}, "
                                f"contexts {g['L_start']}..{g['L_end']} tokens growing one per step",
                    "batch": wl.R, "store_capacity": wl.L, "block": wl.B, "top_k_blocks": wl.K,
-                   "layers": wl.layers, "cap": wl.cap, "kv_layout": args.kv_layout},
+                   "layers": wl.layers, "cap": wl.cap, "kv_layout": args.kv_layout,
+                   "token_write": ("in the fused step (oasis_lookahead_step_append)"
+                                   if args.grow_write == "fused" else
+                                   "oasis_append_kv, then the fused step")},
+        "launches_per_layer_step": 1 if args.grow_write == "fused" else 2,
         "layer_step": {"us": round(ls_us, 2), "algo_bytes_fused": per_ls,
                        "GBps_fused_bytes": round(per_ls / (ls_us * 1e-6) / 1e9, 1),
                        "frac": round(per_ls / (ls_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},

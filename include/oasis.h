@@ -476,6 +476,41 @@ int oasis_lookahead_step(const oasis_shape* s, const void* q, const void* summar
                          float scale, void* out, float* lse, const oasis_step_opts* opts,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * oasis_lookahead_step with the decode step's new token appended in the same
+ * launch (a growing context, [v2] §3.2.1 (i): each generated token's KV joins
+ * its active block, and a block it fills becomes a summarised, selectable
+ * block).  Results equal
+ *   oasis_append_kv(s, k_new, v_new, pos, k_tiles, v_tiles, n_blk_max, summaries)
+ *   oasis_lookahead_step(..., unit_stride = n_blk_max, tail_tile[r][g] = pos[r] / B,
+ *                        tail_len[r] = pos[r] % B + 1, ...)
+ * (no active block for a request with pos[r] < 0): the stores, summaries and
+ * integer outputs bit for bit, attention up to rounding (the new token joins
+ * each row's softmax after the resident tiles and the stored part of the
+ * active block, read from k_new / v_new).
+ *   k_new, v_new  [R][H][D] the token's key and value (dtype)
+ *   pos           [R] int32 its position, < 0 = none
+ *   k_tiles, v_tiles, summaries  the full cache (written: the token's row and
+ *                 column, the summary of a block the token completes)
+ *   unit_stride   must equal n_blk_max (EINVAL otherwise)
+ *   n_blk         must not count the active block (n_blk[r] <= pos[r] / B); the
+ *                 plan's ins_blk is the caller's, as in oasis_lookahead_step
+ * Other arguments as oasis_lookahead_step.  Errors: EINVAL, EUNSUPPORTED,
+ * EWORKSPACE, EHIP.
+ */
+int oasis_lookahead_step_append(const oasis_shape* s, const void* q, void* summaries,
+                                int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
+                                int32_t* topk_idx, float* topk_score, float* scores,
+                                const int32_t* slot_block_in, const int32_t* slot_stamp_in,
+                                int32_t* slot_block_out, int32_t* slot_stamp_out, int32_t step,
+                                int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+                                int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
+                                int32_t* plan_evicted, void* k_tiles, void* v_tiles,
+                                const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
+                                const void* k_new, const void* v_new, const int32_t* pos,
+                                float scale, void* out, float* lse, const oasis_step_opts* opts,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,7 @@ EXPORTS = (
     "oasis_sparse_attn_impl",
     "oasis_lookahead_step_workspace",
     "oasis_lookahead_step",
+    "oasis_lookahead_step_append",
 )
 
 
@@ -141,6 +142,11 @@ def load() -> ctypes.CDLL:
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
+    lib.oasis_lookahead_step_append.argtypes = (
+        [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp,          # q .. scores
+         _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
+         _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, _vp,      # store, table, new token
+         ctypes.c_float, _vp, _vp, _opts, _vp, _sz, _vp])
     for name in ("oasis_copy_blocks_mapped", "oasis_host_tier_fetch", "oasis_host_tier_set_workers",
                  "oasis_host_tier_submit", "oasis_host_tier_wait_issued",
                  "oasis_host_tier_add_generated",
@@ -148,7 +154,7 @@ def load() -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan", "oasis_append_kv",
                  "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl",
-                 "oasis_lookahead_step"):
+                 "oasis_lookahead_step", "oasis_lookahead_step_append"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

@@ -49,14 +49,14 @@ static int set_lds(const void* kern, size_t lds) {
     return OASIS_OK;
 }
 
-template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN>
+template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN, bool TOK = false>
 static int launch_step(const StepArgs& a, size_t lds, hipStream_t st) {
     const long long per_xcd = (long long)((a.U + 7) / 8) *
                               ((SCAN ? a.scan_items : 0) + (ATT != kAttnNone ? a.attn_items : 0));
     const long long grid = 8 * per_xcd;
     if (grid == 0) return OASIS_OK;
     if (grid > 0x7fffffffLL) return OASIS_EUNSUPPORTED;
-    auto kern = step_kernel<DT, D, NQ, ATT, NRG, SCAN>;
+    auto kern = step_kernel<DT, D, NQ, ATT, NRG, SCAN, TOK>;
     int rc = set_lds(reinterpret_cast<const void*>(kern), lds);
     if (rc != OASIS_OK) return rc;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kNT), lds, st, a);
@@ -79,16 +79,28 @@ static int launch_finish(const StepArgs& a, hipStream_t st) {
     return launch_status();
 }
 
-template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN>
+template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN, bool TOK = false>
 static int launch_both(const StepArgs& a, size_t lds, hipStream_t st) {
-    int rc = launch_step<DT, D, NQ, ATT, NRG, SCAN>(a, lds, st);
+    int rc = launch_step<DT, D, NQ, ATT, NRG, SCAN, TOK>(a, lds, st);
     if (rc != OASIS_OK) return rc;
     return launch_finish<DT, D, NQ>(a, st);
 }
 
-// Fused scan + attention launch: choose the instantiation.
+// Fused scan + attention launch: choose the instantiation (TOK: a new token
+// per request is appended in the same launch).
 template <int DT, int D, int NQ>
 static int launch_fused(const StepArgs& a, int att, size_t lds, hipStream_t st) {
+    if (a.pos) {
+        if (att == kAttnMfma) {
+            if constexpr (DT == OASIS_BF16) {
+                if (a.NR <= 16)
+                    return launch_both<DT, D, NQ, kAttnMfma, 1, true, true>(a, lds, st);
+                return launch_both<DT, D, NQ, kAttnMfma, 2, true, true>(a, lds, st);
+            }
+            return OASIS_EUNSUPPORTED;
+        }
+        return launch_both<DT, D, NQ, kAttnValu, 1, true, true>(a, lds, st);
+    }
     if (att == kAttnMfma) {
         if constexpr (DT == OASIS_BF16) {
             if (a.NR <= 16) return launch_both<DT, D, NQ, kAttnMfma, 1, true>(a, lds, st);
@@ -410,16 +422,24 @@ extern "C" size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n
                      scored_rows(s, opts)).total;
 }
 
-extern "C" int oasis_lookahead_step(
+// The fused layer-step; with `tok` (k_new, v_new, pos) also the append of
+// one token per request (oasis_lookahead_step_append).
+struct NewToken {
+    const void* k_new;
+    const void* v_new;
+    const int32_t* pos;
+};
+
+static int lookahead(
     const oasis_shape* s, const void* q, const void* summaries, int32_t n_blk_max,
     const int32_t* n_blk, int32_t top_k, int32_t* topk_idx, float* topk_score, float* scores,
     const int32_t* slot_block_in, const int32_t* slot_stamp_in, int32_t* slot_block_out,
     int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, const int32_t* ins_blk,
-    int32_t* plan_count,
-    int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted, const void* k_tiles,
-    const void* v_tiles, const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
-    const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out, float* lse,
-    const oasis_step_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted,
+    const void* k_tiles, const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
+    int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out,
+    float* lse, const oasis_step_opts* opts, void* workspace, size_t workspace_bytes,
+    hipStream_t stream, const NewToken* tok) {
     int st = step_check(s, n_blk_max, top_k, n_sel, opts);
     if (st != OASIS_OK) return st;
     const int NS = scored_rows(s, opts);
@@ -460,6 +480,49 @@ extern "C" int oasis_lookahead_step(
     a.plan_src = plan_src;
     a.plan_dst = plan_dst;
     a.plan_evicted = plan_evicted;
+    if (tok) {
+        a.k_new = reinterpret_cast<const uint8_t*>(tok->k_new);
+        a.v_new = reinterpret_cast<const uint8_t*>(tok->v_new);
+        a.pos = tok->pos;
+        a.kt_w = const_cast<uint8_t*>(a.kt);
+        a.vt_w = const_cast<uint8_t*>(a.vt);
+        a.summ_w = const_cast<uint8_t*>(a.summ);
+    }
     return dispatch(a, s->dtype, s->head_dim, NS, att, Role::kFused,
                     lds_for(a, Role::kFused, att), stream);
+}
+
+extern "C" int oasis_lookahead_step(
+    const oasis_shape* s, const void* q, const void* summaries, int32_t n_blk_max,
+    const int32_t* n_blk, int32_t top_k, int32_t* topk_idx, float* topk_score, float* scores,
+    const int32_t* slot_block_in, const int32_t* slot_stamp_in, int32_t* slot_block_out,
+    int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+    int32_t* plan_count,
+    int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted, const void* k_tiles,
+    const void* v_tiles, const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
+    const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out, float* lse,
+    const oasis_step_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return lookahead(s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores,
+                            slot_block_in, slot_stamp_in, slot_block_out, slot_stamp_out, step, cap,
+                            pred_row, ins_blk, plan_count, plan_src, plan_dst, plan_evicted,
+                            k_tiles, v_tiles, tile_table, n_sel, unit_stride, tail_tile, tail_len,
+                            scale, out, lse, opts, workspace, workspace_bytes, stream, nullptr);
+}
+
+extern "C" int oasis_lookahead_step_append(
+    const oasis_shape* s, const void* q, void* summaries, int32_t n_blk_max,
+    const int32_t* n_blk, int32_t top_k, int32_t* topk_idx, float* topk_score, float* scores,
+    const int32_t* slot_block_in, const int32_t* slot_stamp_in, int32_t* slot_block_out,
+    int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+    int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted,
+    void* k_tiles, void* v_tiles, const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
+    const void* k_new, const void* v_new, const int32_t* pos, float scale, void* out, float* lse,
+    const oasis_step_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!k_new || !v_new || !pos || unit_stride != n_blk_max) return OASIS_EINVAL;
+    const NewToken tok{k_new, v_new, pos};
+    return lookahead(s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores,
+                            slot_block_in, slot_stamp_in, slot_block_out, slot_stamp_out, step, cap,
+                            pred_row, ins_blk, plan_count, plan_src, plan_dst, plan_evicted,
+                            k_tiles, v_tiles, tile_table, n_sel, unit_stride, nullptr, nullptr,
+                            scale, out, lse, opts, workspace, workspace_bytes, stream, &tok);
 }

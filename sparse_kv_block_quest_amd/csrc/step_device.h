@@ -99,6 +99,15 @@ struct StepArgs {
     float* part_acc;  // [U][S][NR][D]
     // roles enabled in this launch: items per unit (0 = role off)
     int scan_items, attn_items;
+    // new token per request (launches instantiated with TOK only): its K row
+    // and V column land in tile pos/B (a full-cache store), it is attended
+    // from these inputs, and a block it completes gets its summary
+    const uint8_t* k_new;  // [R][H][D]
+    const uint8_t* v_new;  // [R][H][D]
+    const int32_t* pos;    // [R], < 0 = none
+    uint8_t* kt_w;         // writable views of kt, vt and summ
+    uint8_t* vt_w;
+    uint8_t* summ_w;
 };
 
 // ------------------------------------------------------------ utilities
@@ -793,12 +802,23 @@ struct SplitRange {
     int e0, e1, tail_tile, tail_len;
 };
 
+template <bool TOK = false>
 __device__ __forceinline__ SplitRange split_range(const StepArgs& a, int u, int sp) {
     SplitRange s;
     s.e0 = min(sp * a.per_split, a.n_sel);
     s.e1 = min(s.e0 + a.per_split, a.n_sel);
     s.tail_tile = -1;
     s.tail_len = 0;
+    if constexpr (TOK) {  // the tokens of the active block before the new one
+        if (sp == a.S - 1) {
+            const int p = a.pos[u / a.H];
+            if (p >= 0 && p % a.B > 0) {
+                s.tail_tile = p / a.B;
+                s.tail_len = p % a.B;
+            }
+        }
+        return s;
+    }
     if (sp == a.S - 1 && a.tail_tile && a.tail_len) {
         const int r = u / a.H;
         const int tt = a.tail_tile[u];
@@ -845,7 +865,7 @@ struct AttnFin {
 // 16 tokens) hit 16 distinct bank groups.
 // The 4 waves take sub-tiles round robin and keep their next two sub-tiles in
 // flight in registers while the current one is computed.  P is rounded to bf16.
-template <int D, int NRG>
+template <int D, int NRG, bool TOK>
 __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
                                int* tbl) {
     constexpr int KB = D / 32;
@@ -876,7 +896,7 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
     }
     // The unit's tile table goes to LDS while the q loads above are in
     // flight (one round trip for both before the first tile load).
-    const SplitRange sr = split_range(a, u, sp);
+    const SplitRange sr = split_range<TOK>(a, u, sp);
     for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
         tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
     __syncthreads();
@@ -1089,7 +1109,7 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
 
 // VALU split (any dtype and block size): 16-token sub-tiles of K and V staged
 // in LDS as fp32, scalar FMAs.
-template <int DT, int D>
+template <int DT, int D, bool TOK>
 __device__ void attn_item_valu(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
                                const int* tbl) {
     constexpr int ST = 16;
@@ -1119,7 +1139,7 @@ __device__ void attn_item_valu(const StepArgs& a, int u, int sp, LdsCursor& cur,
 #pragma unroll
     for (int k = 0; k < OPT; ++k) acc[k] = 0.f;
     __syncthreads();
-    const SplitRange sr = split_range(a, u, sp);
+    const SplitRange sr = split_range<TOK>(a, u, sp);
     const int sub_tokens = B < ST ? B : ST;
     const int spe = B / sub_tokens;
     const int n_entry_sub = (sr.e1 - sr.e0) * spe;
@@ -1267,7 +1287,109 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr) 
     }
 }
 
-template <int DT, int D, int ATT, int NRG>
+// The new token of unit u's request joins the item's final state: one more
+// key for every row (an online-softmax step in the log2 domain: z = scale *
+// log2(e) * q.k), then its K row and V column go into the active tile, and a
+// block it completes gets its summary (min / max over the B-1 stored rows and
+// the token, as oasis_append_kv computes it; the scan of this launch does not
+// read it, the block being the active one).  Wave w owns rows w, w+4, ...;
+// every load of the tile in the loop happened before.  All loads go out first
+// (one round trip); the state update touches LDS only, so an LDS barrier
+// orders it before the output, and the stores are left in flight (a full
+// barrier would wait for them).
+template <int DT, int D>
+__device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
+    using E = typename Elem<DT>::type;
+    constexpr int PL = (D + 63) / 64;  // dims per lane
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int p = a.pos[r];
+    if (p < 0) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const size_t kn = (size_t)u * D;
+    constexpr int RW = kMaxRows / (kNT / 64);  // rows per wave at most
+    const int b = p / a.B, t = p - (p / a.B) * a.B;
+    const size_t tile = ((size_t)u * a.unit_stride + b) * (size_t)a.tile_stride;
+    // completed block: thread d < D reads column d of the stored rows
+    const bool summ = t == a.B - 1 && threadIdx.x < D;
+    float sx[16];
+    if (summ && a.B <= 17) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+            sx[k] = k < a.B - 1 ? load_elem<DT>(a.kt, tile + (size_t)k * D + threadIdx.x) : 0.f;
+    }
+    float kx[PL], vx[PL], qx[RW][PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+        const int d = lane + 64 * i;
+        kx[i] = d < D ? load_elem<DT>(a.k_new, kn + d) : 0.f;
+        vx[i] = d < D ? load_elem<DT>(a.v_new, kn + d) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+        const int row = w + k * (kNT / 64);
+        const int j = row / a.G, hh = row - (row / a.G) * a.G;
+        const size_t qo = (((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh) * D;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            qx[k][i] = (row < a.NR && d < D) ? load_elem<DT>(a.q, qo + d) : 0.f;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < RW; ++k) {
+        const int row = w + k * (kNT / 64);
+        if (row >= a.NR) break;
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < PL; ++i) part = fmaf(qx[k][i], kx[i], part);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
+        const float z = part * a.scale_log2;
+        const float mo = F.m[row], lo = F.l[row];
+        const float M = fmaxf(mo, z);
+        const float cf = (mo == -__builtin_inff()) ? 0.f : exp2f(mo - M);
+        const float pz = exp2f(z - M);
+#pragma unroll
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            if (d < D) F.acc[(size_t)row * D + d] = fmaf(F.acc[(size_t)row * D + d], cf, pz * vx[i]);
+        }
+        if (lane == 0) {
+            F.m[row] = M;
+            F.l[row] = fmaf(lo, cf, pz);
+        }
+    }
+    lds_barrier();
+    for (int d = threadIdx.x; d < D; d += kNT) {
+        reinterpret_cast<E*>(a.kt_w)[tile + (size_t)t * D + d] =
+            reinterpret_cast<const E*>(a.k_new)[kn + d];
+        reinterpret_cast<E*>(a.vt_w)[tile + (size_t)d * a.B + t] =
+            reinterpret_cast<const E*>(a.v_new)[kn + d];
+    }
+    if (summ) {
+        const int d = threadIdx.x;
+        float lo = load_elem<DT>(a.k_new, kn + d), hi = lo;
+        if (a.B <= 17) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                if (k < a.B - 1) {
+                    lo = fminf(lo, sx[k]);
+                    hi = fmaxf(hi, sx[k]);
+                }
+        } else {
+            for (int j = 0; j < a.B - 1; ++j) {
+                const float x = load_elem<DT>(a.kt, tile + (size_t)j * D + d);
+                lo = fminf(lo, x);
+                hi = fmaxf(hi, x);
+            }
+        }
+        const size_t so = ((size_t)u * a.n_blk_max + b) * 2 * D + d;
+        store_elem<DT>(a.summ_w, so, lo);
+        store_elem<DT>(a.summ_w, so + D, hi);
+    }
+}
+
+template <int DT, int D, int ATT, int NRG, bool TOK>
 __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) {
     LdsCursor cur{lds};
     int* tbl = cur.take<int>(a.per_split > 0 ? a.per_split : 1);
@@ -1276,13 +1398,16 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) 
     F.l = cur.take<float>(a.NR);
     F.acc = cur.take<float>((size_t)a.NR * D);
     if constexpr (ATT == kAttnMfma) {
-        attn_item_mfma<D, NRG>(a, u, sp, cur, F, tbl);  // stages the table after loading q
+        attn_item_mfma<D, NRG, TOK>(a, u, sp, cur, F, tbl);  // stages the table after loading q
     } else {
-        const SplitRange sr = split_range(a, u, sp);
+        const SplitRange sr = split_range<TOK>(a, u, sp);
         for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
             tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
         __syncthreads();
-        attn_item_valu<DT, D>(a, u, sp, cur, F, tbl);
+        attn_item_valu<DT, D, TOK>(a, u, sp, cur, F, tbl);
+    }
+    if constexpr (TOK) {
+        if (sp == a.S - 1) attn_new_token<DT, D>(a, u, F);
     }
     attn_emit<DT, D>(a, u, sp, F);
 }
@@ -1291,7 +1416,7 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) 
 // Main launch.  Roles present are fixed at compile time (SCAN, ATT !=
 // kAttnNone); the number of items per unit of each role comes from the
 // arguments.
-template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN>
+template <int DT, int D, int NQ, int ATT, int NRG, bool SCAN, bool TOK = false>
 __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG == 1 ? 2 : 1))) step_kernel(StepArgs a) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int w = blockIdx.x;
@@ -1310,7 +1435,7 @@ __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG ==
     if constexpr (ATT != kAttnNone) {
         if (k < nu * a.attn_items) {
             const int i = k / a.attn_items, s = k - (k / a.attn_items) * a.attn_items;
-            attn_item<DT, D, ATT, NRG>(a, x + 8 * i, s, lds);
+            attn_item<DT, D, ATT, NRG, TOK>(a, x + 8 * i, s, lds);
         }
     }
 }

@@ -161,10 +161,16 @@ append_kv_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
     const size_t tile = ((size_t)u * n_blk_max + b) * (size_t)stride;
     if (summ && t == B - 1) {
         float lo = load_elem<DT>(&kx, 0), hi = lo;
-        for (int j = 0; j < B - 1; ++j) {  // rows written by earlier launches
-            const float x = load_elem<DT>(kt, tile + (size_t)j * D + d);
-            lo = fminf(lo, x);
-            hi = fmaxf(hi, x);
+        for (int j0 = 0; j0 < B - 1; j0 += 16) {  // rows written by earlier launches:
+            float x[16];                            // 16 loads in flight, then reduce
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                x[k] = j0 + k < B - 1 ? load_elem<DT>(kt, tile + (size_t)(j0 + k) * D + d) : lo;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                lo = fminf(lo, x[k]);
+                hi = fmaxf(hi, x[k]);
+            }
         }
         reinterpret_cast<E*>(kt)[tile + (size_t)t * D + d] = kx;
         reinterpret_cast<E*>(vt)[tile + (size_t)d * B + t] = vx;

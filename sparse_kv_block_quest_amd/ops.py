@@ -579,20 +579,29 @@ class PreparedStep:
     the kernel."""
 
     _Q, _STEP, _BI, _SI, _BO, _SO, _INS, _TBL = 1, 13, 9, 10, 11, 12, 16, 23
+    _KNEW, _VNEW, _POS = 26, 27, 28  # oasis_lookahead_step_append only
 
-    def __init__(self, args, res, lib):
+    def __init__(self, args, res, lib, append=False):
         self.args = args
         self.res = res
-        self._fn = lib.oasis_lookahead_step
+        self.append = append
+        self._name = "oasis_lookahead_step_append" if append else "oasis_lookahead_step"
+        self._fn = getattr(lib, self._name)
 
-    def __call__(self, step: int, q: torch.Tensor | None = None) -> dict:
+    def __call__(self, step: int, q: torch.Tensor | None = None, token=None) -> dict:
+        """token: (k_new, v_new, pos) of this step (append form only)."""
         a = self.args
         a[self._STEP] = int(step)
         if q is not None:
             a[self._Q] = ctypes.c_void_p(q.data_ptr())
+        if token is not None:
+            if not self.append:
+                raise ValueError("this step was prepared without a new token")
+            for i, t in zip((self._KNEW, self._VNEW, self._POS), token):
+                a[i] = ctypes.c_void_p(t.data_ptr())
         st = self._fn(*a)
         if st != 0:
-            check("oasis_lookahead_step", st)
+            check(self._name, st)
         return self.res
 
 
@@ -612,8 +621,13 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                    tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
                    scale: float = 0.0, want_scores: bool = False, want_lse: bool = True,
                    want_evicted: bool = True, opts: OasisStepOpts | None = None,
-                   bufs: dict | None = None, stream=None) -> PreparedStep:
+                   bufs: dict | None = None, stream=None, new_token=None) -> PreparedStep:
     """One fused layer-step (attention over ``tile_table`` + scan, top-K and plan).
+
+    new_token: (k_new [R][H][D], v_new [R][H][D], pos [R] int32) appends one
+    token per request in the same launch (oasis_lookahead_step_append): the
+    full cache is the store (unit_stride = n_blk_max), the active block comes
+    from pos, so tail_tile / tail_len must be None.
 
     q [R][n_q][Hq][D]; summaries [R][H][n_blk_max][2][D]; slot tables [R][H][top_k]
     (the ``*_out`` pair must not overlap ``tile_table``); tiles and table as in
@@ -680,6 +694,19 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             _i32(t, n)
     if ins_blk is not None and ins_blk.shape != (R,):
         raise ValueError("ins_blk must be [R]")
+    if new_token is not None:
+        if tail_tile is not None or tail_len is not None:
+            raise ValueError("with new_token the active block comes from pos")
+        k_new, v_new, pos = new_token
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            if t.shape != (R, H, D) or t.dtype != q.dtype:
+                raise ValueError(f"{n} must be [R][H][D] of q's dtype")
+        _i32(pos, "pos")
+        if pos.shape != (R,):
+            raise ValueError("pos must be [R]")
+        tail = [_ptr(k_new), _ptr(v_new), _ptr(pos)]
+    else:
+        tail = [_ptr(tail_tile), _ptr(tail_len)]
     args = [ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk), K,
             _ptr(res["topk_idx"]), _ptr(res["topk_score"]), _ptr(res["scores"]),
             _ptr(slot_block), _ptr(slot_stamp), _ptr(slot_block_out), _ptr(slot_stamp_out),
@@ -687,12 +714,12 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             _ptr(res["plan_src"]),
             _ptr(res["plan_dst"]), _ptr(res["plan_evicted"]), ctypes.c_void_p(kptr),
             ctypes.c_void_p(vptr),
-            _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile), _ptr(tail_len),
+            _ptr(tile_table), n_sel, int(unit_stride), *tail,
             float(scale), _ptr(res["out"]), _ptr(res["lse"]),
             ctypes.byref(opts) if opts is not None else None, _ptr(ws), ws.numel(),
             _stream(stream)]
-    call = PreparedStep(args, res, lib)
+    call = PreparedStep(args, res, lib, append=new_token is not None)
     call._keep = (shp, opts, q, summaries, slot_block, slot_stamp, slot_block_out,
                   slot_stamp_out, k_tiles, v_tiles, tile_table, n_blk, tail_tile, tail_len, ins_blk,
-                  ws)
+                  ws, new_token)
     return call

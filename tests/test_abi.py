@@ -239,3 +239,19 @@ def test_host_tier_submit_validation(lib):
         assert lib.oasis_host_tier_set_workers(None, 2) == E
     finally:
         lib.oasis_host_tier_destroy(t)
+
+
+def test_lookahead_step_append_validation(lib):
+    """The append form needs the new token and the full-cache store."""
+    s = _shape()
+    E = _lib.OASIS_EINVAL
+    head = [ctypes.byref(s), FAKE, FAKE, 64, None, 4, FAKE, None, None,
+            FAKE, FAKE, FAKE, FAKE, 1, 2, 1, None, FAKE, FAKE, FAKE, None,
+            FAKE, FAKE, FAKE, 4]
+    tail = [0.0, FAKE, None, None, None, 0, None]
+    # unit_stride other than n_blk_max
+    assert lib.oasis_lookahead_step_append(*head, 4, FAKE, FAKE, FAKE, *tail) == E
+    # missing k_new / v_new / pos
+    assert lib.oasis_lookahead_step_append(*head, 64, None, FAKE, FAKE, *tail) == E
+    assert lib.oasis_lookahead_step_append(*head, 64, FAKE, None, FAKE, *tail) == E
+    assert lib.oasis_lookahead_step_append(*head, 64, FAKE, FAKE, None, *tail) == E

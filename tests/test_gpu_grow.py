@@ -68,6 +68,8 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
         vnew = torch.randn((R, H, D), generator=gen, device=dev).to(wl.dtype)
         if kv_write == "append":  # the library's append (summary of a completed block included)
             ops.append_kv(knew, vnew, pos.to(torch.int32), kt, vt, B, summaries=summ)
+        elif kv_write == "fused":  # appended by the step itself (oasis_lookahead_step_append)
+            pass
         else:
             kt[ar, :, bi, ti, :] = knew
             vt[ar, :, bi, :, ti] = vnew
@@ -77,17 +79,23 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
         n_blk = act.clone()
         ins = torch.where(tail_len == B, act, torch.full_like(act, -1))
         inserted += int((ins >= 0).sum())
-        if kv_write != "append":  # summaries of blocks that became full since the last build
+        if kv_write == "torch":  # summaries of blocks that became full since the last build
             lo = max(int(n_blk.min()) - 1, 0)
             ops.build_summaries(kt, B, seq_len=(n_blk * B).to(torch.int32), blk_begin=lo,
                                 blk_end=int(n_blk.max()), out=summ)
         tt = act[:, None].expand(R, H).contiguous()
         qs = cur.to(wl.dtype)
         say(f"  grow step {t}: L={L.tolist()} ins={ins.tolist()}")
-        res = ops.lookahead_step(qs, summ, K, blk[a], stamp[a], blk[b], stamp[b], t + 1, wl.cap,
-                                 kt, vt, blk[a], nb, B, pred_row=1, n_blk=n_blk, ins_blk=ins,
-                                 tail_tile=tt, tail_len=tail_len, want_scores=True, opts=opts,
-                                 bufs=bufs)
+        if kv_write == "fused":
+            res = ops.lookahead_step(qs, summ, K, blk[a], stamp[a], blk[b], stamp[b], t + 1,
+                                     wl.cap, kt, vt, blk[a], nb, B, pred_row=1, n_blk=n_blk,
+                                     ins_blk=ins, want_scores=True, opts=opts, bufs=bufs,
+                                     new_token=(knew, vnew, pos.to(torch.int32)))
+        else:
+            res = ops.lookahead_step(qs, summ, K, blk[a], stamp[a], blk[b], stamp[b], t + 1,
+                                     wl.cap, kt, vt, blk[a], nb, B, pred_row=1, n_blk=n_blk,
+                                     ins_blk=ins, tail_tile=tt, tail_len=tail_len,
+                                     want_scores=True, opts=opts, bufs=bufs)
         torch.cuda.synchronize()
         check_step(wl, qs, summ, kt, vt, blk[a], stamp[a], blk[b], stamp[b], res, t + 1,
                    n_blk.cpu().numpy(), tt, tail_len, units, ins=ins)
@@ -95,8 +103,20 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
         for r in range(R):
             if int(ins[r]) >= 0:
                 assert bool((blk[b][r] == ins[r]).any(dim=1).all())
+        if kv_write == "fused":  # the token landed in its row and column
+            torch.testing.assert_close(kt[ar, :, bi, ti, :], knew, rtol=0, atol=0)
+            torch.testing.assert_close(vt[ar, :, bi, :, ti], vnew, rtol=0, atol=0)
         cur = synth.drift(cur[:, 0], wl.rho, gq)
     assert inserted > 0, "the run completed no block"
+    if kv_write == "torch":  # summaries there trail the writes by a step
+        return
+    # every complete block's summary equals the oracle's over the final keys
+    full = (L // B).cpu().numpy().astype(np.int32)
+    keys64 = np64(kt).reshape(R, H, nb * B, D)
+    ref = oracle.build_summaries(keys64, B, seq_len=full * B)
+    got = np64(summ)
+    for r in range(R):
+        np.testing.assert_array_equal(got[r, :, :full[r]], ref[r, :, :full[r]])
 
 
 @pytest.mark.parametrize("case", [
@@ -104,6 +124,12 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
          kv_write="append"),
     dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[704, 719, 735], steps=18,
          opts=(2, 2, 0), kv_write="torch"),
+    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[700, 713, 725], steps=24, opts=None,
+         kv_write="fused"),
+    dict(wl=dict(R=3, H=2, Hq=8, L=1024, K=16, cap=4), L0=[704, 719, 735], steps=18,
+         opts=(2, 2, 0), kv_write="fused"),
+    dict(wl=dict(R=2, H=2, Hq=8, L=512, K=8, cap=2, dtype=torch.float32), L0=[300, 317],
+         steps=20, opts=None, kv_write="fused"),
 ])
 def test_grow_chain(cuda, case):
     wl = small("qwen3-8b-1layer", **case["wl"])

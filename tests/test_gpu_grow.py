@@ -112,11 +112,11 @@ def run_grow(cuda, wl, L0, steps, opts=None, units=None, kv_write="append"):
         return
     # every complete block's summary equals the oracle's over the final keys
     full = (L // B).cpu().numpy().astype(np.int32)
-    keys64 = np64(kt).reshape(R, H, nb * B, D)
-    ref = oracle.build_summaries(keys64, B, seq_len=full * B)
-    got = np64(summ)
-    for r in range(R):
-        np.testing.assert_array_equal(got[r, :, :full[r]], ref[r, :, :full[r]])
+    for r, g in units:
+        keys64 = np64(kt[r:r + 1, g:g + 1]).reshape(1, 1, nb * B, D)
+        ref = oracle.build_summaries(keys64, B, seq_len=full[r:r + 1] * B)
+        got = np64(summ[r, g, :full[r]])
+        np.testing.assert_array_equal(got, ref[0, 0, :full[r]])
 
 
 @pytest.mark.parametrize("case", [
@@ -136,6 +136,16 @@ def test_grow_chain(cuda, case):
     say(f"growing contexts {case}")
     o = None if case["opts"] is None else ops.step_opts(*case["opts"])
     run_grow(cuda, wl, case["L0"], case["steps"], opts=o, kv_write=case["kv_write"])
+
+
+def test_grow_full_size(cuda):
+    """The growing-context benchmark's shape and launch configuration (batch 32,
+    32K store, K = 128, cap 16, interleaved store, automatic splits), the token
+    appended inside the fused step; sampled units checked every step."""
+    wl = synth.workload("llama3.1-8b-32layer", layers=1)
+    L0 = [wl.L - 64 + (5 * r) % wl.B for r in range(wl.R)]
+    say("growing contexts full size, fused append")
+    run_grow(cuda, wl, L0, 18, units=[(0, 0), (3, 1), (13, 5), (31, 7)], kv_write="fused")
 
 
 @pytest.mark.parametrize("dtype,D,B,interleaved", [(torch.float32, 64, 16, False),

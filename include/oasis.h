@@ -8,7 +8,9 @@
  * a per-head top-K, (4) diffs the prediction against the resident set into a
  * capped least-recently-selected transfer plan, (5) copies planned tiles from
  * pinned host memory into HBM, and (6) runs paged GQA decode attention of both
- * stacked queries over the resident tiles in one call.
+ * stacked queries over the resident tiles in one call.  Around it: the append
+ * of each decode step's token (growing contexts) and a decode-host cache of
+ * whole blocks in front of a remote KV store.
  *
  * Sources (web pages about "OasisKV: Scaling In-Decode KV Cache Beyond HBM
  * with Lookahead Sparse Prefetching"):
@@ -20,9 +22,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers are DEVICE pointers owned by the caller unless stated otherwise.
- *    The library allocates nothing, keeps no state between calls and never
- *    synchronises: every call validates its host-side arguments, enqueues its
- *    kernels on `stream` and returns.  Calls are thread-safe.
+ *    The kernel entry points allocate nothing, keep no state between calls and
+ *    never synchronise: every call validates its host-side arguments, enqueues
+ *    its kernels on `stream` and returns.  They are thread-safe.  The one
+ *    exception is the decode-host block cache (oasis_host_tier_*), a
+ *    caller-created host object with its own threads, staging and stream.
  *  - All arrays are dense and row-major in the layouts given below.
  *  - dtype (oasis_shape.dtype) applies to q, keys, values, summaries and out.
  *    Scores, lse and all accumulation are fp32.

@@ -233,85 +233,85 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
             stamp[l][1 - p], 0, wl.cap, layers[l]["keys"], layers[l]["vt"], blk[l][p], wl.n_blk,
             wl.B, pred_row=1, want_evicted=False, opts=opts, bufs=bufs) for p in range(2)]
             for l in range(n_layers)]
+    else:  # the three standalone entry points, prepared once per (layer, buffer)
+        attn = [[ops.sparse_attn(qseq[0, l], layers[l]["keys"], layers[l]["vt"], blk[l][p],
+                                 wl.n_blk, wl.B, impl=impl, out=out, lse=lse, workspace=ws_at,
+                                 prepare=True) for p in range(2)] for l in range(n_layers)]
+        scan = [ops.score_topk(qseq[0, l], layers[l]["summ"], K, out=(idx, val, None, ws_sc),
+                               opts=vopts, prepare=True) for l in range(n_layers)]
+        plans = [[ops.select_plan(idx, blk[l][p], stamp[l][p], 1, wl.cap, pred_row=1,
+                                  slot_block_out=blk[l][1 - p], slot_stamp_out=stamp[l][1 - p],
+                                  plan=plan, prepare=True) for p in range(2)]
+                 for l in range(n_layers)]
 
-    ev_attn, ev_scan, ev_plan = [], [], []
-
-    def layer_step(t, l, timed):
-        """One layer-step; `timed` (unfused breakdown pass only) brackets each
-        entry point with events.  The main timed region records no events
-        between launches: they add a gap of ~10 us per marker on this stack."""
+    def layer_step(t, l):
+        """One layer-step.  The timed region records no events between launches:
+        they add a gap of ~10 us per marker on this stack."""
         q = qseq[t, l]
-        L = layers[l]
         p = t % 2
         if fused:
             return calls[l][p](t + 1, q)["plan_count"]
-        if timed:
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s1, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record()
-        ops.sparse_attn(q, L["keys"], L["vt"], blk[l][p], wl.n_blk, wl.B, impl=impl, out=out,
-                        lse=lse, workspace=ws_at)
-        if timed:
-            a1.record()
-        ops.score_topk(q, L["summ"], K, out=(idx, val, None, ws_sc))
-        if timed:
-            s1.record()
-        ops.select_plan(idx, blk[l][p], stamp[l][p], t + 1, wl.cap, pred_row=1,
-                        slot_block_out=blk[l][1 - p], slot_stamp_out=stamp[l][1 - p], plan=plan)
-        if timed:
-            p1.record()
-            ev_attn.append((a0, a1))
-            ev_scan.append((a1, s1))
-            ev_plan.append((s1, p1))
-        return plan["plan_count"]
+        attn[l][p](q=q)
+        scan[l](q=q)
+        return plans[l][p](step=t + 1)["plan_count"]
 
     for t in range(args.warmup):
         for l in range(n_layers):
-            layer_step(t, l, False)
+            layer_step(t, l)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for t in range(args.warmup, args.warmup + args.steps):
         for l in range(n_layers):
-            layer_step(t, l, False)
+            layer_step(t, l)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = ev0.elapsed_time(ev1)
-    if not fused:
-        # Per-entry-point split of a layer-step, from a replay of the timed
-        # steps (the slot tables advance; the workload is the same).
-        for t in range(args.warmup, args.warmup + args.steps):
-            for l in range(n_layers):
-                layer_step(t, l, True)
-        torch.cuda.synchronize()
     # Churn, counted outside the timed region on the one spare step of queries.
     t = args.warmup + args.steps
     for l in range(n_layers):
-        admitted.add_(layer_step(t, l, False).sum())
+        admitted.add_(layer_step(t, l).sum())
     torch.cuda.synchronize()
     cur = (t + 1) % 2  # buffer holding the newest resident set
+    blk_at_t, stamp_at_t = blk[0][cur].clone(), stamp[0][cur].clone()
+    split = {}
+    if not fused:
+        # Per-entry-point time: each entry point alone, back to back over the
+        # timed steps' queries and layers, events only around each loop (the
+        # plan loop re-plans from the last top-K: its inputs stay valid, the
+        # slot tables no longer follow a decode).
+        def alone(name, fn):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for t in range(args.warmup, args.warmup + args.steps):
+                for l in range(n_layers):
+                    fn(t, l)
+            e1.record()
+            torch.cuda.synchronize()
+            split[name] = e0.elapsed_time(e1) * 1000.0 / (args.steps * n_layers)
+
+        alone("attn", lambda t, l: attn[l][t % 2](q=qseq[t, l]))
+        alone("scan", lambda t, l: scan[l](q=qseq[t, l]))
+        alone("plan", lambda t, l: plans[l][t % 2](step=t + 1))
     launches = 1
     if fused:
         # A fused layer-step is one launch unless units are split (then the
         # library adds a merge launch and needs a workspace).
         launches = 1 if calls[0][0].res is not None and bufs["workspace"].numel() <= 1 else 2
 
-    def avg_us(evs):
-        return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / len(evs)
-
     res = {
         "total_ms": total_ms, "wall_s": wall, "fused": fused,
         "step_us": total_ms * 1000.0 / (args.steps * n_layers) if fused else None,
         "launches": launches,
-        "attn_us": avg_us(ev_attn) if not fused else None,
-        "scan_topk_us": avg_us(ev_scan) if not fused else None,
-        "plan_us": avg_us(ev_plan) if not fused else None,
+        "attn_us": split.get("attn"),
+        "scan_topk_us": split.get("scan"),
+        "plan_us": split.get("plan"),
         "summ_ms": summ_ms,
         "admitted_per_head_step": float(admitted.item()) / (n_layers * R * H),
         "layers": layers, "qseq": qseq,
-        "blk_at_t": blk[0][cur], "stamp_at_t": stamp[0][cur],
+        "blk_at_t": blk_at_t, "stamp_at_t": stamp_at_t,
     }
     return res
 

@@ -202,15 +202,41 @@ def scored_rows(n_q: int, opts: OasisStepOpts | None) -> int:
     return 2 if (opts is not None and opts.draft_avg) else int(n_q)
 
 
+class PreparedCall:
+    """A validated entry-point call whose ctypes arguments are built once;
+    calling it re-issues the call, with named slots optionally replaced: a
+    tensor of the same shape (its pointer) or an integer.  For decode loops and
+    timing, where marshalling would cost as much as the kernel."""
+
+    def __init__(self, name: str, args: list, keep, lib, slots: dict, result=None):
+        self.args = args
+        self.result = result
+        self._keep = keep
+        self._slots = slots
+        self._name = name
+        self._fn = getattr(lib, name)
+
+    def __call__(self, **updates):
+        a = self.args
+        for k, v in updates.items():
+            a[self._slots[k]] = ctypes.c_void_p(v.data_ptr()) if isinstance(v, torch.Tensor) \
+                else int(v)
+        st = self._fn(*a)
+        if st != 0:
+            check(self._name, st)
+        return self.result
+
+
 def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                n_blk: torch.Tensor | None = None, want_scores: bool = False,
-               stream=None, out=None, opts: OasisStepOpts | None = None):
+               stream=None, out=None, opts: OasisStepOpts | None = None, prepare: bool = False):
     """q [R][n_q][Hq][D], summaries [R][H][n_blk_max][2][D].
 
     Returns (topk_idx int32, topk_score fp32, scores fp32 or None), top-K tensors
     shaped [R][n_s][H][top_k], scores [R][n_s][H][n_blk_max], n_s the scored rows
     (``scored_rows``).  ``opts`` selects the scoring variant (``step_opts``).
     ``out`` may pass preallocated (topk_idx, topk_score, scores, workspace).
+    ``prepare``: return a PreparedCall (slot ``q``) instead of running.
     """
     lib = _lib.load()
     R, n_q, Hq, D = q.shape
@@ -230,20 +256,23 @@ def score_topk(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
         ws = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
     if n_blk is not None:
         _i32(n_blk, "n_blk")
-    check("oasis_score_topk",
-          lib.oasis_score_topk(ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk),
-                               int(top_k), _ptr(idx), _ptr(val), _ptr(sc), _opts_ref(opts),
-                               _ptr(ws), ws.numel(), _stream(stream)))
+    args = [ctypes.byref(shp), _ptr(q), _ptr(summaries), nb, _ptr(n_blk), int(top_k), _ptr(idx),
+            _ptr(val), _ptr(sc), _opts_ref(opts), _ptr(ws), ws.numel(), _stream(stream)]
+    if prepare:
+        return PreparedCall("oasis_score_topk", args, (shp, opts, q, summaries, n_blk, ws), lib,
+                            {"q": 1}, (idx, val, sc))
+    check("oasis_score_topk", lib.oasis_score_topk(*args))
     return idx, val, sc
 
 
 def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: torch.Tensor,
                 step: int, cap: int, pred_row: int = 1, slot_block_out=None,
                 slot_stamp_out=None, plan=None, want_evicted: bool = True,
-                ins_blk: torch.Tensor | None = None, stream=None):
+                ins_blk: torch.Tensor | None = None, stream=None, prepare: bool = False):
     """Capped least-recently-selected plan, plus the insertion of each request's
     newly completed block (``ins_blk`` [R] int32, -1 = none).  Slot tables are
-    updated in place unless *_out tensors are given.  Returns dict of plan tensors."""
+    updated in place unless *_out tensors are given.  Returns dict of plan tensors
+    (``prepare``: a PreparedCall with slot ``step`` instead)."""
     lib = _lib.load()
     R, n_q, H, K = topk_idx.shape
     for t, n in ((topk_idx, "topk_idx"), (slot_block, "slot_block"), (slot_stamp, "slot_stamp")):
@@ -265,12 +294,15 @@ def select_plan(topk_idx: torch.Tensor, slot_block: torch.Tensor, slot_stamp: to
             "plan_evicted": (torch.empty((R, H, K), dtype=torch.int32, device=dev)
                              if want_evicted else None),
         }
-    check("oasis_select_plan",
-          lib.oasis_select_plan(R, H, n_q, int(pred_row), K, _ptr(topk_idx), _ptr(slot_block),
-                                _ptr(slot_stamp), _ptr(bo), _ptr(so), int(step), int(cap),
-                                _ptr(ins_blk), _ptr(plan["plan_count"]), _ptr(plan["plan_src"]),
-                                _ptr(plan["plan_dst"]), _ptr(plan.get("plan_evicted")),
-                                _stream(stream)))
+    args = [R, H, n_q, int(pred_row), K, _ptr(topk_idx), _ptr(slot_block), _ptr(slot_stamp),
+            _ptr(bo), _ptr(so), int(step), int(cap), _ptr(ins_blk), _ptr(plan["plan_count"]),
+            _ptr(plan["plan_src"]), _ptr(plan["plan_dst"]), _ptr(plan.get("plan_evicted")),
+            _stream(stream)]
+    if prepare:
+        return PreparedCall("oasis_select_plan", args,
+                            (topk_idx, slot_block, slot_stamp, bo, so, ins_blk), lib,
+                            {"step": 10}, plan)
+    check("oasis_select_plan", lib.oasis_select_plan(*args))
     return plan
 
 
@@ -511,9 +543,10 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
                 tile_table: torch.Tensor, unit_stride: int, block_size: int,
                 tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
                 scale: float = 0.0, want_lse: bool = True, impl: int = IMPL_AUTO,
-                out=None, lse=None, workspace=None, stream=None):
+                out=None, lse=None, workspace=None, stream=None, prepare: bool = False):
     """q [R][n_q][Hq][D]; k_tiles [..][B][D]; v_tiles [..][D][B] (dim-major);
-    tile_table [R][H][n_sel] unit-local indices (-1 = skip).  Returns (out, lse)."""
+    tile_table [R][H][n_sel] unit-local indices (-1 = skip).  Returns (out, lse)
+    (``prepare``: a PreparedCall with slot ``q`` instead)."""
     lib = _lib.load()
     R, n_q, Hq, D = q.shape
     R2, H, n_sel = tile_table.shape
@@ -541,14 +574,17 @@ def sparse_attn(q: torch.Tensor, k_tiles: torch.Tensor, v_tiles: torch.Tensor,
     for t, n in ((tail_tile, "tail_tile"), (tail_len, "tail_len")):
         if t is not None:
             _i32(t, n)
-    check("oasis_sparse_attn_impl",
-          lib.oasis_sparse_attn_impl(ctypes.byref(shp), _ptr(q), ctypes.c_void_p(kptr),
-                                     ctypes.c_void_p(vptr),
-                                     _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile),
-                                     _ptr(tail_len), float(scale), _ptr(out),
-                                     _ptr(lse if want_lse else None), _ptr(workspace),
-                                     workspace.numel(), int(impl), _stream(stream)))
-    return out, (lse if want_lse else None)
+    args = [ctypes.byref(shp), _ptr(q), ctypes.c_void_p(kptr), ctypes.c_void_p(vptr),
+            _ptr(tile_table), n_sel, int(unit_stride), _ptr(tail_tile), _ptr(tail_len),
+            float(scale), _ptr(out), _ptr(lse if want_lse else None), _ptr(workspace),
+            workspace.numel(), int(impl), _stream(stream)]
+    res = (out, (lse if want_lse else None))
+    if prepare:
+        return PreparedCall("oasis_sparse_attn_impl", args,
+                            (shp, q, k_tiles, v_tiles, tile_table, tail_tile, tail_len,
+                             workspace), lib, {"q": 1}, res)
+    check("oasis_sparse_attn_impl", lib.oasis_sparse_attn_impl(*args))
+    return res
 
 
 def step_opts(scan_chunks: int = 0, attn_splits: int = 0, impl: int = IMPL_AUTO,

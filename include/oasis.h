@@ -340,7 +340,9 @@ int oasis_host_tier_fetch(oasis_host_tier* t, int64_t step, const int32_t* plan_
  *                oasis_host_tier_wait_issued has returned for this job
  * The plan, slot table and `after` must stay unchanged until `done` is
  * issued.  Host calls that change the tier (fetch, add_generated, trim,
- * set_workers) or read it (state) wait until every submitted job is issued.
+ * set_workers) or read it (state) first wait until every submitted job is
+ * issued; before one that changes the cache, the caller also waits for the
+ * `done` of the gathers still reading it.
  * Errors: EINVAL, EUNSUPPORTED, EHIP (setting up the dispatcher); errors of
  * a dispatched job are returned by oasis_host_tier_wait_issued.
  */

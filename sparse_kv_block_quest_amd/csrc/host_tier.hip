@@ -376,6 +376,14 @@ static void dispatcher_main(oasis_host_tier* t) {
     }
 }
 
+// Host calls on the tier first let the dispatcher issue every submitted job
+// (it uses the same state); returns that jobs' sticky status.
+static int drain(oasis_host_tier* t) {
+    std::unique_lock<std::mutex> lk(t->dmu);
+    t->dissued.wait(lk, [&] { return t->issued == t->submitted; });
+    return t->async_status;
+}
+
 static void stop_dispatcher(oasis_host_tier* t) {
     if (!t->dispatcher.joinable()) return;
     {
@@ -426,6 +434,7 @@ extern "C" oasis_host_tier* oasis_host_tier_create(int32_t batch, int32_t n_kv_h
 
 extern "C" int oasis_host_tier_set_workers(oasis_host_tier* t, int32_t n_workers) {
     if (!t || n_workers < 1 || n_workers > 64) return OASIS_EINVAL;
+    (void)drain(t);
     stop_pool(t);
     init_scratch(t, n_workers);
     try {
@@ -452,6 +461,7 @@ extern "C" void oasis_host_tier_destroy(oasis_host_tier* t) {
 extern "C" int oasis_host_tier_fetch(oasis_host_tier* t, int64_t step, const int32_t* plan_count,
                                      const int32_t* plan_src, const int32_t* slot_block) {
     if (!t || !plan_count || !plan_src) return OASIS_EINVAL;
+    (void)drain(t);
     return tier_fetch(t, step, plan_count, plan_src, slot_block);
 }
 
@@ -491,13 +501,29 @@ extern "C" int oasis_host_tier_submit(oasis_host_tier* t, const oasis_shape* s,
     j.copy_stream = copy_stream;
     if (!t->dispatcher.joinable()) {  // first submit: staging, private stream, thread
         const size_t nc = (size_t)t->R * t->H * sizeof(int32_t), ns = nc * t->K;
-        if (hipGetDevice(&t->device) != hipSuccess ||
-            (!t->st_count && (hipHostMalloc((void**)&t->st_count, nc) != hipSuccess ||
-                              hipHostMalloc((void**)&t->st_src, ns) != hipSuccess ||
-                              hipHostMalloc((void**)&t->st_slots, ns) != hipSuccess)) ||
-            (!t->dstream && hipStreamCreateWithFlags(&t->dstream, hipStreamNonBlocking) !=
-                                hipSuccess)) {
+        if (hipGetDevice(&t->device) != hipSuccess) {
             (void)hipGetLastError();
+            return OASIS_EHIP;
+        }
+        if (!t->st_count) {  // all three buffers or none
+            int32_t *c = nullptr, *sr = nullptr, *sl = nullptr;
+            if (hipHostMalloc((void**)&c, nc) != hipSuccess ||
+                hipHostMalloc((void**)&sr, ns) != hipSuccess ||
+                hipHostMalloc((void**)&sl, ns) != hipSuccess) {
+                (void)hipGetLastError();
+                if (c) (void)hipHostFree(c);
+                if (sr) (void)hipHostFree(sr);
+                if (sl) (void)hipHostFree(sl);
+                return OASIS_EHIP;
+            }
+            t->st_count = c;
+            t->st_src = sr;
+            t->st_slots = sl;
+        }
+        if (!t->dstream && hipStreamCreateWithFlags(&t->dstream, hipStreamNonBlocking) !=
+                               hipSuccess) {
+            (void)hipGetLastError();
+            t->dstream = nullptr;
             return OASIS_EHIP;
         }
         try {
@@ -518,14 +544,13 @@ extern "C" int oasis_host_tier_submit(oasis_host_tier* t, const oasis_shape* s,
 
 extern "C" int oasis_host_tier_wait_issued(oasis_host_tier* t) {
     if (!t) return OASIS_EINVAL;
-    std::unique_lock<std::mutex> lk(t->dmu);
-    t->dissued.wait(lk, [&] { return t->issued == t->submitted; });
-    return t->async_status;
+    return drain(t);
 }
 
 extern "C" int oasis_host_tier_add_generated(oasis_host_tier* t, int32_t req, int32_t block,
                                              int64_t step, const int32_t* slot_block) {
     if (!t || req < 0 || req >= t->R || block < 0 || block >= t->n_blk) return OASIS_EINVAL;
+    (void)drain(t);
     TierScratch& x = t->scr[0];
     x.begin_request();
     if (slot_block)
@@ -546,6 +571,7 @@ extern "C" int oasis_host_tier_add_generated(oasis_host_tier* t, int32_t req, in
 extern "C" int oasis_host_tier_trim(oasis_host_tier* t, const int32_t* target,
                                     const int32_t* slot_block) {
     if (!t || !target) return OASIS_EINVAL;
+    (void)drain(t);
     TierScratch& x = t->scr[0];
     for (int r = 0; r < t->R; ++r) {
         x.begin_request();
@@ -573,6 +599,7 @@ extern "C" int oasis_host_tier_trim(oasis_host_tier* t, const int32_t* target,
 extern "C" int oasis_host_tier_state(const oasis_host_tier* t, int32_t* slot_block_out,
                                      int64_t* last_out, int64_t* stats_out) {
     if (!t) return OASIS_EINVAL;
+    (void)drain(const_cast<oasis_host_tier*>(t));  // the lock and wait only
     const size_t n = (size_t)t->R * t->cap_max;
     if (slot_block_out)
         for (size_t i = 0; i < n; ++i) slot_block_out[i] = t->slot_blk[i];

@@ -39,6 +39,11 @@ if ROOT not in sys.path:
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
+SHAPE_NAMES = {"llama3.1-8b-32layer": "Llama-3.1-8B/Qwen3-8B", "qwen3-8b-1layer": "Qwen3-8B",
+               "qwen3-235b-1layer": "Qwen3-235B-A22B", "qwen3-8b-pipeline": "Qwen3-8B",
+               "tiny-fp32": "tiny"}
+
+
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -116,9 +121,10 @@ def kernel_source_hash(files=FUSED_SOURCES):
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(kernel_name, src_hash):
-    """HBM bytes per launch of `kernel_name` from the committed counter summary,
-    or None when it is missing or was taken on other kernel sources."""
+def pmc_traffic(kernel_name, workload, src_hash):
+    """HBM bytes per launch of `kernel_name` on `workload` from the committed
+    counter summary, or None when it is missing or was taken on other kernel
+    sources."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
@@ -126,8 +132,8 @@ def pmc_traffic(kernel_name, src_hash):
     m = re.search(r"kernel sources sha256\[:16\]:\s*`?([0-9a-f]{16})", txt, re.I)
     if not m or m.group(1) != src_hash:
         return None
-    m = re.search(rf"^\|\s*{re.escape(kernel_name)}\s*\|\s*([0-9.]+)\s*\|\s*([0-9.]+)\s*\|"
-                  rf"\s*([0-9.]+)\s*\|", txt, re.M)
+    m = re.search(rf"^\|\s*{re.escape(kernel_name)}\s*\|\s*{re.escape(workload)}\s*\|"
+                  rf"\s*([0-9.]+)\s*\|\s*([0-9.]+)\s*\|\s*([0-9.]+)\s*\|", txt, re.M)
     if not m:
         return None
     return float(m.group(3))
@@ -846,7 +852,7 @@ def main(argv=None):
     dom = max(kern, key=lambda k: kern[k]["us"])
     achieved = kern[dom]["GBps"]
     src_hash = kernel_source_hash()
-    traffic = pmc_traffic(dom, src_hash)
+    traffic = pmc_traffic(dom, f"{wl.name} batch {wl.R}", src_hash)
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -868,8 +874,8 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16" if e == 2 else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{wl.name}: Llama-3.1-8B/Qwen3-8B attention shape, "
-                               f"{wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}",
+        "config": {"workload": f"{wl.name}: {SHAPE_NAMES.get(wl.name, 'custom')} attention "
+                               f"shape, {wl.Hq} q / {wl.H} KV heads, head_dim {wl.D}",
                    "batch": wl.R, "context": wl.L, "block": wl.B, "top_k_blocks": wl.K,
                    "budget_tokens": wl.K * wl.B, "layers": wl.layers, "cap": wl.cap,
                    "stacked_queries": 3 if args.draft_avg else wl.n_q,

@@ -71,7 +71,7 @@ static int launch_finish(const StepArgs& a, hipStream_t st) {
     if (!sel && !mrg) return OASIS_OK;
     const long long grid = 8LL * ((a.U + 7) / 8) * (sel + mrg);
     if (grid > 0x7fffffffLL) return OASIS_EUNSUPPORTED;
-    const size_t lds = sel ? finish_lds_bytes(NQ, a.K) : 256;
+    const size_t lds = finish_lds_bytes(NQ, a.K, a.n_blk_max, sel != 0);
     auto kern = finish_kernel<DT, D, NQ>;
     int rc = set_lds(reinterpret_cast<const void*>(kern), lds);
     if (rc != OASIS_OK) return rc;

@@ -48,6 +48,9 @@ constexpr int kMaxTopK = 1024;  // largest K (resident slots per KV head)
 constexpr int kMaxRows = 32;    // n_q * G rows one attention item handles
 constexpr int kScanUnroll = 8;  // block passes in flight per scan thread
 constexpr int kTopkKPT = 16;    // top-K keys per thread held in registers
+constexpr int kFinishKPT = 32;
+constexpr int kTopkGroup = 8;   // keys re-read per group beyond the register-held ones
+constexpr int kStageVec = 8;    // 16-byte score loads in flight per thread when staging  // the same in the selection launch of split units
 constexpr int kMaxSplitEntries = 1024;  // tile-table entries of one attention item
 constexpr size_t kScoreLdsMax = 65536;  // scores of a whole unit kept in LDS up to this size
 
@@ -332,12 +335,14 @@ struct TopkLds {
 // take.  The threshold ties are compacted in block order and the survivors
 // ranked by counting.  Integer work only, so the result is exact for the fp32
 // scores given.
-template <int NQ>
+// With `padded`, row j of `sc` holds key i at i + i / per (per = keys of one
+// thread): a thread's keys then start one bank apart from its neighbour's, so
+// the loads of a key by all threads at once are conflict-free.
+template <int NQ, int KPT = kTopkKPT, bool GROUPED = false>
 __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oidx, float* oscore,
-                          size_t ors, int pred_row, const TopkLds& L) {
+                          size_t ors, int pred_row, const TopkLds& L, bool padded = false) {
     constexpr int TPR = kNT / NQ;  // threads per row
     constexpr int WPR = TPR / 64;  // waves per row
-    constexpr int KPT = kTopkKPT;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int j = tid / TPR, t = tid - (tid / TPR) * TPR;  // row, thread within row
@@ -359,10 +364,25 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
     }
     const int per = (n + TPR - 1) / TPR;
     const int i0 = min(t * per, n), i1 = min(i0 + per, n);
+    // Where key i of this thread's range sits in the row; with GROUPED,
+    // out-of-range keys read entry 0 (always present), so every load is
+    // unconditional and all of them are in flight together.
+    const int pad = padded ? t : 0;
+    auto at = [&](int i) { return i < i1 ? i + pad : 0; };
     uint32_t key[KPT];
+    if constexpr (GROUPED) {
+        float f[KPT];
 #pragma unroll
-    for (int e = 0; e < KPT; ++e) key[e] = (i0 + e < i1) ? float_key(row[i0 + e]) : 0u;
-    // Visit this thread's keys in block order.
+        for (int e = 0; e < KPT; ++e) f[e] = row[at(i0 + e)];
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = (i0 + e < i1) ? float_key(f[e]) : 0u;
+    } else {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) key[e] = (i0 + e < i1) ? float_key(row[i0 + pad + e]) : 0u;
+    }
+    // Visit this thread's keys in block order; keys beyond the register-held
+    // ones are re-read (GROUPED: kTopkGroup loads in flight at a time, for the
+    // selection launch; one at a time where registers are scarce).
 #define OASIS_FOR_KEYS(BODY)                                                      \
     {                                                                             \
         _Pragma("unroll") for (int e_ = 0; e_ < KPT; ++e_) {                      \
@@ -372,8 +392,20 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
                 BODY                                                              \
             }                                                                     \
         }                                                                         \
-        for (int ii = i0 + KPT; ii < i1; ++ii) {                                  \
-            const uint32_t kk = float_key(row[ii]);                               \
+        for (int ib_ = i0 + KPT; GROUPED && ib_ < i1; ib_ += kTopkGroup) {        \
+            float f_[kTopkGroup];                                                 \
+            _Pragma("unroll") for (int e_ = 0; e_ < kTopkGroup; ++e_)             \
+                f_[e_] = row[at(ib_ + e_)];                                       \
+            _Pragma("unroll") for (int e_ = 0; e_ < kTopkGroup; ++e_) {           \
+                if (ib_ + e_ < i1) {                                              \
+                    const uint32_t kk = float_key(f_[e_]);                        \
+                    const int ii = ib_ + e_;                                      \
+                    BODY                                                          \
+                }                                                                 \
+            }                                                                     \
+        }                                                                         \
+        for (int ii = i0 + KPT; !GROUPED && ii < i1; ++ii) {                      \
+            const uint32_t kk = float_key(row[ii + pad]);                         \
             BODY                                                                  \
         }                                                                         \
     }
@@ -746,15 +778,15 @@ __device__ __forceinline__ TopkLds carve_topk(LdsCursor& cur, int NQ, int K4) {
 
 // Top-K of every row of unit u from `sc` (row stride rs), then, in the fused
 // step, the plan of the unit from row pred_row.
-template <int NQ>
+template <int NQ, int KPT = kTopkKPT, bool GROUPED = false>
 __device__ void select_unit(const StepArgs& a, int u, const float* sc, size_t rs,
-                            const TopkLds& T, const PlanLds& Pl) {
+                            const TopkLds& T, const PlanLds& Pl, bool padded = false) {
     const int r = u / a.H, g = u - (u / a.H) * a.H;
     const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
     const size_t ors = (size_t)a.H * a.K;
     const size_t ob = ((size_t)r * NQ * a.H + g) * a.K;
-    topk_rows<NQ>(sc, rs, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
-                  ors, a.do_plan ? a.pred_row : -1, T);
+    topk_rows<NQ, KPT, GROUPED>(sc, rs, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
+                  ors, a.do_plan ? a.pred_row : -1, T, padded);
     if (!a.do_plan) return;
     const size_t so = (size_t)u * a.K;
     plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
@@ -1251,36 +1283,72 @@ __device__ void attn_emit(const StepArgs& a, int u, int sp, const AttnFin& F) {
 }
 
 // LSE merge of a unit's S split partials, in split order.
+// LSE merge of the S partials of unit u, all loads issued side by side (the
+// partials come from another launch, so each round trip reaches the L2 of
+// another XCD or HBM).  (m, l) pairs lie [s][row], so thread t reads row t % NR
+// of the splits t / NR, t / NR + 256 / NR, ...: coalesced, one round trip.  The
+// per-thread maxima, then the per-thread sums of exp2(m - M) * l, are reduced
+// per row through LDS.  Each output element then sums its splits' weighted
+// accumulators, kMergeBatch splits' loads in flight at a time.
+constexpr int kMergeBatch = 8;  // splits whose partial loads a merge thread keeps in flight
+
 template <int DT, int D>
-__device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr) {
+__device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr, float* red) {
     const int tid = threadIdx.x;
-    const int NR = a.NR;
+    const int NR = a.NR, S = a.S;
+    const int nsub = kNT / NR;                // threads per row
+    const int row_t = tid % NR, sub = tid / NR;
+    const float* ml = a.part_ml + (size_t)u * S * NR * 2;
+    const float ninf = -__builtin_inff();
+    float mx = ninf;
+    if (sub < nsub)
+        for (int s = sub; s < S; s += nsub) mx = fmaxf(mx, ml[((size_t)s * NR + row_t) * 2]);
+    red[tid] = mx;
+    __syncthreads();
     if (tid < NR) {
-        float M = -__builtin_inff();
-        for (int s = 0; s < a.S; ++s)
-            M = fmaxf(M, a.part_ml[(((size_t)u * a.S + s) * NR + tid) * 2]);
-        float L = 0.f;
-        if (M != -__builtin_inff()) {
-            for (int s = 0; s < a.S; ++s) {
-                const size_t pr = ((size_t)u * a.S + s) * NR + tid;
-                const float ms = a.part_ml[pr * 2];
-                if (ms != -__builtin_inff()) L += exp2f(ms - M) * a.part_ml[pr * 2 + 1];
-            }
-        }
+        float M = ninf;
+        for (int k = 0; k < nsub; ++k) M = fmaxf(M, red[tid + k * NR]);
         Mr[tid] = M;
-        Lr[tid] = L;
-        if (a.lse) a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : -__builtin_inff();
     }
     __syncthreads();
-    for (int o = tid; o < NR * D; o += kNT) {
+    float sm = 0.f;
+    if (sub < nsub) {
+        const float M = Mr[row_t];
+        if (M != ninf)
+            for (int s = sub; s < S; s += nsub) {
+                const size_t pr = ((size_t)s * NR + row_t) * 2;
+                const float ms = ml[pr];
+                if (ms != ninf) sm += exp2f(ms - M) * ml[pr + 1];
+            }
+    }
+    red[tid] = sm;
+    __syncthreads();
+    if (tid < NR) {
+        float L = 0.f;
+        for (int k = 0; k < nsub; ++k) L += red[tid + k * NR];
+        Lr[tid] = L;
+        const float M = Mr[tid];
+        if (a.lse) a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
+    }
+    __syncthreads();  // Mr / Lr ready
+    const int nout = NR * D;
+    const float* pa = a.part_acc + (size_t)u * S * NR * D;
+    for (int o = tid; o < nout; o += kNT) {
         const int row = o / D, d = o - (o / D) * D;
         const float M = Mr[row], L = Lr[row];
         float acc = 0.f;
         if (L > 0.f) {
-            for (int s = 0; s < a.S; ++s) {
-                const size_t pr = ((size_t)u * a.S + s) * NR + row;
-                const float ms = a.part_ml[pr * 2];
-                if (ms != -__builtin_inff()) acc = fmaf(exp2f(ms - M), a.part_acc[pr * D + d], acc);
+            for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+                float m[kMergeBatch], v[kMergeBatch];
+#pragma unroll
+                for (int e = 0; e < kMergeBatch; ++e) {
+                    const bool ok = s0 + e < S;
+                    m[e] = ok ? ml[((size_t)(s0 + e) * NR + row) * 2] : ninf;
+                    v[e] = ok ? pa[(size_t)(s0 + e) * NR * D + o] : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < kMergeBatch; ++e)
+                    if (m[e] != ninf) acc = fmaf(exp2f(m[e] - M), v[e], acc);
             }
         }
         store_elem<DT>(a.out, attn_out_row(a, u, row) * D + d, L > 0.f ? acc / L : 0.f);
@@ -1443,6 +1511,15 @@ __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG ==
 // Second launch for split units: top-K (+ plan) from the global scores when
 // NC > 1 (`select` items), LSE merge of the attention partials when S > 1
 // (`merge` items).  Same XCD mapping as the main launch.
+// Scores of a split unit are staged in LDS (padded rows) for its selection
+// up to this size.
+__host__ __device__ inline bool finish_scores_in_lds(int NQ, int n_blk_max) {
+    return (size_t)NQ * n_blk_max * 4 <= kScoreLdsMax;
+}
+__host__ __device__ inline size_t finish_scores_lds(int NQ, int n_blk_max) {
+    return finish_scores_in_lds(NQ, n_blk_max) ? (size_t)NQ * (n_blk_max + kNT / NQ) : 0;
+}
+
 template <int DT, int D, int NQ>
 __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_items, int merge_items) {
     extern __shared__ __align__(16) unsigned char lds[];
@@ -1460,8 +1537,53 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
             if (a.do_plan)
                 plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
             const int r = u / a.H, g = u - (u / a.H) * a.H;
-            select_unit<NQ>(a, u, a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max,
-                            (size_t)a.H * a.n_blk_max, T, Pl);
+            const float* gsc = a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max;
+            const size_t grs = (size_t)a.H * a.n_blk_max;
+            if (finish_scores_in_lds(NQ, a.n_blk_max)) {
+                // The rows go to LDS in coalesced loads, padded for the
+                // selection's conflict-free loads of every key into registers.
+                const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
+                const int per = max(1, (n_r + kNT / NQ - 1) / (kNT / NQ));
+                const int rsp = a.n_blk_max + kNT / NQ;
+                float* lsc = cur.take<float>((size_t)NQ * rsp);
+                if ((a.n_blk_max & 3) == 0 && (reinterpret_cast<uintptr_t>(gsc) & 15) == 0) {
+                    // 16-byte loads, kStageVec of them in flight per thread
+                    const int n4 = (n_r + 3) >> 2;
+                    for (int j = 0; j < NQ; ++j) {
+                        const float4* g4 = reinterpret_cast<const float4*>(gsc + j * grs);
+                        for (int i0 = 0; i0 < n4; i0 += kStageVec * kNT) {
+                            float4 v[kStageVec];
+#pragma unroll
+                            for (int e = 0; e < kStageVec; ++e) {
+                                const int i = i0 + e * kNT + threadIdx.x;
+                                if (i < n4) v[e] = g4[i];
+                            }
+#pragma unroll
+                            for (int e = 0; e < kStageVec; ++e) {
+                                const int i = i0 + e * kNT + threadIdx.x;
+                                if (i < n4) {
+                                    const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+#pragma unroll
+                                    for (int c = 0; c < 4; ++c) {
+                                        const int b = 4 * i + c;
+                                        if (b < n_r) lsc[j * rsp + b + b / per] = f[c];
+                                    }
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    for (int j = 0; j < NQ; ++j) {
+#pragma unroll 8
+                        for (int i = threadIdx.x; i < n_r; i += kNT)
+                            lsc[j * rsp + i + i / per] = gsc[j * grs + i];
+                    }
+                }
+                __syncthreads();
+                select_unit<NQ, kFinishKPT, true>(a, u, lsc, rsp, T, Pl, true);
+            } else {
+                select_unit<NQ, kFinishKPT, true>(a, u, gsc, grs, T, Pl);
+            }
             return;
         }
         k -= nu;
@@ -1469,13 +1591,18 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
     if (merge_items && k < nu) {
         float* Mr = cur.take<float>(kMaxRows);
         float* Lr = cur.take<float>(kMaxRows);
-        attn_merge_unit<DT, D>(a, x + 8 * k, Mr, Lr);
+        float* red = cur.take<float>(kNT);
+        attn_merge_unit<DT, D>(a, x + 8 * k, Mr, Lr, red);
     }
 }
 
-__host__ __device__ inline size_t finish_lds_bytes(int NQ, int K) {
-    const size_t s = scan_lds_bytes(NQ, 0, K, 0);
-    return s > 256 ? s : 256;
+// LDS of finish_kernel: a select item's top-K and plan state (+ the unit's
+// scores when finish_scores_in_lds), a merge item's reduction buffers.
+__host__ __device__ inline size_t finish_lds_bytes(int NQ, int K, int n_blk_max, bool sel) {
+    const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4;
+    if (!sel) return m;
+    const size_t s = scan_lds_bytes(NQ, 0, K, (int)finish_scores_lds(NQ, n_blk_max));
+    return s > m ? s : m;
 }
 
 // ============================================================ host helpers

@@ -63,15 +63,18 @@ static int launch_step(const StepArgs& a, size_t lds, hipStream_t st) {
     return launch_status();
 }
 
+// Rows one attention item computes.
+static int item_rows(const StepArgs& a) { return a.RGN > 1 ? a.G : a.NR; }
+
 // Second launch of split units (see finish_kernel); nothing when no unit is split.
 template <int DT, int D, int NQ>
 static int launch_finish(const StepArgs& a, hipStream_t st) {
     const int sel = a.scan_items > 1 ? 1 : 0;
-    const int mrg = a.attn_items > 1 ? 1 : 0;
+    const int mrg = (a.attn_items > 0 && a.S > 1) ? 1 : 0;
     if (!sel && !mrg) return OASIS_OK;
-    const long long grid = 8LL * ((a.U + 7) / 8) * (sel + mrg);
+    const long long grid = 8LL * ((a.U + 7) / 8) * (sel * NQ + mrg * a.RGN);
     if (grid > 0x7fffffffLL) return OASIS_EUNSUPPORTED;
-    const size_t lds = finish_lds_bytes(NQ, a.K, a.n_blk_max, sel != 0);
+    const size_t lds = finish_lds_bytes(a.K, a.n_blk_max, sel != 0);
     auto kern = finish_kernel<DT, D, NQ>;
     int rc = set_lds(reinterpret_cast<const void*>(kern), lds);
     if (rc != OASIS_OK) return rc;
@@ -93,7 +96,7 @@ static int launch_fused(const StepArgs& a, int att, size_t lds, hipStream_t st) 
     if (a.pos) {
         if (att == kAttnMfma) {
             if constexpr (DT == OASIS_BF16) {
-                if (a.NR <= 16)
+                if (item_rows(a) <= 16)
                     return launch_both<DT, D, NQ, kAttnMfma, 1, true, true>(a, lds, st);
                 return launch_both<DT, D, NQ, kAttnMfma, 2, true, true>(a, lds, st);
             }
@@ -103,7 +106,7 @@ static int launch_fused(const StepArgs& a, int att, size_t lds, hipStream_t st) 
     }
     if (att == kAttnMfma) {
         if constexpr (DT == OASIS_BF16) {
-            if (a.NR <= 16) return launch_both<DT, D, NQ, kAttnMfma, 1, true>(a, lds, st);
+            if (item_rows(a) <= 16) return launch_both<DT, D, NQ, kAttnMfma, 1, true>(a, lds, st);
             return launch_both<DT, D, NQ, kAttnMfma, 2, true>(a, lds, st);
         }
         return OASIS_EUNSUPPORTED;
@@ -115,7 +118,7 @@ template <int DT, int D>
 static int launch_attn_only(const StepArgs& a, int att, size_t lds, hipStream_t st) {
     if (att == kAttnMfma) {
         if constexpr (DT == OASIS_BF16) {
-            if (a.NR <= 16) return launch_both<DT, D, 1, kAttnMfma, 1, false>(a, lds, st);
+            if (item_rows(a) <= 16) return launch_both<DT, D, 1, kAttnMfma, 1, false>(a, lds, st);
             return launch_both<DT, D, 1, kAttnMfma, 2, false>(a, lds, st);
         }
         return OASIS_EUNSUPPORTED;
@@ -221,6 +224,15 @@ static int pick_attn(const oasis_shape* s, int impl, int* att) {
     return OASIS_OK;
 }
 
+// Row groups of the attention: a unit with more than 16 rows (both query rows
+// of a wide GQA group) on the MFMA path runs one item per query row, G <= 16
+// rows each, instead of one item of two 16-row MFMA blocks.  Not with an
+// appended token (that item also writes the token into the store).
+static int row_groups(const oasis_shape* s, int att, bool tok) {
+    const int G = s->n_q_heads / s->n_kv_heads;
+    return (att == kAttnMfma && !tok && s->n_q > 1 && s->n_q * G > 16 && G <= 16) ? s->n_q : 1;
+}
+
 static void fill_shape(StepArgs& a, const oasis_shape* s) {
     a = StepArgs{};
     a.R = s->batch;
@@ -235,14 +247,16 @@ static void fill_shape(StepArgs& a, const oasis_shape* s) {
     a.NS = s->n_q;
     a.alpha = 1.f;
     a.pred_row = -1;
+    a.RGN = 1;
 }
 
 static void fill_attn(StepArgs& a, const oasis_shape* s, const void* q, const void* k_tiles,
                       const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
                       int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len,
-                      float scale, void* out, float* lse, const StepPlan& p, uint8_t* ws,
+                      float scale, void* out, float* lse, const StepPlan& p, int rgn, uint8_t* ws,
                       const WsLayout& L) {
     a.q = reinterpret_cast<const uint8_t*>(q);
+    a.RGN = rgn;
     a.kt = reinterpret_cast<const uint8_t*>(k_tiles);
     a.vt = reinterpret_cast<const uint8_t*>(v_tiles);
     a.table = tile_table;
@@ -257,7 +271,7 @@ static void fill_attn(StepArgs& a, const oasis_shape* s, const void* q, const vo
     a.lse = lse;
     a.S = p.S;
     a.per_split = p.per_split;
-    a.attn_items = p.S;
+    a.attn_items = p.S * rgn;
     if (p.S > 1) {
         a.part_ml = reinterpret_cast<float*>(ws + L.part_ml);
         a.part_acc = reinterpret_cast<float*>(ws + L.part_acc);
@@ -287,7 +301,7 @@ static size_t lds_for(const StepArgs& a, Role role, int att) {
     if (role != Role::kAttn)
         b = scan_lds_bytes(a.NS, a.D, a.K, a.scores_lds ? a.NS * a.n_blk_max : 0);
     if (role != Role::kScan) {
-        const size_t t = attn_lds_bytes(att, a.NR, a.D, a.per_split > 0 ? a.per_split : 1);
+        const size_t t = attn_lds_bytes(att, item_rows(a), a.D, a.per_split > 0 ? a.per_split : 1);
         b = t > b ? t : b;
     }
     return b;
@@ -339,9 +353,15 @@ extern "C" int oasis_score_topk(const oasis_shape* s, const void* q, const void*
 // ================================================================ attention
 extern "C" size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel) {
     if (attn_check(s, n_sel) != OASIS_OK) return 0;
-    const StepPlan p = plan_items(s->batch * s->n_kv_heads, 0, n_sel, s->head_dim, s->block_size,
-                                  elem_bytes(s), false, true, 0, 0);
-    return ws_layout(s, 0, false, false, true, p, s->n_q).total;
+    // the larger of the layouts with and without row groups (impl decides)
+    size_t best = 0;
+    for (int rgn : {1, row_groups(s, kAttnMfma, false)}) {
+        const StepPlan p = plan_items(s->batch * s->n_kv_heads, 0, n_sel, s->head_dim,
+                                      s->block_size, elem_bytes(s), false, true, 0, 0, rgn);
+        const size_t t = ws_layout(s, 0, false, false, true, p, s->n_q).total;
+        best = t > best ? t : best;
+    }
+    return best;
 }
 
 extern "C" int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const void* k_tiles,
@@ -356,14 +376,15 @@ extern "C" int oasis_sparse_attn_impl(const oasis_shape* s, const void* q, const
     if (n_sel > 0 && !tile_table) return OASIS_EINVAL;
     int att;
     if ((st = pick_attn(s, impl, &att)) != OASIS_OK) return st;
+    const int rgn = row_groups(s, att, false);
     const StepPlan p = plan_items(s->batch * s->n_kv_heads, 0, n_sel, s->head_dim, s->block_size,
-                                  elem_bytes(s), false, true, 0, 0);
+                                  elem_bytes(s), false, true, 0, 0, rgn);
     const WsLayout L = ws_layout(s, 0, false, false, true, p, s->n_q);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return OASIS_EWORKSPACE;
     StepArgs a;
     fill_shape(a, s);
     fill_attn(a, s, q, k_tiles, v_tiles, tile_table, n_sel, unit_stride, tail_tile, tail_len,
-              scale, out, lse, p, reinterpret_cast<uint8_t*>(workspace), L);
+              scale, out, lse, p, rgn, reinterpret_cast<uint8_t*>(workspace), L);
     return dispatch(a, s->dtype, s->head_dim, s->n_q, att, Role::kAttn,
                     lds_for(a, Role::kAttn, att), stream);
 }
@@ -409,17 +430,26 @@ static int step_check(const oasis_shape* s, int32_t n_blk_max, int32_t top_k, in
 }
 
 static StepPlan step_plan(const oasis_shape* s, int32_t n_blk_max, int32_t n_sel,
-                          const oasis_step_opts* o) {
+                          const oasis_step_opts* o, int rgn) {
     return plan_items(s->batch * s->n_kv_heads, n_blk_max, n_sel, s->head_dim, s->block_size,
-                      elem_bytes(s), true, true, o ? o->scan_chunks : 0, o ? o->attn_splits : 0);
+                      elem_bytes(s), true, true, o ? o->scan_chunks : 0, o ? o->attn_splits : 0,
+                      rgn);
 }
 
 extern "C" size_t oasis_lookahead_step_workspace(const oasis_shape* s, int32_t n_blk_max,
                                                  int32_t top_k, int32_t n_sel,
                                                  const oasis_step_opts* opts) {
     if (step_check(s, n_blk_max, top_k, n_sel, opts) != OASIS_OK) return 0;
-    return ws_layout(s, n_blk_max, true, true, true, step_plan(s, n_blk_max, n_sel, opts),
-                     scored_rows(s, opts)).total;
+    // the larger of the layouts with and without row groups (the attention
+    // path and the appended token decide)
+    size_t best = 0;
+    for (int rgn : {1, row_groups(s, kAttnMfma, false)}) {
+        const size_t t = ws_layout(s, n_blk_max, true, true, true,
+                                   step_plan(s, n_blk_max, n_sel, opts, rgn),
+                                   scored_rows(s, opts)).total;
+        best = t > best ? t : best;
+    }
+    return best;
 }
 
 // The fused layer-step; with `tok` (k_new, v_new, pos) also the append of
@@ -457,7 +487,8 @@ static int lookahead(
         return OASIS_EINVAL;
     int att;
     if ((st = pick_attn(s, opts ? opts->attn_impl : 0, &att)) != OASIS_OK) return st;
-    const StepPlan p = step_plan(s, n_blk_max, n_sel, opts);
+    const int rgn = row_groups(s, att, tok != nullptr);
+    const StepPlan p = step_plan(s, n_blk_max, n_sel, opts, rgn);
     const WsLayout L = ws_layout(s, n_blk_max, true, scores == nullptr, true, p, NS);
     if (L.total > 0 && (!workspace || workspace_bytes < L.total)) return OASIS_EWORKSPACE;
     uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
@@ -466,7 +497,7 @@ static int lookahead(
     fill_variant(a, s, opts);
     fill_scan(a, s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores, p, ws, L);
     fill_attn(a, s, q, k_tiles, v_tiles, tile_table, n_sel, unit_stride, tail_tile, tail_len, scale,
-              out, lse, p, ws, L);
+              out, lse, p, rgn, ws, L);
     a.do_plan = 1;
     a.pred_row = pred_row;
     a.step = step;

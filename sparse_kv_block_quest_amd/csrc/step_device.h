@@ -98,8 +98,9 @@ struct StepArgs {
     void* out;   // [R][NQ][Hq][D]
     float* lse;  // [R][NQ][Hq] or null
     int S, per_split;
-    float* part_ml;   // [U][S][NR][2]
-    float* part_acc;  // [U][S][NR][D]
+    int RGN;          // row groups per unit: 1, or NQ (one per query row, G rows each)
+    float* part_ml;   // [RGN][U][S][rows][2]
+    float* part_acc;  // [RGN][U][S][rows][D]
     // roles enabled in this launch: items per unit (0 = role off)
     int scan_items, attn_items;
     // new token per request (launches instantiated with TOK only): its K row
@@ -883,6 +884,19 @@ struct AttnFin {
     float* acc;  // [NR][D] unnormalised output
 };
 
+// Rows of a unit one attention item computes: [row0, row0 + nr), partials in
+// buffer group grp.  With row groups (RGN > 1, wide GQA groups) each query row
+// j is its own item of the G rows of head group g, so an item needs one
+// 16-row MFMA block and the kernel keeps two waves per SIMD; the item pair
+// of a split reads the same tiles back to back on one XCD.
+struct RowWin {
+    int row0, nr, grp;
+};
+
+__device__ __forceinline__ RowWin row_win(const StepArgs& a, int grp) {
+    return a.RGN > 1 ? RowWin{grp * a.G, a.G, grp} : RowWin{0, a.NR, 0};
+}
+
 // MFMA split (bf16, B % 16 == 0).  Per 16-token sub-tile:
 //   S^T[16 tok][16 rows] = K_sub[16][D] * Q^T  (v_mfma_f32_16x16x32_bf16, q in
 //   registers),
@@ -898,14 +912,14 @@ struct AttnFin {
 // The 4 waves take sub-tiles round robin and keep their next two sub-tiles in
 // flight in registers while the current one is computed.  P is rounded to bf16.
 template <int D, int NRG, bool TOK>
-__device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur, const AttnFin& F,
-                               int* tbl) {
+__device__ void attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& win, LdsCursor& cur,
+                               const AttnFin& F, int* tbl) {
     constexpr int KB = D / 32;
     constexpr int DB = D / 16;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, lg = lane >> 4;
     const int r = u / a.H, g = u - (u / a.H) * a.H;
-    const int NR = a.NR, B = a.B;
+    const int NR = win.nr, B = a.B;
     constexpr int CPR = D * 2 / 16;  // 16-byte chunks per K row (KB loads of 1 KiB per sub-tile)
     float* lm = cur.take<float>(3 * NR);
     float* ll = cur.take<float>(3 * NR);
@@ -919,7 +933,8 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, LdsCursor& cur,
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) qv[rg][kb] = bf16x8_t{0, 0, 0, 0, 0, 0, 0, 0};
         if (row < NR) {
-            const int j = row / a.G, hh = row - (row / a.G) * a.G;
+            const int grow = win.row0 + row;
+            const int j = grow / a.G, hh = grow - (grow / a.G) * a.G;
             const bf16x8_t* qp = reinterpret_cast<const bf16x8_t*>(
                 a.q + ((((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh) * D) * 2);
 #pragma unroll
@@ -1259,22 +1274,24 @@ __device__ __forceinline__ size_t attn_out_row(const StepArgs& a, int u, int row
 // Output of an attention item: normalised outputs when the unit has one
 // split, else the split's partial (max, sum, acc) for finish_kernel.
 template <int DT, int D>
-__device__ void attn_emit(const StepArgs& a, int u, int sp, const AttnFin& F) {
+__device__ void attn_emit(const StepArgs& a, int u, int sp, const RowWin& win, const AttnFin& F) {
     const int tid = threadIdx.x;
-    const int NR = a.NR;
+    const int NR = win.nr;
     if (a.S == 1) {
         for (int o = tid; o < NR * D; o += kNT) {
             const int row = o / D, d = o - (o / D) * D;
             const float L = F.l[row];
-            store_elem<DT>(a.out, attn_out_row(a, u, row) * D + d, L > 0.f ? F.acc[o] / L : 0.f);
+            store_elem<DT>(a.out, attn_out_row(a, u, win.row0 + row) * D + d,
+                           L > 0.f ? F.acc[o] / L : 0.f);
         }
         if (a.lse && tid < NR) {
             const float L = F.l[tid];
-            a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (F.m[tid] + log2f(L)) * kLn2 : -__builtin_inff();
+            a.lse[attn_out_row(a, u, win.row0 + tid)] =
+                L > 0.f ? (F.m[tid] + log2f(L)) * kLn2 : -__builtin_inff();
         }
         return;
     }
-    const size_t pb = ((size_t)u * a.S + sp) * NR;
+    const size_t pb = (((size_t)win.grp * a.U + u) * a.S + sp) * NR;
     for (int o = tid; o < NR * D; o += kNT) a.part_acc[pb * D + o] = F.acc[o];
     if (tid < NR) {
         a.part_ml[(pb + tid) * 2 + 0] = F.m[tid];
@@ -1293,12 +1310,14 @@ __device__ void attn_emit(const StepArgs& a, int u, int sp, const AttnFin& F) {
 constexpr int kMergeBatch = 8;  // splits whose partial loads a merge thread keeps in flight
 
 template <int DT, int D>
-__device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr, float* red) {
+__device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, float* Mr, float* Lr,
+                                float* red) {
     const int tid = threadIdx.x;
-    const int NR = a.NR, S = a.S;
+    const int NR = win.nr, S = a.S;
     const int nsub = kNT / NR;                // threads per row
     const int row_t = tid % NR, sub = tid / NR;
-    const float* ml = a.part_ml + (size_t)u * S * NR * 2;
+    const size_t ub = (size_t)win.grp * a.U + u;  // this item's partials: [S][NR]
+    const float* ml = a.part_ml + ub * S * NR * 2;
     const float ninf = -__builtin_inff();
     float mx = ninf;
     if (sub < nsub)
@@ -1328,11 +1347,11 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr, 
         for (int k = 0; k < nsub; ++k) L += red[tid + k * NR];
         Lr[tid] = L;
         const float M = Mr[tid];
-        if (a.lse) a.lse[attn_out_row(a, u, tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
+        if (a.lse) a.lse[attn_out_row(a, u, win.row0 + tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
     }
     __syncthreads();  // Mr / Lr ready
     const int nout = NR * D;
-    const float* pa = a.part_acc + (size_t)u * S * NR * D;
+    const float* pa = a.part_acc + ub * S * NR * D;
     for (int o = tid; o < nout; o += kNT) {
         const int row = o / D, d = o - (o / D) * D;
         const float M = Mr[row], L = Lr[row];
@@ -1351,7 +1370,7 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, float* Mr, float* Lr, 
                     if (m[e] != ninf) acc = fmaf(exp2f(m[e] - M), v[e], acc);
             }
         }
-        store_elem<DT>(a.out, attn_out_row(a, u, row) * D + d, L > 0.f ? acc / L : 0.f);
+        store_elem<DT>(a.out, attn_out_row(a, u, win.row0 + row) * D + d, L > 0.f ? acc / L : 0.f);
     }
 }
 
@@ -1458,15 +1477,16 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
 }
 
 template <int DT, int D, int ATT, int NRG, bool TOK>
-__device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) {
+__device__ void attn_item(const StepArgs& a, int u, int sp, int grp, unsigned char* lds) {
     LdsCursor cur{lds};
+    const RowWin win = row_win(a, grp);
     int* tbl = cur.take<int>(a.per_split > 0 ? a.per_split : 1);
-    AttnFin F;
-    F.m = cur.take<float>(a.NR);
-    F.l = cur.take<float>(a.NR);
-    F.acc = cur.take<float>((size_t)a.NR * D);
+    AttnFin F;  // the item's rows (attn_lds_bytes sizes LDS for them)
+    F.m = cur.take<float>(win.nr);
+    F.l = cur.take<float>(win.nr);
+    F.acc = cur.take<float>((size_t)win.nr * D);
     if constexpr (ATT == kAttnMfma) {
-        attn_item_mfma<D, NRG, TOK>(a, u, sp, cur, F, tbl);  // stages the table after loading q
+        attn_item_mfma<D, NRG, TOK>(a, u, sp, win, cur, F, tbl);  // stages the table after loading q
     } else {
         const SplitRange sr = split_range<TOK>(a, u, sp);
         for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
@@ -1477,7 +1497,7 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, unsigned char* lds) 
     if constexpr (TOK) {
         if (sp == a.S - 1) attn_new_token<DT, D>(a, u, F);
     }
-    attn_emit<DT, D>(a, u, sp, F);
+    attn_emit<DT, D>(a, u, sp, win, F);
 }
 
 // ============================================================ the kernels
@@ -1503,7 +1523,9 @@ __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG ==
     if constexpr (ATT != kAttnNone) {
         if (k < nu * a.attn_items) {
             const int i = k / a.attn_items, s = k - (k / a.attn_items) * a.attn_items;
-            attn_item<DT, D, ATT, NRG, TOK>(a, x + 8 * i, s, lds);
+            // a split's row groups are adjacent items (same tiles, same XCD)
+            const int sp = a.RGN > 1 ? s / a.RGN : s, grp = a.RGN > 1 ? s - sp * a.RGN : 0;
+            attn_item<DT, D, ATT, NRG, TOK>(a, x + 8 * i, sp, grp, lds);
         }
     }
 }
@@ -1511,13 +1533,13 @@ __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG ==
 // Second launch for split units: top-K (+ plan) from the global scores when
 // NC > 1 (`select` items), LSE merge of the attention partials when S > 1
 // (`merge` items).  Same XCD mapping as the main launch.
-// Scores of a split unit are staged in LDS (padded rows) for its selection
-// up to this size.
-__host__ __device__ inline bool finish_scores_in_lds(int NQ, int n_blk_max) {
-    return (size_t)NQ * n_blk_max * 4 <= kScoreLdsMax;
+// A split unit's score row is staged in LDS (padded) for its selection up to
+// this size.
+__host__ __device__ inline bool finish_scores_in_lds(int n_blk_max) {
+    return (size_t)n_blk_max * 4 <= kScoreLdsMax;
 }
-__host__ __device__ inline size_t finish_scores_lds(int NQ, int n_blk_max) {
-    return finish_scores_in_lds(NQ, n_blk_max) ? (size_t)NQ * (n_blk_max + kNT / NQ) : 0;
+__host__ __device__ inline size_t finish_scores_lds(int n_blk_max) {
+    return finish_scores_in_lds(n_blk_max) ? (size_t)n_blk_max + kNT : 0;
 }
 
 template <int DT, int D, int NQ>
@@ -1529,79 +1551,88 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
     const int nu = a.U > x ? (a.U - x + 7) / 8 : 0;
     LdsCursor cur{lds};
     if (select_items) {
-        if (k < nu) {
-            const int u = x + 8 * k;
+        // One item per (unit, scored row): the row's 256 threads hold its keys;
+        // the item of row pred_row also plans the unit.
+        if (k < nu * NQ) {
+            const int u = x + 8 * (k / NQ), j = k - (k / NQ) * NQ;
             const int K4 = pad4(a.K);
-            const TopkLds T = carve_topk(cur, NQ, K4);
+            const TopkLds T = carve_topk(cur, 1, K4);
             const PlanLds Pl = carve_plan(cur, K4);
-            if (a.do_plan)
+            const bool plan = a.do_plan && j == a.pred_row;
+            if (plan)
                 plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
             const int r = u / a.H, g = u - (u / a.H) * a.H;
-            const float* gsc = a.scores + ((size_t)r * NQ * a.H + g) * a.n_blk_max;
-            const size_t grs = (size_t)a.H * a.n_blk_max;
-            if (finish_scores_in_lds(NQ, a.n_blk_max)) {
-                // The rows go to LDS in coalesced loads, padded for the
+            const float* gsc = a.scores + (((size_t)r * NQ + j) * a.H + g) * a.n_blk_max;
+            const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
+            const float* sc = gsc;
+            bool padded = false;
+            if (finish_scores_in_lds(a.n_blk_max)) {
+                // The row goes to LDS in coalesced loads, padded for the
                 // selection's conflict-free loads of every key into registers.
-                const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
-                const int per = max(1, (n_r + kNT / NQ - 1) / (kNT / NQ));
-                const int rsp = a.n_blk_max + kNT / NQ;
-                float* lsc = cur.take<float>((size_t)NQ * rsp);
+                const int per = max(1, (n_r + kNT - 1) / kNT);
+                float* lsc = cur.take<float>((size_t)a.n_blk_max + kNT);
                 if ((a.n_blk_max & 3) == 0 && (reinterpret_cast<uintptr_t>(gsc) & 15) == 0) {
                     // 16-byte loads, kStageVec of them in flight per thread
                     const int n4 = (n_r + 3) >> 2;
-                    for (int j = 0; j < NQ; ++j) {
-                        const float4* g4 = reinterpret_cast<const float4*>(gsc + j * grs);
-                        for (int i0 = 0; i0 < n4; i0 += kStageVec * kNT) {
-                            float4 v[kStageVec];
+                    const float4* g4 = reinterpret_cast<const float4*>(gsc);
+                    for (int i0 = 0; i0 < n4; i0 += kStageVec * kNT) {
+                        float4 v[kStageVec];
 #pragma unroll
-                            for (int e = 0; e < kStageVec; ++e) {
-                                const int i = i0 + e * kNT + threadIdx.x;
-                                if (i < n4) v[e] = g4[i];
-                            }
+                        for (int e = 0; e < kStageVec; ++e) {
+                            const int i = i0 + e * kNT + threadIdx.x;
+                            if (i < n4) v[e] = g4[i];
+                        }
 #pragma unroll
-                            for (int e = 0; e < kStageVec; ++e) {
-                                const int i = i0 + e * kNT + threadIdx.x;
-                                if (i < n4) {
-                                    const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+                        for (int e = 0; e < kStageVec; ++e) {
+                            const int i = i0 + e * kNT + threadIdx.x;
+                            if (i < n4) {
+                                const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
 #pragma unroll
-                                    for (int c = 0; c < 4; ++c) {
-                                        const int b = 4 * i + c;
-                                        if (b < n_r) lsc[j * rsp + b + b / per] = f[c];
-                                    }
+                                for (int c = 0; c < 4; ++c) {
+                                    const int bb = 4 * i + c;
+                                    if (bb < n_r) lsc[bb + bb / per] = f[c];
                                 }
                             }
                         }
                     }
                 } else {
-                    for (int j = 0; j < NQ; ++j) {
 #pragma unroll 8
-                        for (int i = threadIdx.x; i < n_r; i += kNT)
-                            lsc[j * rsp + i + i / per] = gsc[j * grs + i];
-                    }
+                    for (int i = threadIdx.x; i < n_r; i += kNT) lsc[i + i / per] = gsc[i];
                 }
                 __syncthreads();
-                select_unit<NQ, kFinishKPT, true>(a, u, lsc, rsp, T, Pl, true);
-            } else {
-                select_unit<NQ, kFinishKPT, true>(a, u, gsc, grs, T, Pl);
+                sc = lsc;
+                padded = true;
+            }
+            const size_t ors = (size_t)a.H * a.K;
+            const size_t ob = (((size_t)r * NQ + j) * a.H + g) * a.K;
+            topk_rows<1, kFinishKPT, true>(sc, 0, n_r, a.K, a.topk_idx + ob,
+                                           a.topk_score ? a.topk_score + ob : nullptr, ors,
+                                           plan ? 0 : -1, T, padded);
+            if (plan) {
+                const size_t so = (size_t)u * a.K;
+                plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
+                          a.ins_blk ? a.ins_blk[r] : -1, a.plan_count + u, a.plan_src + so,
+                          a.plan_dst + so, a.plan_evicted ? a.plan_evicted + so : nullptr, Pl);
             }
             return;
         }
-        k -= nu;
+        k -= nu * NQ;
     }
-    if (merge_items && k < nu) {
+    if (merge_items && k < nu * a.RGN) {
         float* Mr = cur.take<float>(kMaxRows);
         float* Lr = cur.take<float>(kMaxRows);
         float* red = cur.take<float>(kNT);
-        attn_merge_unit<DT, D>(a, x + 8 * k, Mr, Lr, red);
+        const int i = k / a.RGN, grp = k - (k / a.RGN) * a.RGN;
+        attn_merge_unit<DT, D>(a, x + 8 * i, row_win(a, grp), Mr, Lr, red);
     }
 }
 
-// LDS of finish_kernel: a select item's top-K and plan state (+ the unit's
-// scores when finish_scores_in_lds), a merge item's reduction buffers.
-__host__ __device__ inline size_t finish_lds_bytes(int NQ, int K, int n_blk_max, bool sel) {
+// LDS of finish_kernel: a select item's top-K and plan state (+ its score row
+// when finish_scores_in_lds), a merge item's reduction buffers.
+__host__ __device__ inline size_t finish_lds_bytes(int K, int n_blk_max, bool sel) {
     const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4;
     if (!sel) return m;
-    const size_t s = scan_lds_bytes(NQ, 0, K, (int)finish_scores_lds(NQ, n_blk_max));
+    const size_t s = scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max));
     return s > m ? s : m;
 }
 
@@ -1616,11 +1647,12 @@ struct StepPlan {
 // sharing the items between scan and attention by their bytes, with at least
 // 64 blocks per scan item and 4 tiles per attention split; the split units
 // then take a second, small launch.
+// With rgn row groups every split is rgn items, each reading the split's tiles.
 inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb, bool scan,
-                           bool attn, int want_nc, int want_s) {
+                           bool attn, int want_nc, int want_s, int rgn = 1) {
     StepPlan p{0, 0, 0, 0};
     const double scan_b = scan ? (double)n_blk_max * 2 * D * eb : 0.0;
-    const double attn_b = attn ? (double)n_sel * 2 * B * D * eb : 0.0;
+    const double attn_b = attn ? (double)n_sel * 2 * B * D * eb * rgn : 0.0;
     const int items = U >= 256 ? (scan ? 1 : 0) + (attn ? 1 : 0) : (511 + U) / U;
     const double tot = scan_b + attn_b > 0 ? scan_b + attn_b : 1.0;
     if (scan) {
@@ -1634,7 +1666,7 @@ inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb
         p.NC = (n_blk_max + chunk - 1) / chunk;
     }
     if (attn) {
-        int s = want_s > 0 ? want_s : (U >= 256 ? 1 : (int)(items * attn_b / tot + 0.5));
+        int s = want_s > 0 ? want_s : (U >= 256 ? 1 : (int)(items * attn_b / tot / rgn + 0.5));
         if (want_s <= 0 && s > (n_sel + 3) / 4) s = (n_sel + 3) / 4;
         const int min_s = (n_sel + kMaxSplitEntries - 1) / kMaxSplitEntries;
         if (s < min_s) s = min_s;

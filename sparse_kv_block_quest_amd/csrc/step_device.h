@@ -1643,9 +1643,9 @@ struct StepPlan {
 
 // Items per unit.  With at least 256 units (one per CU) every unit gets one
 // scan item and one attention item: no partials, one launch.  Smaller batches
-// split units until about 512 main workgroups (two per CU) are in flight,
-// sharing the items between scan and attention by their bytes, with at least
-// 64 blocks per scan item and 4 tiles per attention split; the split units
+// split units until about 512 main workgroups (two per CU) are in flight:
+// the attention takes its share of the items by bytes (at least 4 tiles per
+// split), the scan the items left (at least 64 blocks each); the split units
 // then take a second, small launch.
 // With rgn row groups every split is rgn items, each reading the split's tiles.
 inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb, bool scan,
@@ -1655,16 +1655,6 @@ inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb
     const double attn_b = attn ? (double)n_sel * 2 * B * D * eb * rgn : 0.0;
     const int items = U >= 256 ? (scan ? 1 : 0) + (attn ? 1 : 0) : (511 + U) / U;
     const double tot = scan_b + attn_b > 0 ? scan_b + attn_b : 1.0;
-    if (scan) {
-        int nc = want_nc > 0 ? want_nc
-                             : (U >= 256 ? 1 : (int)(items * scan_b / tot + 0.5));
-        const int max_nc = want_nc > 0 ? n_blk_max : (n_blk_max + 63) / 64;
-        if (nc > max_nc) nc = max_nc;
-        if (nc < 1) nc = 1;
-        const int chunk = (n_blk_max + nc - 1) / nc;
-        p.chunk = chunk;
-        p.NC = (n_blk_max + chunk - 1) / chunk;
-    }
     if (attn) {
         int s = want_s > 0 ? want_s : (U >= 256 ? 1 : (int)(items * attn_b / tot / rgn + 0.5));
         if (want_s <= 0 && s > (n_sel + 3) / 4) s = (n_sel + 3) / 4;
@@ -1675,6 +1665,18 @@ inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb
         const int per = n_sel > 0 ? (n_sel + s - 1) / s : 0;
         p.per_split = per;
         p.S = per > 0 ? (n_sel + per - 1) / per : 1;
+    }
+    if (scan) {
+        // the scan takes the items the attention leaves (all items fit at once)
+        const int left = items - (attn ? p.S * rgn : 0);
+        int nc = want_nc > 0 ? want_nc
+                             : (U >= 256 ? 1 : (attn ? left : (int)(items * scan_b / tot + 0.5)));
+        const int max_nc = want_nc > 0 ? n_blk_max : (n_blk_max + 63) / 64;
+        if (nc > max_nc) nc = max_nc;
+        if (nc < 1) nc = 1;
+        const int chunk = (n_blk_max + nc - 1) / nc;
+        p.chunk = chunk;
+        p.NC = (n_blk_max + chunk - 1) / chunk;
     }
     return p;
 }

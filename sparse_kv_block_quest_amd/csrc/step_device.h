@@ -129,6 +129,34 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Wave-wide inclusive scans over the 64 lanes by DPP: row shifts by 1, 2, 4
+// and 8 lanes scan each row of 16, then the row broadcasts of lanes 15 and 31
+// carry the row totals into the following rows.  Lanes without a source keep
+// the identity.  One VALU op per step, no LDS round trip.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, uint32_t ident, Op op) {
+    const int id = (int)ident;
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xa, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+    return wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+// Minimum / maximum over the wave, the same in every lane.
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+    v = wave_incl_scan(v, 0xffffffffu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+    v = wave_incl_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Exclusive prefix sums over the workgroup of N values per thread.
 template <int N>
 __device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&excl)[N],
@@ -136,15 +164,7 @@ __device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&ex
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t inc[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) inc[i] = v[i];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const uint32_t t = __shfl_up(inc[i], off, 64);
-            if (lane >= off) inc[i] += t;
-        }
-    }
+    for (int i = 0; i < N; ++i) inc[i] = wave_incl_sum(v[i]);
     if (lane == 63) {
 #pragma unroll
         for (int i = 0; i < N; ++i) buf[w * N + i] = inc[i];
@@ -418,11 +438,8 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
         lo = kk < lo ? kk : lo;
         hi = kk > hi ? kk : hi;
     })
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t x = __shfl_xor(lo, off, 64), y = __shfl_xor(hi, off, 64);
-        lo = x < lo ? x : lo;
-        hi = y > hi ? y : hi;
-    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
     if (lane == 0) {
         L.scanbuf[wv * 2] = lo;
         L.scanbuf[wv * 2 + 1] = hi;
@@ -477,11 +494,7 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
 #pragma unroll
             for (int e = 0; e < 4; ++e) c[e] = hist[255 - (4 * lane + e)];
             const int local = c[0] + c[1] + c[2] + c[3];
-            int inc = local;
-            for (int off = 1; off < 64; off <<= 1) {
-                const int x = __shfl_up(inc, off, 64);
-                if (lane >= off) inc += x;
-            }
+            const int inc = (int)wave_incl_sum((uint32_t)local);
             int before = inc - local;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -519,14 +532,7 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
         gt += mk > prefix;
         eq += mk == prefix;
     })
-    uint32_t ig = gt, ie = eq;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t x = __shfl_up(ig, off, 64), y = __shfl_up(ie, off, 64);
-        if (lane >= off) {
-            ig += x;
-            ie += y;
-        }
-    }
+    uint32_t ig = wave_incl_sum(gt), ie = wave_incl_sum(eq);
     if (lane == 63) {
         L.scanbuf[wv * 2] = ig;
         L.scanbuf[wv * 2 + 1] = ie;

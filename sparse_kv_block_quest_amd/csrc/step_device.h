@@ -1570,7 +1570,7 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
             const int r = u / a.H, g = u - (u / a.H) * a.H;
             const float* gsc = a.scores + (((size_t)r * NQ + j) * a.H + g) * a.n_blk_max;
             const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
-            const float* sc = gsc;
+            const float* lsc_row = nullptr;
             bool padded = false;
             if (finish_scores_in_lds(a.n_blk_max)) {
                 // The row goes to LDS in coalesced loads, padded for the
@@ -1606,14 +1606,20 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
                     for (int i = threadIdx.x; i < n_r; i += kNT) lsc[i + i / per] = gsc[i];
                 }
                 __syncthreads();
-                sc = lsc;
+                lsc_row = lsc;
                 padded = true;
             }
             const size_t ors = (size_t)a.H * a.K;
             const size_t ob = (((size_t)r * NQ + j) * a.H + g) * a.K;
-            topk_rows<1, kFinishKPT, true>(sc, 0, n_r, a.K, a.topk_idx + ob,
-                                           a.topk_score ? a.topk_score + ob : nullptr, ors,
-                                           plan ? 0 : -1, T, padded);
+            // two call sites, so the staged row is read with LDS instructions
+            if (padded)
+                topk_rows<1, kFinishKPT, true>(lsc_row, 0, n_r, a.K, a.topk_idx + ob,
+                                               a.topk_score ? a.topk_score + ob : nullptr, ors,
+                                               plan ? 0 : -1, T, true);
+            else
+                topk_rows<1, kFinishKPT, true>(gsc, 0, n_r, a.K, a.topk_idx + ob,
+                                               a.topk_score ? a.topk_score + ob : nullptr, ors,
+                                               plan ? 0 : -1, T, false);
             if (plan) {
                 const size_t so = (size_t)u * a.K;
                 plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,

@@ -282,6 +282,23 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
     torch.cuda.synchronize()
     cur = (t + 1) % 2  # buffer holding the newest resident set
     blk_at_t, stamp_at_t = blk[0][cur].clone(), stamp[0][cur].clone()
+    # Spread over steps: the timed steps' queries once more, events only
+    # between steps (one marker per step of all layers).
+    spread = None
+    if fused:
+        evs = []
+        for t in range(args.warmup, args.warmup + args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for l in range(n_layers):
+                layer_step(t, l)
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1000.0 / n_layers for a, b in evs)
+        q = lambda f: per[min(len(per) - 1, int(round(f * (len(per) - 1))))]
+        spread = {"p10_us": round(q(0.1), 2), "p50_us": round(q(0.5), 2),
+                  "p90_us": round(q(0.9), 2), "steps": len(per)}
     split = {}
     if not fused:
         # Per-entry-point time: each entry point alone, back to back over the
@@ -316,7 +333,7 @@ def run_gpu(args, wl, torch, synth, ops, _lib):
         "plan_us": split.get("plan"),
         "summ_ms": summ_ms,
         "admitted_per_head_step": float(admitted.item()) / (n_layers * R * H),
-        "layers": layers, "qseq": qseq,
+        "layers": layers, "qseq": qseq, "spread": spread,
         "blk_at_t": blk_at_t, "stamp_at_t": stamp_at_t,
     }
     return res
@@ -727,6 +744,17 @@ def report_pipeline(args, wl, g):
 
 
 # ----------------------------------------------------------------- CPU leg
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def run_cpu_baseline(args, wl, g, torch, synth):
     """The oracle, as it stands, on a bounded sample of the same workload: whole
     layer-steps (scan + top-K + plan + attention) for the first few requests of
@@ -755,27 +783,36 @@ def run_cpu_baseline(args, wl, g, torch, synth):
         "blk": blk[:R_s].cpu().numpy(), "stamp": g["stamp_at_t"][:R_s].cpu().numpy(),
     }
     table = np.tile(np.arange(wl.K, dtype=np.int32), (R_s, wl.H, 1))
+    def passes(seconds):
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            sc = oracle.block_scores(inp["q"], inp["summ"],
+                                     alpha=1.0 if args.alpha is None else args.alpha,
+                                     draft_avg=args.draft_avg)
+            ti, _ = oracle.topk(sc, wl.K)
+            oracle.select_plan(ti, inp["blk"], inp["stamp"], t + 1, wl.cap, pred_row=1)
+            oracle.sparse_attn(inp["q"], inp["kt"], inp["vt"], table, wl.K)
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return done, el
+
     threads = oracle.num_threads()
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        sc = oracle.block_scores(inp["q"], inp["summ"],
-                                 alpha=1.0 if args.alpha is None else args.alpha,
-                                 draft_avg=args.draft_avg)
-        ti, _ = oracle.topk(sc, wl.K)
-        oracle.select_plan(ti, inp["blk"], inp["stamp"], t + 1, wl.cap, pred_row=1)
-        oracle.sparse_attn(inp["q"], inp["kt"], inp["vt"], table, wl.K)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    layer_steps = done * R_s / wl.R
-    return {"value": layer_steps / el, "unit": "layer-steps/s", "cores": int(threads),
+    done, el = passes(args.cpu_seconds)
+    # The same sample on one host core (a third of the time budget).
+    oracle.set_threads(1)
+    done1, el1 = passes(args.cpu_seconds / 3.0)
+    oracle.set_threads(threads)
+    scale = R_s / wl.R
+    return {"value": done * scale / el, "unit": "layer-steps/s", "cores": int(threads),
             "kind": "oracle",
             "sample": (f"{done} passes of scan+top-K+plan+attention over {R_s} of {wl.R} "
                        f"requests (all {wl.H} KV heads) of layer 0 at step {t}, fp64, "
                        f"{el:.1f} s; scaled to whole-batch layer-steps"),
-            "host_cpus": os.cpu_count()}
+            "one_core": {"value": done1 * scale / el1, "passes": done1,
+                         "seconds": round(el1, 1)},
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 # ----------------------------------------------------------------- main
@@ -888,6 +925,7 @@ def main(argv=None):
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic},
         "layer_step": {"algo_bytes": per_ls, "us": round(g["total_ms"] * 1000 / n_ls, 2),
+                       "per_step_spread": g["spread"],
                        "GBps": round(per_ls * n_ls / (g["total_ms"] / 1000) / 1e9, 1),
                        "frac": round(per_ls * n_ls / (g["total_ms"] / 1000) / 1e9 /
                                      PEAK_HBM_GBS, 4)},

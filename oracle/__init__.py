@@ -55,10 +55,11 @@ def _load():
                                                           _i32p, _i32p, ctypes.c_double,
                                                           _f64p, _f64p])
     lib.oro_num_threads.argtypes = []
+    lib.oro_set_threads.argtypes = [ctypes.c_int]
     for name in ("oro_build_summaries", "oro_append_kv", "oro_block_scores",
                  "oro_block_scores_variant", "oro_topk",
                  "oro_select_plan",
-                 "oro_copy_blocks", "oro_sparse_attn", "oro_num_threads"):
+                 "oro_copy_blocks", "oro_sparse_attn", "oro_num_threads", "oro_set_threads"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -84,6 +85,11 @@ def _check(rc: int, name: str) -> None:
 def num_threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS honoured)."""
     return int(_load().oro_num_threads())
+
+
+def set_threads(n: int) -> int:
+    """Threads of the following oracle calls; returns the count now in use."""
+    return int(_load().oro_set_threads(int(n)))
 
 
 def build_summaries(keys, block_size: int, seq_len=None, blk_begin: int = 0,

@@ -31,6 +31,16 @@ int oro_num_threads(void) {
 #endif
 }
 
+/* Threads of the following calls (timing runs on one host core). */
+int oro_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return oro_num_threads();
+}
+
 /* Number of full blocks of request r. */
 static int full_blocks(const int32_t* seq_len, int r, int B, int n_blk_max) {
     long L = seq_len ? (long)seq_len[r] : (long)n_blk_max * B;

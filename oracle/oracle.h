@@ -73,6 +73,7 @@ int oro_sparse_attn(int R, int n_q, int Hq, int H, int D, int B,
                     double scale, double* out, double* lse);
 
 int oro_num_threads(void);
+int oro_set_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -189,6 +189,8 @@ def test_step_tiny_fp32(cuda, case):
     (4, 128, 16, 32, dict(draft_avg=True)),
     (4, 128, 16, 24, dict(draft_avg=True, alpha=0.25, scan_chunks=3, attn_splits=2)),
     (8, 64, 16, 16, dict(draft_avg=True, impl=1)),  # 24 rows, VALU attention
+    (8, 128, 16, 16, dict(draft_avg=True)),          # 24 rows: three MFMA row groups
+    (8, 128, 16, 16, dict(draft_avg=True, scan_chunks=2, attn_splits=3)),
 ])
 def test_step_scoring_variants(cuda, G, D, B, K, opts):
     """s_b(alpha) and two drafts averaged before scoring (three query rows)."""

@@ -166,7 +166,11 @@ int oasis_append_kv(const oasis_shape* s, const void* k_new, const void* v_new,
  * partials) go through a caller-owned scratch buffer and a second, small
  * launch merges them.  The *_workspace() queries give its size for a shape;
  * 0 means none is needed (or the shape is invalid, which the call reports).
- * The content need not be initialised.  One workspace serves one call at a
+ * A size covers every attention path the call may take for the shape (MFMA or
+ * VALU, with or without an appended token): units of more than 16 query rows
+ * (two rows of a GQA group above 8) run one attention item per query row on the
+ * MFMA path, which splits them differently.  The content need not be
+ * initialised.  One workspace serves one call at a
  * time: calls that may overlap in time (other streams) need their own.
  *
  * Workspace bytes oasis_score_topk needs.

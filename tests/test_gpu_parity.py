@@ -154,7 +154,11 @@ def check_score_topk_against_oracle(wl, summ, q, idx, val, sc, n_blk_np, K):
 
 
 @pytest.mark.parametrize("name,L,K,G", [("tiny-fp32", 1024, 8, None), ("tiny-fp32", 1031, 8, None),
-                                        ("tiny-fp32", 256, 20, 4), ("qwen3-8b-1layer", 4096, 64, None)])
+                                        ("tiny-fp32", 256, 20, 4), ("qwen3-8b-1layer", 4096, 64, None),
+                                        # split selection: staged row beyond the keys held in
+                                        # registers, and a row too long to stage (global reads)
+                                        ("tiny-fp32", 16 * 9000 + 5, 64, None),
+                                        ("tiny-fp32", 16 * 20000 + 3, 64, None)])
 def test_score_topk_small(cuda, name, L, K, G):
     say(f"score_topk {name} L={L} K={K} G={G}")
     wl = synth.workload(name)

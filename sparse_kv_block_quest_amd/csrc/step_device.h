@@ -48,9 +48,9 @@ constexpr int kMaxTopK = 1024;  // largest K (resident slots per KV head)
 constexpr int kMaxRows = 32;    // n_q * G rows one attention item handles
 constexpr int kScanUnroll = 8;  // block passes in flight per scan thread
 constexpr int kTopkKPT = 16;    // top-K keys per thread held in registers
-constexpr int kFinishKPT = 32;
+constexpr int kFinishKPT = 32;  // the same in the selection launch of split units
 constexpr int kTopkGroup = 8;   // keys re-read per group beyond the register-held ones
-constexpr int kStageVec = 8;    // 16-byte score loads in flight per thread when staging  // the same in the selection launch of split units
+constexpr int kStageVec = 8;    // 16-byte score loads in flight per thread when staging
 constexpr int kMaxSplitEntries = 1024;  // tile-table entries of one attention item
 constexpr size_t kScoreLdsMax = 65536;  // scores of a whole unit kept in LDS up to this size
 
@@ -785,15 +785,15 @@ __device__ __forceinline__ TopkLds carve_topk(LdsCursor& cur, int NQ, int K4) {
 
 // Top-K of every row of unit u from `sc` (row stride rs), then, in the fused
 // step, the plan of the unit from row pred_row.
-template <int NQ, int KPT = kTopkKPT, bool GROUPED = false>
+template <int NQ>
 __device__ void select_unit(const StepArgs& a, int u, const float* sc, size_t rs,
-                            const TopkLds& T, const PlanLds& Pl, bool padded = false) {
+                            const TopkLds& T, const PlanLds& Pl) {
     const int r = u / a.H, g = u - (u / a.H) * a.H;
     const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
     const size_t ors = (size_t)a.H * a.K;
     const size_t ob = ((size_t)r * NQ * a.H + g) * a.K;
-    topk_rows<NQ, KPT, GROUPED>(sc, rs, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
-                  ors, a.do_plan ? a.pred_row : -1, T, padded);
+    topk_rows<NQ>(sc, rs, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
+                  ors, a.do_plan ? a.pred_row : -1, T);
     if (!a.do_plan) return;
     const size_t so = (size_t)u * a.K;
     plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
@@ -1305,7 +1305,6 @@ __device__ void attn_emit(const StepArgs& a, int u, int sp, const RowWin& win, c
     }
 }
 
-// LSE merge of a unit's S split partials, in split order.
 // LSE merge of the S partials of unit u, all loads issued side by side (the
 // partials come from another launch, so each round trip reaches the L2 of
 // another XCD or HBM).  (m, l) pairs lie [s][row], so thread t reads row t % NR
@@ -1536,9 +1535,6 @@ __global__ void __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(NRG ==
     }
 }
 
-// Second launch for split units: top-K (+ plan) from the global scores when
-// NC > 1 (`select` items), LSE merge of the attention partials when S > 1
-// (`merge` items).  Same XCD mapping as the main launch.
 // A split unit's score row is staged in LDS (padded) for its selection up to
 // this size.
 __host__ __device__ inline bool finish_scores_in_lds(int n_blk_max) {
@@ -1548,6 +1544,10 @@ __host__ __device__ inline size_t finish_scores_lds(int n_blk_max) {
     return finish_scores_in_lds(n_blk_max) ? (size_t)n_blk_max + kNT : 0;
 }
 
+// Second launch for split units: top-K (+ plan) from the global scores when
+// NC > 1 (`select` items, one per unit and scored row), LSE merge of the
+// attention partials when S > 1 (`merge` items, one per unit and row group).
+// Same XCD mapping as the main launch.
 template <int DT, int D, int NQ>
 __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_items, int merge_items) {
     extern __shared__ __align__(16) unsigned char lds[];

@@ -926,6 +926,9 @@ def main(argv=None):
                      "traffic": traffic},
         "layer_step": {"algo_bytes": per_ls, "us": round(g["total_ms"] * 1000 / n_ls, 2),
                        "per_step_spread": g["spread"],
+                       # HBM bytes from the committed counters over the same time
+                       "counter_GBps": (round(traffic * n_ls / (g["total_ms"] / 1000) / 1e9, 1)
+                                        if traffic and g["fused"] else None),
                        "GBps": round(per_ls * n_ls / (g["total_ms"] / 1000) / 1e9, 1),
                        "frac": round(per_ls * n_ls / (g["total_ms"] / 1000) / 1e9 /
                                      PEAK_HBM_GBS, 4)},

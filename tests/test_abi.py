@@ -129,6 +129,22 @@ def test_workspace_queries(lib):
                                               ctypes.byref(o)) >= 32 * 2 * 8 * 2048 * 4
 
 
+def test_workspace_split_layout_qwen3_235b(lib):
+    """Qwen3-235B-A22B shape (batch 8, 4 KV heads, G = 16, 8,192 blocks, K = 128):
+    32 units, 16 items each.  Fused step: 3 attention splits (x 2 query-row
+    items on the MFMA path, or 1 item each on VALU), the scan the rest; the
+    scratch is both rows' global scores plus (max, sum, acc) partials of every
+    split and row, the same for either path.  Attention alone: 8 splits with row
+    groups, 16 without; the query answers the larger layout."""
+    s = _shape(batch=8, n_q_heads=64, n_kv_heads=4)
+    U, NR, D, nb, S = 32, 32, 128, 8192, 3
+    scores = 2 * U * nb * 4
+    partials = U * S * NR * 2 * 4 + U * S * NR * D * 4
+    assert lib.oasis_lookahead_step_workspace(ctypes.byref(s), nb, 128, 128, None) == \
+        scores + partials
+    assert lib.oasis_sparse_attn_workspace(ctypes.byref(s), 128) == U * 16 * NR * (2 + D) * 4
+
+
 def _step(lib, s, **kw):
     """oasis_lookahead_step with every pointer FAKE unless overridden."""
     a = dict(q=FAKE, summ=FAKE, nb=8, n_blk=None, K=4, idx=FAKE, tsc=None, sc=None,

@@ -204,6 +204,7 @@ def test_step_scoring_variants(cuda, G, D, B, K, opts):
     (4, 128, 16, 4096, 32, (4, 3, 0)),
     (4, 128, 16, 4112, 32, (0, 0, 1)),   # VALU attention in the fused kernel
     (16, 128, 16, 2048, 24, (2, 2, 0)),  # 32 rows: two MFMA row groups
+    (16, 128, 16, 2064, 24, (3, 1, 0)),  # row groups of one split each (no merge), tail
     (8, 64, 32, 2048, 16, (0, 0, 0)),
     (4, 128, 8, 1024, 20, (2, 3, 0)),    # B < 16: VALU
 ])

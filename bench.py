@@ -889,7 +889,12 @@ def main(argv=None):
     dom = max(kern, key=lambda k: kern[k]["us"])
     achieved = kern[dom]["GBps"]
     src_hash = kernel_source_hash()
-    traffic = pmc_traffic(dom, f"{wl.name} batch {wl.R}", src_hash)
+    # The counters were taken on the default variant of each workload only.
+    default_variant = (args.alpha is None and not args.draft_avg and args.impl == "auto" and
+                       args.kv_layout == "interleaved" and not args.scan_chunks and
+                       not args.attn_splits)
+    traffic = (pmc_traffic(dom, f"{wl.name} batch {wl.R}", src_hash) if default_variant
+               else None)
 
     cpu = None
     if args.cpu_seconds > 0:

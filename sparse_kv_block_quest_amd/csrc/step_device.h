@@ -343,6 +343,7 @@ struct TopkLds {
     uint32_t* sel_key;  // [NQ][Kp4]
     int* sel_idx;       // [NQ][Kp4]
     int* P;             // [Kp4] ranked blocks of the plan's row (-1 pad)
+    unsigned long long* ek;  // [NQ][Kp4] (key, position) rank keys; GROUPED selections only
 };
 
 // Ranked top-K of NQ score rows (row j at sc + j*rs, n valid entries each; LDS
@@ -566,6 +567,30 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
     }
     lds_barrier();
     // Counting rank under (key desc, position asc); survivors sit in block order.
+    if constexpr (GROUPED) {
+        // One 64-bit compare per survivor: the key above the complement of its
+        // position (padding 0 sorts last; every real key is above 2^32).
+        unsigned long long* ek = L.ek + (size_t)j * K4;
+        for (int a = t; a < K4; a += TPR)
+            ek[a] = a < Kp ? ((unsigned long long)skey[a] << 32) | (0xffffffffu - (uint32_t)a) : 0ull;
+        lds_barrier();
+        const ulonglong2* e2 = reinterpret_cast<const ulonglong2*>(ek);
+        for (int a = t; a < Kp; a += TPR) {
+            const unsigned long long ea = ek[a];
+            int rank = 0;
+#pragma unroll 8
+            for (int i = 0; i < K4 / 2; ++i) {
+                const ulonglong2 x = e2[i];
+                rank += (x.x > ea) + (x.y > ea);
+            }
+            const int bi = sidx[a];
+            orow[rank] = bi;
+            if (srow) srow[rank] = key_float((uint32_t)(ea >> 32));
+            if (j == pred_row) L.P[rank] = bi;
+        }
+        lds_barrier();
+        return;
+    }
     const uint4* kv = reinterpret_cast<const uint4*>(skey);
     for (int a = t; a < Kp; a += TPR) {
         const uint32_t ka = skey[a];
@@ -780,6 +805,7 @@ __device__ __forceinline__ TopkLds carve_topk(LdsCursor& cur, int NQ, int K4) {
     T.sel_key = cur.take<uint32_t>((size_t)NQ * K4);
     T.sel_idx = cur.take<int>((size_t)NQ * K4);
     T.P = cur.take<int>(K4);
+    T.ek = nullptr;
     return T;
 }
 
@@ -1562,8 +1588,9 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
         if (k < nu * NQ) {
             const int u = x + 8 * (k / NQ), j = k - (k / NQ) * NQ;
             const int K4 = pad4(a.K);
-            const TopkLds T = carve_topk(cur, 1, K4);
+            TopkLds T = carve_topk(cur, 1, K4);
             const PlanLds Pl = carve_plan(cur, K4);
+            T.ek = cur.take<unsigned long long>(K4);
             const bool plan = a.do_plan && j == a.pred_row;
             if (plan)
                 plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
@@ -1644,7 +1671,8 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
 __host__ __device__ inline size_t finish_lds_bytes(int K, int n_blk_max, bool sel) {
     const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4;
     if (!sel) return m;
-    const size_t s = scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max));
+    const size_t s = scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max)) +
+                     ((size_t)pad4(K) * 8 + 15) / 16 * 16;  // rank keys
     return s > m ? s : m;
 }
 

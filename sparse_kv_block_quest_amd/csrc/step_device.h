@@ -526,13 +526,29 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
     }
     // Take every key above the threshold prefix and the first `remaining`
     // keys equal to it, in block order: exclusive counts within the row group.
+    // GROUPED with every key in registers: bit masks of the keys above / at the
+    // threshold, so the take below visits only those keys (few per thread).
+    const bool masks = GROUPED && per <= KPT && KPT <= 32;
+    uint32_t mgt = 0, meq = 0;
     uint32_t gt = 0, eq = 0;
-    OASIS_FOR_KEYS({
-        (void)ii;
-        const uint32_t mk = kk & mask;
-        gt += mk > prefix;
-        eq += mk == prefix;
-    })
+    if (masks) {
+#pragma unroll
+        for (int e = 0; e < KPT; ++e) {
+            const uint32_t mk = key[e] & mask;
+            const bool in = i0 + e < i1;
+            mgt |= uint32_t(in && mk > prefix) << e;
+            meq |= uint32_t(in && mk == prefix) << e;
+        }
+        gt = __builtin_popcount(mgt);
+        eq = __builtin_popcount(meq);
+    } else {
+        OASIS_FOR_KEYS({
+            (void)ii;
+            const uint32_t mk = kk & mask;
+            gt += mk > prefix;
+            eq += mk == prefix;
+        })
+    }
     uint32_t ig = wave_incl_sum(gt), ie = wave_incl_sum(eq);
     if (lane == 63) {
         L.scanbuf[wv * 2] = ig;
@@ -547,19 +563,39 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
     int eqb = int(ie - eq);
     uint32_t* skey = L.sel_key + j * K4;
     int* sidx = L.sel_idx + j * K4;
-    OASIS_FOR_KEYS({
-        const uint32_t mk = kk & mask;
-        bool take = mk > prefix;
-        if (mk == prefix) {
-            take = eqb < remaining;
-            ++eqb;
+    if (masks) {
+        // the threshold ties this thread may take, lowest positions first
+        const int take_eq = max(0, min(int(eq), remaining - eqb));
+        uint32_t m = mgt;
+        uint32_t me = meq;
+        for (int q = 0; q < take_eq; ++q) {
+            m |= me & (0u - me);  // lowest set bit
+            me &= me - 1u;
         }
-        if (take) {
-            skey[pos] = kk;
-            sidx[pos] = ii;
+        while (m) {
+            const int e = __builtin_ctz(m);
+            m &= m - 1u;
+            // the key again from the staged row (a register array is not
+            // indexed by a run-time position)
+            skey[pos] = float_key(row[i0 + pad + e]);
+            sidx[pos] = i0 + e;
             ++pos;
         }
-    })
+    } else {
+        OASIS_FOR_KEYS({
+            const uint32_t mk = kk & mask;
+            bool take = mk > prefix;
+            if (mk == prefix) {
+                take = eqb < remaining;
+                ++eqb;
+            }
+            if (take) {
+                skey[pos] = kk;
+                sidx[pos] = ii;
+                ++pos;
+            }
+        })
+    }
 #undef OASIS_FOR_KEYS
     for (int a = Kp + t; a < K4; a += TPR) {
         skey[a] = 0u;

@@ -10,7 +10,8 @@ Per step the fused call must give
   - the plan and new slot tables bit-exact against the oracle's plan on the
     kernel's top-K.
 Workgroup splits (scan chunks, attention splits) are swept through the
-options so the arrival-counter merges are exercised.
+options, so the split-unit path (per-chunk partial results merged by the
+second launch, finish_kernel) is exercised next to the one-launch path.
 """
 import numpy as np
 import pytest

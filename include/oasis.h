@@ -30,9 +30,14 @@
  *  - All arrays are dense and row-major in the layouts given below.
  *  - dtype (oasis_shape.dtype) applies to q, keys, values, summaries and out.
  *    Scores, lse and all accumulation are fp32.
- *  - Device-side preconditions are NOT checked and violating them is undefined
- *    behaviour: tile / block ids within range, distinct ids in one table row,
- *    finite inputs, buffers at least as large as stated.
+ *  - Ids that address memory are range-checked where they are used: a tile
+ *    table entry or active-block tile outside [0, unit_stride), a token
+ *    position past the store, and a plan entry whose source block or
+ *    destination slot lies outside its store are skipped (the entry is
+ *    treated as empty), so a corrupt id cannot make a kernel touch memory
+ *    outside the caller's buffers.  Other device-side preconditions are NOT
+ *    checked and violating them is undefined behaviour: distinct ids in one
+ *    table row, finite inputs, buffers at least as large as stated.
  *  - Notation: R batch, n_q stacked query rows (1 or 2; row 0 = normal query
  *    of step t, row 1 = draft query of step t+1; 3 with two drafts, see
  *    oasis_step_opts), n_s scored rows (n_q, or 2 when the two drafts are
@@ -357,7 +362,11 @@ int oasis_host_tier_submit(oasis_host_tier* t, const oasis_shape* s, const void*
                            hipStream_t copy_stream, hipEvent_t done);
 
 /* Host wait until every submitted job has been issued (its `done` recorded).
- * Returns OASIS_OK or the first error of a dispatched job (sticky). */
+ * Returns OASIS_OK or the first error of a dispatched job (sticky): EHIP for a
+ * failed copy-back or launch, EINVAL when a fetch found a request's budget
+ * without an evictable block (as oasis_host_tier_fetch; the gather still ran
+ * and `done` was recorded, but the planned slots of the blocks that did not
+ * fit hold stale tiles, so the caller must treat the step as failed). */
 int oasis_host_tier_wait_issued(oasis_host_tier* t);
 
 /* A block generated on the decode node (already written to the cache slot
@@ -409,6 +418,7 @@ size_t oasis_sparse_attn_workspace(const oasis_shape* s, int32_t n_sel);
  *   q           [R][n_q][Hq][D] (dtype)
  *   k_tiles     tile store, K tiles [B][D];  v_tiles  V tiles [D][B]
  *   tile_table  [R][H][n_sel] int32 unit-local tile indices, -1 = skip
+ *               (entries outside [0, unit_stride) are skipped too)
  *   unit_stride tiles per unit in the store: K for a resident set of K slots
  *               per head, n_blk_max when the full cache is the store
  *   tail_tile   [R][H] int32 unit-local tile index of the active block, or NULL

@@ -27,10 +27,12 @@ copy_blocks_kernel(const uint4* __restrict__ src_k, const uint4* __restrict__ sr
                    int K, int tile_u4, long long stride_u4, const int32_t* __restrict__ plan_count,
                    const int32_t* __restrict__ plan_src, const int32_t* __restrict__ plan_dst) {
     const size_t u = blockIdx.y;
-    const int n = plan_count[u];
+    const int n = min(plan_count[u], K);
     for (int i = blockIdx.x; i < n; i += kCopySplit) {
         const int src = plan_src[u * K + i];
         const int dst = plan_dst[u * K + i];
+        // an entry naming a block or slot outside the stores is skipped
+        if ((unsigned)src >= (unsigned)n_blk_max || (unsigned)dst >= (unsigned)K) continue;
         const uint4* sk = src_k + (u * n_blk_max + src) * (size_t)stride_u4;
         const uint4* sv = src_v + (u * n_blk_max + src) * (size_t)stride_u4;
         uint4* dk = res_k + (u * K + dst) * (size_t)stride_u4;

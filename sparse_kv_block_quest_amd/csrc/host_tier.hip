@@ -286,11 +286,11 @@ copy_mapped_kernel(const uint4* __restrict__ src_k, const uint4* __restrict__ sr
                    const int32_t* __restrict__ plan_src, const int32_t* __restrict__ plan_dst) {
     const size_t u = blockIdx.y;
     const size_t r = u / H, g = u - (u / H) * H;
-    const int n = plan_count[u];
+    const int n = min(plan_count[u], K);
     for (int i = blockIdx.x; i < n; i += kMapCopySplit) {
         const int src = plan_src[u * K + i];
         const int dst = plan_dst[u * K + i];
-        if (src < 0 || src >= n_blk) continue;
+        if (src < 0 || src >= n_blk || dst < 0 || dst >= K) continue;
         const int slot = map[r * n_blk + src];
         if (slot < 0 || slot >= cap_max) continue;
         const size_t so = ((r * cap_max + slot) * H + g) * (size_t)stride_u4;
@@ -349,14 +349,19 @@ static int run_job(oasis_host_tier* t, const TierJob& j) {
         (void)hipGetLastError();
         return OASIS_EHIP;
     }
-    (void)tier_fetch(t, ++t->clock, t->st_count, t->st_src, t->st_slots);  // failures counted
+    // A request whose budget held no evictable block leaves some planned
+    // blocks absent (EINVAL, counted as failed).  The gather still runs and
+    // `done` is still recorded, so no stream waits forever, but the slots of
+    // the absent blocks keep stale tiles: the status goes to the caller
+    // through oasis_host_tier_wait_issued.
+    const int fst = tier_fetch(t, ++t->clock, t->st_count, t->st_src, t->st_slots);
     const int st = launch_mapped(t->R * t->H, t->H, t->n_blk, t->cap_max, t->K, j);
     if (st != OASIS_OK) return st;
     if (hipEventRecord(j.done, j.copy_stream) != hipSuccess) {
         (void)hipGetLastError();
         return OASIS_EHIP;
     }
-    return OASIS_OK;
+    return fst;
 }
 
 static void dispatcher_main(oasis_host_tier* t) {

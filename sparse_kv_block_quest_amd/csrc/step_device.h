@@ -206,7 +206,7 @@ __host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_sco
     size_t b = a16(NQ * 2 * D * 4);                                     // pn
     b += a16(NQ * 512 * 4) + a16(4 * 2 * 4) + a16(16 * 4);             // hist, scan, sh
     b += a16(NQ * kp * 4) * 2 + a16(kp * 4);                            // sel key/idx, P
-    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 5 + a16(64) + a16(16);  // plan
+    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 5 + a16(64) + a16(48);  // plan
     b += a16((size_t)n_scores * 4);                                     // scores
     return b;
 }
@@ -661,7 +661,8 @@ struct PlanLds {
     int* new_stamp;        // [K4]
     int* rank_of_slot;     // [K4] victim rank of a slot (K for hits)
     uint32_t* scanbuf;     // [4][2]
-    unsigned long long* ins_key;  // [2]: oldest (stamp, slot) key; slot holding the new block
+    unsigned long long* ins_key;  // [6]: oldest (stamp, slot) key; slot holding the new block;
+                                  // [2..5] each wave's oldest key
 };
 
 __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
@@ -677,7 +678,7 @@ __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
     L.new_stamp = cur.take<int>(K4);
     L.rank_of_slot = cur.take<int>(K4);
     L.scanbuf = cur.take<uint32_t>(16);
-    L.ins_key = cur.take<unsigned long long>(2);
+    L.ins_key = cur.take<unsigned long long>(6);
     return L;
 }
 
@@ -778,21 +779,31 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
         L.new_blk[dst] = L.missing_of_rank[i];
         L.new_stamp[dst] = step;
     }
-    if (ins >= 0 && tid == 0) {
-        L.ins_key[0] = ~0ull;
-        L.ins_key[1] = ~0ull;
-    }
+    if (ins >= 0 && tid == 0) L.ins_key[1] = ~0ull;
     lds_barrier();
     if (ins >= 0) {  // uniform: one value per request
+        // The oldest (stamp, slot) after the admissions: a minimum per thread,
+        // per wave (DPP, high words first, then the low words of the lanes
+        // holding the smallest high word), then over the 4 waves.
+        unsigned long long best = ~0ull;
         for (int s = tid; s < K; s += kNT) {
             // Stamps are >= -1: the offset keeps the unsigned order of (stamp, slot).
             const unsigned long long key =
                 ((unsigned long long)((long long)L.new_stamp[s] + 0x80000000LL) << 32) | (unsigned)s;
-            atomicMin(&L.ins_key[0], key);
+            best = key < best ? key : best;
             if (L.new_blk[s] == ins) L.ins_key[1] = (unsigned)s;  // at most one slot
         }
+        const uint32_t bh = (uint32_t)(best >> 32);
+        const uint32_t mh = wave_min(bh);
+        const uint32_t ml = wave_min(bh == mh ? (uint32_t)best : 0xffffffffu);
+        if ((tid & 63) == 0) L.ins_key[2 + (tid >> 6)] = ((unsigned long long)mh << 32) | ml;
         lds_barrier();
         if (tid == 0) {
+            unsigned long long oldest = L.ins_key[2];
+#pragma unroll
+            for (int ww = 1; ww < kNT / 64; ++ww)
+                oldest = L.ins_key[2 + ww] < oldest ? L.ins_key[2 + ww] : oldest;
+            L.ins_key[0] = oldest;
             const unsigned long long at = L.ins_key[1];
             if (at != ~0ull) {
                 L.new_stamp[(int)at] = step;
@@ -913,7 +924,7 @@ __device__ __forceinline__ SplitRange split_range(const StepArgs& a, int u, int 
     if constexpr (TOK) {  // the tokens of the active block before the new one
         if (sp == a.S - 1) {
             const int p = a.pos[u / a.H];
-            if (p >= 0 && p % a.B > 0) {
+            if (p >= 0 && p / a.B < a.unit_stride && p % a.B > 0) {
                 s.tail_tile = p / a.B;
                 s.tail_len = p % a.B;
             }
@@ -924,7 +935,7 @@ __device__ __forceinline__ SplitRange split_range(const StepArgs& a, int u, int 
         const int r = u / a.H;
         const int tt = a.tail_tile[u];
         const int tl = min(a.tail_len[r], a.B);
-        if (tt >= 0 && tl > 0) {
+        if (tt >= 0 && tt < a.unit_stride && tl > 0) {
             s.tail_tile = tt;
             s.tail_len = tl;
         }
@@ -1040,7 +1051,8 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& w
             const int e = st / spe;
             tile = tbl[e];
             sub = st - e * spe;
-            ntok = tile >= 0 ? 16 : 0;
+            // ids outside the unit's tiles are skipped like -1 entries
+            ntok = (tile >= 0 && tile < a.unit_stride) ? 16 : 0;
         } else if (st < n_sub) {
             tile = sr.tail_tile;
             sub = st - n_entry_sub;
@@ -1266,7 +1278,7 @@ __device__ void attn_item_valu(const StepArgs& a, int u, int sp, LdsCursor& cur,
             tile = tbl[st / spe];
             sub = st - (st / spe) * spe;
             nt = sub_tokens;
-            if (tile < 0) continue;
+            if (tile < 0 || tile >= a.unit_stride) continue;  // -1 or out of range: skipped
         } else {
             tile = sr.tail_tile;
             sub = st - n_entry_sub;
@@ -1457,7 +1469,7 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
     constexpr int PL = (D + 63) / 64;  // dims per lane
     const int r = u / a.H, g = u - (u / a.H) * a.H;
     const int p = a.pos[r];
-    if (p < 0) return;
+    if (p < 0 || p / a.B >= a.unit_stride) return;  // no token, or past the store
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t kn = (size_t)u * D;
     constexpr int RW = kMaxRows / (kNT / 64);  // rows per wave at most

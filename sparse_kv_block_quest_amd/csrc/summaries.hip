@@ -156,7 +156,7 @@ append_kv_kernel(const void* __restrict__ k_new, const void* __restrict__ v_new,
     const int p = pos[r];
     const E kx = reinterpret_cast<const E*>(k_new)[i];
     const E vx = reinterpret_cast<const E*>(v_new)[i];
-    if (p < 0) return;
+    if (p < 0 || p / B >= n_blk_max) return;  // no token, or past the store
     const int b = p / B, t = p - b * B;
     const size_t tile = ((size_t)u * n_blk_max + b) * (size_t)stride;
     if (summ && t == B - 1) {

@@ -5,16 +5,22 @@ Run A synchronises after every layer-step and checks each step against the
 oracle: scores, top-K, plan and slot tables, and attention over the resident
 store (which must hold exactly the host tiles its slot table names, byte for
 byte).  Run B repeats the same steps free-running, ordered only by the
-pipeline's events, and must reproduce run A bit for bit; a missing wait
-between a copy and the attention that reads or last read its slots would
-show up there.
+pipeline's events, and must reproduce run A bit for bit.  Runs C and D do the
+same with a bounded delay kernel (a clock spin that always ends) enqueued
+before every fused step on the main stream (C), or before every copy on the
+copy stream (D).  C holds each attention back while the copy stream is free:
+a copy not ordered after the attention that last read its slots (the WAR
+hazard of v2 §3.3.1's per-layer event ordering) would overwrite them first.
+D holds each copy back: a next-step attention not ordered after the copy
+into its slots (RAW) would read the old tiles.  Either missing event makes
+C or D differ from A deterministically, not by timing luck.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from sparse_kv_block_quest_amd import ops, pipeline, synth
+from sparse_kv_block_quest_amd import _lib, ops, pipeline, synth
 from test_gpu_step import check_step, small
 
 pytestmark = pytest.mark.gpu
@@ -79,8 +85,14 @@ def resident_matches_host(layer, blk):
     assert torch.equal(layer.res.view(torch.int16), want.view(torch.int16))
 
 
+# Bounded spin of the delay kernel (torch.cuda._sleep counts shader clock
+# cycles): ~0.5 ms at the MI355X's 2.4 GHz, far longer than a small fused step
+# or copy, and it always ends.
+DELAY_CYCLES = 1_200_000
+
+
 def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_capacity=None,
-                      host_workers=1):
+                      host_workers=1, n_runs=3):
     dev = cuda
     qs = query_steps(wl, dev, n_layers, n_steps)
     n_valid = np.full(wl.R, wl.n_blk, np.int32)
@@ -123,23 +135,31 @@ def run_pipeline_case(cuda, wl, n_layers, n_steps, units=None, opts=None, host_c
                 assert L.tier.state()[2]["failed"] == 0
     del pa
 
-    # run B: free-running, events only
-    pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False, host_capacity=host_capacity,
-                       host_workers=host_workers)
-    pb.seed(q0s)
-    outs_b = []
-    for t in range(n_steps):
+    # runs B (free-running, events only), C (delay before every fused step on
+    # the main stream) and D (delay before every copy on the copy stream)
+    for name, delay in (("B", None), ("C", "main"), ("D", "copy"))[:n_runs]:
+        pb, q0s, _ = build(wl, dev, n_layers, opts, want_scores=False,
+                           host_capacity=host_capacity, host_workers=host_workers)
+        pb.seed(q0s)
+        outs_b = []
+        for t in range(n_steps):
+            for l in range(n_layers):
+                if delay == "main":
+                    torch.cuda._sleep(DELAY_CYCLES)  # the current (main) stream
+                elif delay == "copy":  # lands before this layer-step's copy
+                    with torch.cuda.stream(pb.copy_stream):
+                        torch.cuda._sleep(DELAY_CYCLES)
+                res = pb.layer_step(t, l, qs[t][l])
+                outs_b.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
+        pb.drain()
+        torch.cuda.synchronize()
+        say(f"  pipeline {name} done")
+        for i, (xa, xb) in enumerate(zip(outs_a, outs_b)):
+            for ta, tb in zip(xa, xb):
+                assert torch.equal(ta, tb), f"run {name}: layer-step {i} differs from run A"
         for l in range(n_layers):
-            res = pb.layer_step(t, l, qs[t][l])
-            outs_b.append((res["out"].clone(), res["lse"].clone(), res["topk_idx"].clone()))
-    pb.drain()
-    torch.cuda.synchronize()
-    say("  pipeline B done")
-    for i, (xa, xb) in enumerate(zip(outs_a, outs_b)):
-        for ta, tb in zip(xa, xb):
-            assert torch.equal(ta, tb), f"free-running layer-step {i} differs"
-    for l in range(n_layers):
-        resident_matches_host(pb.layers[l], pb.resident_blocks(l, n_steps))
+            resident_matches_host(pb.layers[l], pb.resident_blocks(l, n_steps))
+        del pb
 
 
 def test_pipeline_small(cuda):
@@ -152,7 +172,34 @@ def test_pipeline_full_shape(cuda):
     """The Qwen3-8B pipeline shape (R=8, 32K context, K=128, cap 16), two layers."""
     wl = synth.workload("qwen3-8b-pipeline", layers=2)
     say("pipeline qwen3-8b shape, 2 layers x 2 steps")
-    run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)])
+    run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)], n_runs=1)
+
+
+def test_pipeline_cache_budget_too_small(cuda):
+    """A decode-host budget below the union of the heads' working sets: the
+    seeding fetch finds no evictable block for some planned blocks.  The
+    dispatcher still launches the gather and records the copy event (nothing
+    waits forever), and the failure comes back as EINVAL from the host wait
+    that the pipeline makes before using that event.  The reference cache on
+    the same plan fails the same way (v2 §3.2.3: the budget must hold the
+    working set)."""
+    wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=2048, K=16, cap=4)
+    cap = 20  # per request; the two heads' seeding sets hold up to 32 blocks
+    say(f"pipeline with decode-host cache of {cap} blocks per request (too small)")
+    p, q0s, _ = build(wl, cuda, 1, host_capacity=cap)
+    p.seed(q0s)
+    with pytest.raises(_lib.OasisError) as e:
+        p.drain()
+    assert e.value.status == _lib.OASIS_EINVAL
+    torch.cuda.synchronize()
+    L = p.layers[0]
+    stats = L.tier.state()[2]
+    assert stats["failed"] > 0
+    # the same plan in the reference cache also runs out of evictable blocks
+    model = oracle.HostTierModel([cap] * wl.R, wl.n_blk)
+    with pytest.raises(RuntimeError):
+        model.fetch(1, L.plan["plan_count"].cpu().numpy(), L.plan["plan_src"].cpu().numpy(),
+                    L.blk[0].cpu().numpy())
 
 
 @pytest.mark.parametrize("cap,workers", [(40, 1), (36, 1), (36, 3)])
@@ -172,4 +219,4 @@ def test_pipeline_with_decode_host_cache_full_shape(cuda):
     wl = synth.workload("qwen3-8b-pipeline", layers=2)
     say("pipeline qwen3-8b shape with decode-host cache 1229, 2 layers x 2 steps")
     run_pipeline_case(cuda, wl, 2, 2, units=[(0, 0), (3, 5), (7, 7)], host_capacity=1229,
-                      host_workers=4)
+                      host_workers=4, n_runs=1)

@@ -531,6 +531,42 @@ int oasis_lookahead_step_append(const oasis_shape* s, const void* q, void* summa
                                 float scale, void* out, float* lse, const oasis_step_opts* opts,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of the per-GPU scratch array behind oasis_lookahead_step_noalloc. */
+#define OASIS_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * oasis_lookahead_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not call hipMalloc,
+ * harnesses that forbid allocation): the same arguments, results and errors
+ * without workspace / workspace_bytes.  The scratch of split units lives in a
+ * library-owned device array of OASIS_NOALLOC_SCRATCH_BYTES per GPU (16 MiB,
+ * held by every GPU the library runs on until the process ends); its device
+ * address is looked up once per device, on the first call with that device
+ * current.  The call allocates nothing.  The caller still passes every input
+ * and output.
+ *   EWORKSPACE  the shape needs more scratch than the array holds, i.e.
+ *               oasis_lookahead_step_workspace() > OASIS_NOALLOC_SCRATCH_BYTES
+ *               (checked on the host before any launch)
+ *   EINVAL      as oasis_lookahead_step, or `stream` belongs to a device other
+ *               than the current one while the shape needs scratch
+ *   EHIP        the scratch address could not be looked up, or a launch failed
+ * Every call on one GPU uses the same array and leaves its contents there (no
+ * call needs it zeroed): calls that may overlap in time on one GPU (several
+ * streams or host threads) race on it and must be serialised by the caller.
+ */
+int oasis_lookahead_step_noalloc(const oasis_shape* s, const void* q, const void* summaries,
+                                 int32_t n_blk_max, const int32_t* n_blk, int32_t top_k,
+                                 int32_t* topk_idx, float* topk_score, float* scores,
+                                 const int32_t* slot_block_in, const int32_t* slot_stamp_in,
+                                 int32_t* slot_block_out, int32_t* slot_stamp_out, int32_t step,
+                                 int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+                                 int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst,
+                                 int32_t* plan_evicted, const void* k_tiles, const void* v_tiles,
+                                 const int32_t* tile_table, int32_t n_sel, int64_t unit_stride,
+                                 const int32_t* tail_tile, const int32_t* tail_len, float scale,
+                                 void* out, float* lse, const oasis_step_opts* opts,
+                                 hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

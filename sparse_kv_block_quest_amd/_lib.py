@@ -20,6 +20,8 @@ OASIS_EHIP = -4
 OASIS_F32 = 0
 OASIS_BF16 = 1
 
+OASIS_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/oasis.h
+
 IMPL_AUTO = 0
 IMPL_VALU = 1
 IMPL_MFMA = 2
@@ -50,6 +52,7 @@ EXPORTS = (
     "oasis_lookahead_step_workspace",
     "oasis_lookahead_step",
     "oasis_lookahead_step_append",
+    "oasis_lookahead_step_noalloc",
 )
 
 
@@ -142,6 +145,11 @@ def load() -> ctypes.CDLL:
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
          _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
          _opts, _vp, _sz, _vp])
+    lib.oasis_lookahead_step_noalloc.argtypes = (
+        [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp,          # q .. scores
+         _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
+         _vp, _vp, _vp, _i32, ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp,  # attention
+         _opts, _vp])
     lib.oasis_lookahead_step_append.argtypes = (
         [_shp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp,          # q .. scores
          _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,  # slots .. plan
@@ -154,7 +162,8 @@ def load() -> ctypes.CDLL:
         getattr(lib, name).restype = ctypes.c_int
     for name in ("oasis_build_summaries", "oasis_score_topk", "oasis_select_plan", "oasis_append_kv",
                  "oasis_copy_blocks", "oasis_sparse_attn", "oasis_sparse_attn_impl",
-                 "oasis_lookahead_step", "oasis_lookahead_step_append"):
+                 "oasis_lookahead_step", "oasis_lookahead_step_append",
+                 "oasis_lookahead_step_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib

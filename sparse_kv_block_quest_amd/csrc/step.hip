@@ -2,6 +2,8 @@
 // oasis_lookahead_step (scan + top-K + plan fused with the attention of the
 // current resident set in one launch), oasis_score_topk (scan + top-K only),
 // oasis_sparse_attn (attention only) and oasis_select_plan (plan only).
+#include <mutex>
+
 #include "step_device.h"
 
 namespace oasis {
@@ -556,4 +558,74 @@ extern "C" int oasis_lookahead_step_append(
                             pred_row, ins_blk, plan_count, plan_src, plan_dst, plan_evicted,
                             k_tiles, v_tiles, tile_table, n_sel, unit_stride, nullptr, nullptr,
                             scale, out, lse, opts, workspace, workspace_bytes, stream, &tok);
+}
+
+// ================================================================ fused step, no allocation
+// oasis_lookahead_step_noalloc: the split-unit scratch (block scores, attention
+// partials) lives in this file-scope device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy for the life of
+// the process; the host reaches it only through the address
+// hipGetSymbolAddress returns on that device (the array's name is a host-side
+// stand-in, not a device address).  Every call on one GPU shares the array.
+static __device__ __align__(256) unsigned char scratch[OASIS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];  // per device, set on the first call there
+}  // namespace
+
+// Device address of `scratch` on the current device (looked up once per device,
+// with that device current).
+static int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return OASIS_EHIP;
+    }
+    if (dev < 0 || dev >= kScratchDevices) return OASIS_EUNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return OASIS_EHIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return OASIS_OK;
+}
+
+extern "C" int oasis_lookahead_step_noalloc(
+    const oasis_shape* s, const void* q, const void* summaries, int32_t n_blk_max,
+    const int32_t* n_blk, int32_t top_k, int32_t* topk_idx, float* topk_score, float* scores,
+    const int32_t* slot_block_in, const int32_t* slot_stamp_in, int32_t* slot_block_out,
+    int32_t* slot_stamp_out, int32_t step, int32_t cap, int32_t pred_row, const int32_t* ins_blk,
+    int32_t* plan_count, int32_t* plan_src, int32_t* plan_dst, int32_t* plan_evicted,
+    const void* k_tiles, const void* v_tiles, const int32_t* tile_table, int32_t n_sel,
+    int64_t unit_stride, const int32_t* tail_tile, const int32_t* tail_len, float scale, void* out,
+    float* lse, const oasis_step_opts* opts, hipStream_t stream) {
+    int st = step_check(s, n_blk_max, top_k, n_sel, opts);
+    if (st != OASIS_OK) return st;
+    // The scratch this call needs (0 when every unit fits one launch), checked
+    // against the array's size before anything touches the GPU.
+    const size_t need = oasis_lookahead_step_workspace(s, n_blk_max, top_k, n_sel, opts);
+    if (need > (size_t)OASIS_NOALLOC_SCRATCH_BYTES) return OASIS_EWORKSPACE;
+    void* ws = nullptr;
+    if (need > 0 && (st = scratch_address(&ws)) != OASIS_OK) return st;
+    if (stream && need > 0) {  // the scratch address belongs to the current device
+        int cur = -1, sdev = -1;
+        if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess) {
+            (void)hipGetLastError();
+            return OASIS_EHIP;
+        }
+        if (sdev != cur) return OASIS_EINVAL;
+    }
+    return lookahead(s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores,
+                     slot_block_in, slot_stamp_in, slot_block_out, slot_stamp_out, step, cap,
+                     pred_row, ins_blk, plan_count, plan_src, plan_dst, plan_evicted, k_tiles,
+                     v_tiles, tile_table, n_sel, unit_stride, tail_tile, tail_len, scale, out,
+                     lse, opts, ws, need > 0 ? (size_t)OASIS_NOALLOC_SCRATCH_BYTES : 0, stream,
+                     nullptr);
 }

@@ -617,11 +617,12 @@ class PreparedStep:
     _Q, _STEP, _BI, _SI, _BO, _SO, _INS, _TBL = 1, 13, 9, 10, 11, 12, 16, 23
     _KNEW, _VNEW, _POS = 26, 27, 28  # oasis_lookahead_step_append only
 
-    def __init__(self, args, res, lib, append=False):
+    def __init__(self, args, res, lib, append=False, no_alloc=False):
         self.args = args
         self.res = res
         self.append = append
-        self._name = "oasis_lookahead_step_append" if append else "oasis_lookahead_step"
+        self._name = ("oasis_lookahead_step_append" if append else
+                      "oasis_lookahead_step_noalloc" if no_alloc else "oasis_lookahead_step")
         self._fn = getattr(lib, self._name)
 
     def __call__(self, step: int, q: torch.Tensor | None = None, token=None) -> dict:
@@ -657,8 +658,12 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
                    tail_tile: torch.Tensor | None = None, tail_len: torch.Tensor | None = None,
                    scale: float = 0.0, want_scores: bool = False, want_lse: bool = True,
                    want_evicted: bool = True, opts: OasisStepOpts | None = None,
-                   bufs: dict | None = None, stream=None, new_token=None) -> PreparedStep:
+                   bufs: dict | None = None, stream=None, new_token=None,
+                   no_alloc: bool = False) -> PreparedStep:
     """One fused layer-step (attention over ``tile_table`` + scan, top-K and plan).
+
+    no_alloc: call oasis_lookahead_step_noalloc (the library's per-GPU scratch
+    array instead of a workspace tensor; no ``workspace`` is allocated).
 
     new_token: (k_new [R][H][D], v_new [R][H][D], pos [R] int32) appends one
     token per request in the same launch (oasis_lookahead_step_append): the
@@ -719,11 +724,16 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
         "plan_dst": get("plan_dst", (R, H, K), torch.int32),
         "plan_evicted": get("plan_evicted", (R, H, K), torch.int32) if want_evicted else None,
     }
-    if b.get("workspace") is None:
-        wsb = lib.oasis_lookahead_step_workspace(ctypes.byref(shp), nb, K, n_sel,
-                                                 ctypes.byref(opts) if opts is not None else None)
-        b["workspace"] = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
-    ws = b["workspace"]
+    if no_alloc and new_token is not None:
+        raise ValueError("the no-allocation form has no appended token")
+    if no_alloc:
+        ws = None
+    else:
+        if b.get("workspace") is None:
+            wsb = lib.oasis_lookahead_step_workspace(
+                ctypes.byref(shp), nb, K, n_sel, ctypes.byref(opts) if opts is not None else None)
+            b["workspace"] = torch.zeros(max(int(wsb), 1), dtype=torch.uint8, device=dev)
+        ws = b["workspace"]
     for t, n in ((n_blk, "n_blk"), (tail_tile, "tail_tile"), (tail_len, "tail_len"),
                  (ins_blk, "ins_blk")):
         if t is not None:
@@ -752,9 +762,9 @@ def prepare_lookahead_step(q: torch.Tensor, summaries: torch.Tensor, top_k: int,
             ctypes.c_void_p(vptr),
             _ptr(tile_table), n_sel, int(unit_stride), *tail,
             float(scale), _ptr(res["out"]), _ptr(res["lse"]),
-            ctypes.byref(opts) if opts is not None else None, _ptr(ws), ws.numel(),
-            _stream(stream)]
-    call = PreparedStep(args, res, lib, append=new_token is not None)
+            ctypes.byref(opts) if opts is not None else None,
+            *([] if no_alloc else [_ptr(ws), ws.numel()]), _stream(stream)]
+    call = PreparedStep(args, res, lib, append=new_token is not None, no_alloc=no_alloc)
     call._keep = (shp, opts, q, summaries, slot_block, slot_stamp, slot_block_out,
                   slot_stamp_out, k_tiles, v_tiles, tile_table, n_blk, tail_tile, tail_len, ins_blk,
                   ws, new_token)

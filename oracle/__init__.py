@@ -21,7 +21,9 @@ import numpy as np
 from .host_tier import HostTierModel  # noqa: F401  (decode-host cache reference)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboasis_oracle.so")
+# OASIS_ORACLE_LIB names another build of oracle.c (the sanitizer test loads an
+# address/undefined-behaviour instrumented one); by default the plain build.
+_LIB_PATH = os.environ.get("OASIS_ORACLE_LIB") or os.path.join(_HERE, "liboasis_oracle.so")
 _lib = None
 
 _f64p = ctypes.POINTER(ctypes.c_double)

@@ -408,12 +408,21 @@ def run_grow(args, wl, torch, synth, ops):
     g = synth.generator(wl.seed + 99, synth.S_MISC, dev)
     knew = torch.randn((T, n_layers, R, H, D), generator=g, device=dev).to(wl.dtype)
     vnew = torch.randn((T, n_layers, R, H, D), generator=g, device=dev).to(wl.dtype)
-    # Per-step bookkeeping, shared by the layers (device buffers the prepared
-    # calls point at, rewritten in place).
-    n_blk = (L0 // B).to(torch.int32)
-    tail_tile = torch.zeros((R, H), dtype=torch.int32, device=dev)
-    tail_len = torch.zeros(R, dtype=torch.int32, device=dev)
-    ins = torch.full((R,), -1, dtype=torch.int32, device=dev)
+    # Per-step bookkeeping of every step, computed before timing (it is the
+    # engine's, not the layer-step's): at step t each request appends the token
+    # at position L0 + t; its block is the active one (not scored), and a token
+    # that completes its block makes that block the plan's insertion.
+    steps = torch.arange(T, device=dev)[:, None]
+    pos_all = (L0[None, :] + steps).to(torch.int32).contiguous()           # [T][R]
+    act_all = (pos_all // B).to(torch.int32)
+    tl_all = (pos_all - act_all * B + 1).to(torch.int32).contiguous()       # tokens incl. the new one
+    n_blk_all = act_all.contiguous()
+    tt_all = act_all[:, :, None].expand(T, R, H).contiguous()
+    ins_all = torch.where(tl_all == B, act_all, torch.full_like(act_all, -1)).contiguous()
+    n_blk = n_blk_all[0].clone()
+    tail_tile = tt_all[0].clone()
+    tail_len = tl_all[0].clone()
+    ins = ins_all[0].clone()
     idx = torch.empty((R, wl.n_q, H, K), dtype=torch.int32, device=dev)
     blk = [[torch.full((R, H, K), -1, dtype=torch.int32, device=dev) for _ in range(2)]
            for _ in range(n_layers)]
@@ -426,8 +435,7 @@ def run_grow(args, wl, torch, synth, ops):
         ops.select_plan(idx, blk[l][0], stamp[l][0], 0, wl.cap, pred_row=0)
     opts = ops.step_opts(args.scan_chunks, args.attn_splits, impl)
     bufs = {}
-    L = L0.clone()
-    pos = torch.zeros(R, dtype=torch.int32, device=dev)
+    pos = pos_all[0].clone()
     tail = (dict(new_token=(knew[0, 0], vnew[0, 0], pos)) if fused else
             dict(tail_tile=tail_tile, tail_len=tail_len))
     calls = [[ops.prepare_lookahead_step(
@@ -438,33 +446,25 @@ def run_grow(args, wl, torch, synth, ops):
     # One prepared append per (step, layer): the token write and, for a token
     # that completes its block, that block's summaries, in one launch.
     appends = None if fused else [
-        [ops.prepare_append_kv(knew[t, l], vnew[t, l], pos, layers[l]["keys"], layers[l]["vt"], B,
-                               summaries=layers[l]["summ"])
+        [ops.prepare_append_kv(knew[t, l], vnew[t, l], pos_all[t], layers[l]["keys"],
+                               layers[l]["vt"], B, summaries=layers[l]["summ"])
          for l in range(n_layers)] for t in range(T)]
-    inserted = torch.zeros((), dtype=torch.int64, device=dev)
 
     def step(t):
-        nonlocal L
-        pos.copy_(L)
-        L = L + 1
-        act = (L - 1) // B
-        tl = L - act * B
-        n_blk.copy_(act)
-        tail_len.copy_(tl)
-        tail_tile.copy_(act[:, None].expand(R, H))
-        ins.copy_(torch.where(tl == B, act, torch.full_like(act, -1)))
+        """Step t of every layer: launches only (the step's bookkeeping tensors
+        were computed above)."""
         for l in range(n_layers):
             if fused:
-                calls[l][t % 2](t + 1, qseq[t, l], token=(knew[t, l], vnew[t, l], pos))
+                calls[l][t % 2](t + 1, qseq[t, l], token=(knew[t, l], vnew[t, l], pos_all[t]),
+                                n_blk=n_blk_all[t], ins_blk=ins_all[t])
             else:
                 appends[t][l]()
-                calls[l][t % 2](t + 1, qseq[t, l])
-        inserted.add_((ins >= 0).sum())
+                calls[l][t % 2](t + 1, qseq[t, l], n_blk=n_blk_all[t], ins_blk=ins_all[t],
+                                tail=(tt_all[t], tl_all[t]))
 
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    inserted.zero_()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     ev0.record()
@@ -472,9 +472,10 @@ def run_grow(args, wl, torch, synth, ops):
         step(t)
     ev1.record()
     torch.cuda.synchronize()
+    inserted = int((ins_all[args.warmup:T] >= 0).sum().item())
     return {"total_ms": ev0.elapsed_time(ev1), "wall_s": time.perf_counter() - w0,
-            "inserted_per_step": float(inserted.item()) / args.steps,
-            "L_start": int(L0.min()), "L_end": int(L.max())}
+            "inserted_per_step": float(inserted) / args.steps,
+            "L_start": int(L0.min()), "L_end": int(pos_all[T - 1].max()) + 1}
 
 
 def report_grow(args, wl, g):

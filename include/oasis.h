@@ -508,7 +508,7 @@ int oasis_lookahead_step(const oasis_shape* s, const void* q, const void* summar
  * integer outputs bit for bit, attention up to rounding (the new token joins
  * each row's softmax after the resident tiles and the stored part of the
  * active block, read from k_new / v_new).
- *   k_new, v_new  [R][H][D] the token's key and value (dtype)
+ *   k_new, v_new  [R][H][D] the token's key and value (dtype), 16-byte aligned
  *   pos           [R] int32 its position, < 0 = none
  *   k_tiles, v_tiles, summaries  the full cache (written: the token's row and
  *                 column, the summary of a block the token completes)

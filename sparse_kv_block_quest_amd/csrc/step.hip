@@ -303,7 +303,8 @@ static size_t lds_for(const StepArgs& a, Role role, int att) {
     if (role != Role::kAttn)
         b = scan_lds_bytes(a.NS, a.D, a.K, a.scores_lds ? a.NS * a.n_blk_max : 0);
     if (role != Role::kScan) {
-        const size_t t = attn_lds_bytes(att, item_rows(a), a.D, a.per_split > 0 ? a.per_split : 1);
+        const size_t t = attn_lds_bytes(att, item_rows(a), a.D, a.per_split > 0 ? a.per_split : 1,
+                                        a.pos != nullptr);
         b = t > b ? t : b;
     }
     return b;
@@ -552,6 +553,9 @@ extern "C" int oasis_lookahead_step_append(
     const void* k_new, const void* v_new, const int32_t* pos, float scale, void* out, float* lse,
     const oasis_step_opts* opts, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!k_new || !v_new || !pos || unit_stride != n_blk_max) return OASIS_EINVAL;
+    // the token's rows are read as 16-byte vectors
+    if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15)
+        return OASIS_EINVAL;
     const NewToken tok{k_new, v_new, pos};
     return lookahead(s, q, summaries, n_blk_max, n_blk, top_k, topk_idx, topk_score, scores,
                             slot_block_in, slot_stamp_in, slot_block_out, slot_stamp_out, step, cap,

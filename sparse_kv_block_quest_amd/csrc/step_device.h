@@ -52,6 +52,7 @@ constexpr int kFinishKPT = 32;  // the same in the selection launch of split uni
 constexpr int kTopkGroup = 8;   // keys re-read per group beyond the register-held ones
 constexpr int kStageVec = 8;    // 16-byte score loads in flight per thread when staging
 constexpr int kMaxSplitEntries = 1024;  // tile-table entries of one attention item
+constexpr int kSummRows = 16;   // stored rows of a completed block staged for its summary
 constexpr size_t kScoreLdsMax = 65536;  // scores of a whole unit kept in LDS up to this size
 
 enum { kAttnNone = 0, kAttnMfma = 1, kAttnValu = 2 };
@@ -944,10 +945,13 @@ __device__ __forceinline__ SplitRange split_range(const StepArgs& a, int u, int 
 }
 
 // LDS of an attention item: table slice + final (m, l, acc) of the item, plus
-// the kernel-specific staging below.
-__host__ __device__ inline size_t attn_lds_bytes(int att, int NR, int D, int per_split) {
+// the kernel-specific staging below, plus (tok) the appended token's stage.
+__host__ __device__ inline size_t attn_lds_bytes(int att, int NR, int D, int per_split,
+                                                 bool tok = false) {
     auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
     size_t b = a16((size_t)per_split * 4) + a16(NR * 4) * 2 + a16((size_t)NR * D * 4);
+    if (tok) b += a16((size_t)NR * D * 4) + a16((size_t)D * 4) * 2 +
+                  a16((size_t)kSummRows * D * 4);  // TokStage (raw elements, fp32 at most)
     if (att == kAttnMfma) {
         b += a16(3 * NR * 4) * 2 + a16((size_t)3 * NR * D * 4) + a16((size_t)4 * 16 * D * 2);
     } else {
@@ -976,6 +980,84 @@ __device__ __forceinline__ RowWin row_win(const StepArgs& a, int grp) {
     return a.RGN > 1 ? RowWin{grp * a.G, a.G, grp} : RowWin{0, a.NR, 0};
 }
 
+// The appended token of a growing context (launches instantiated with TOK):
+// what its online-softmax step and its summary need -- the unit's query rows,
+// the token's key and value, and the active block's stored keys (used when
+// the token completes the block, B <= kSummRows + 1) -- loaded as 16-byte
+// vectors in the round trip the attention item makes anyway before its first
+// tile, and kept in LDS as raw elements, so the step after the loop issues no
+// load (under the launch's full HBM stream a round trip there costs several
+// microseconds at the end of the critical path).  Every load is issued before
+// the first LDS store, unconditionally with its index clamped (a guarded load
+// compiles to a branch that waits for it).
+struct TokStage {
+    const uint8_t* q;     // [NR][D] the unit's query rows (LDS, raw elements)
+    const uint8_t* k;     // [D] the new key
+    const uint8_t* v;     // [D] the new value
+    const uint8_t* rows;  // [B-1][D] stored keys of the active block
+    int active;           // this item appends a token (uniform)
+    int summ;             // the token completes its block: 0 no, 1 rows staged, 2 load them
+};
+
+template <int DT, int D>
+__device__ __forceinline__ TokStage tok_prefetch(const StepArgs& a, int u, int sp, LdsCursor& cur) {
+    constexpr int EB = Elem<DT>::bytes;
+    constexpr int RV = D * EB / 16;  // 16-byte vectors per row of D elements
+    uint4* q = cur.take<uint4>((size_t)a.NR * RV);
+    uint4* k = cur.take<uint4>(RV);
+    uint4* v = cur.take<uint4>(RV);
+    uint4* rows = cur.take<uint4>((size_t)kSummRows * D * 4 / 16);
+    TokStage ts;
+    ts.q = reinterpret_cast<const uint8_t*>(q);
+    ts.k = reinterpret_cast<const uint8_t*>(k);
+    ts.v = reinterpret_cast<const uint8_t*>(v);
+    ts.rows = reinterpret_cast<const uint8_t*>(rows);
+    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int p = a.pos[r];
+    ts.active = sp == a.S - 1 && p >= 0 && p / a.B < a.unit_stride;
+    ts.summ = 0;
+    if (!ts.active) return ts;
+    const int tid = threadIdx.x;
+    const int b = p / a.B, t = p - (p / a.B) * a.B;
+    if (t == a.B - 1) ts.summ = a.B - 1 <= kSummRows ? 1 : 2;
+    // query rows: for each query row group j the G heads' rows are contiguous
+    constexpr int QPT = (kMaxRows * D * 4 / 16 + kNT - 1) / kNT;  // q vectors per thread at most
+    const int nqv = a.NR * RV, gv = a.G * RV;
+    const uint4* qsrc = reinterpret_cast<const uint4*>(a.q) +
+                        ((size_t)r * a.NQ * a.Hq + (size_t)g * a.G) * RV;
+    const size_t qj = (size_t)a.Hq * RV;
+    uint4 qv[QPT];
+#pragma unroll
+    for (int e = 0; e < QPT; ++e) {
+        const int i = min(tid + e * kNT, nqv - 1);
+        const int j = (i >= gv) + (i >= 2 * gv);  // n_q <= 3
+        qv[e] = qsrc[(size_t)j * qj + (i - j * gv)];
+    }
+    const int kvi = min(tid, RV - 1);
+    const uint4 kx = reinterpret_cast<const uint4*>(a.k_new)[(size_t)u * RV + kvi];
+    const uint4 vx = reinterpret_cast<const uint4*>(a.v_new)[(size_t)u * RV + kvi];
+    constexpr int RPT = (kSummRows * D * 4 / 16 + kNT - 1) / kNT;  // row vectors per thread at most
+    const int nrv = min(a.B - 1, kSummRows) * RV;
+    const uint4* rsrc = reinterpret_cast<const uint4*>(
+        a.kt + ((size_t)u * a.unit_stride + b) * (size_t)a.tile_stride * EB);
+    uint4 rv[RPT];
+#pragma unroll
+    for (int e = 0; e < RPT; ++e) rv[e] = rsrc[min(tid + e * kNT, max(nrv - 1, 0))];
+#pragma unroll
+    for (int e = 0; e < QPT; ++e)
+        if (tid + e * kNT < nqv) q[tid + e * kNT] = qv[e];
+    if (tid < RV) {
+        k[tid] = kx;
+        v[tid] = vx;
+    }
+    if (ts.summ == 1) {
+#pragma unroll
+        for (int e = 0; e < RPT; ++e)
+            if (tid + e * kNT < nrv) rows[tid + e * kNT] = rv[e];
+    }
+    return ts;
+}
+
 // MFMA split (bf16, B % 16 == 0).  Per 16-token sub-tile:
 //   S^T[16 tok][16 rows] = K_sub[16][D] * Q^T  (v_mfma_f32_16x16x32_bf16, q in
 //   registers),
@@ -990,9 +1072,10 @@ __device__ __forceinline__ RowWin row_win(const StepArgs& a, int grp) {
 // 16 tokens) hit 16 distinct bank groups.
 // The 4 waves take sub-tiles round robin and keep their next two sub-tiles in
 // flight in registers while the current one is computed.  P is rounded to bf16.
+// Returns the appended token's stage (TOK; inactive otherwise).
 template <int D, int NRG, bool TOK>
-__device__ void attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& win, LdsCursor& cur,
-                               const AttnFin& F, int* tbl) {
+__device__ TokStage attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& win,
+                                   LdsCursor& cur, const AttnFin& F, int* tbl) {
     constexpr int KB = D / 32;
     constexpr int DB = D / 16;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1021,7 +1104,10 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& w
         }
     }
     // The unit's tile table goes to LDS while the q loads above are in
-    // flight (one round trip for both before the first tile load).
+    // flight (one round trip for both before the first tile load), and so
+    // does an appended token's stage.
+    TokStage ts{};
+    if constexpr (TOK) ts = tok_prefetch<OASIS_BF16, D>(a, u, sp, cur);
     const SplitRange sr = split_range<TOK>(a, u, sp);
     for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
         tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
@@ -1232,6 +1318,7 @@ __device__ void attn_item_mfma(const StepArgs& a, int u, int sp, const RowWin& w
         }
     }
     __syncthreads();
+    return ts;
 }
 
 // VALU split (any dtype and block size): 16-token sub-tiles of K and V staged
@@ -1458,48 +1545,28 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
 // log2(e) * q.k), then its K row and V column go into the active tile, and a
 // block it completes gets its summary (min / max over the B-1 stored rows and
 // the token, as oasis_append_kv computes it; the scan of this launch does not
-// read it, the block being the active one).  Wave w owns rows w, w+4, ...;
-// every load of the tile in the loop happened before.  All loads go out first
-// (one round trip); the state update touches LDS only, so an LDS barrier
-// orders it before the output, and the stores are left in flight (a full
-// barrier would wait for them).
+// read it, the block being the active one).  Inputs come from the item's
+// TokStage.  Wave w owns rows w, w+4, ...; the state update touches LDS only,
+// so an LDS barrier orders it before the output, and the stores are left in
+// flight (a full barrier would wait for them).
 template <int DT, int D>
-__device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
+__device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F, const TokStage& ts) {
     using E = typename Elem<DT>::type;
+    if (!ts.active) return;
     constexpr int PL = (D + 63) / 64;  // dims per lane
-    const int r = u / a.H, g = u - (u / a.H) * a.H;
+    const int r = u / a.H;
     const int p = a.pos[r];
-    if (p < 0 || p / a.B >= a.unit_stride) return;  // no token, or past the store
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t kn = (size_t)u * D;
     constexpr int RW = kMaxRows / (kNT / 64);  // rows per wave at most
     const int b = p / a.B, t = p - (p / a.B) * a.B;
     const size_t tile = ((size_t)u * a.unit_stride + b) * (size_t)a.tile_stride;
-    // completed block: thread d < D reads column d of the stored rows
-    const bool summ = t == a.B - 1 && threadIdx.x < D;
-    float sx[16];
-    if (summ && a.B <= 17) {
-#pragma unroll
-        for (int k = 0; k < 16; ++k)
-            sx[k] = k < a.B - 1 ? load_elem<DT>(a.kt, tile + (size_t)k * D + threadIdx.x) : 0.f;
-    }
-    float kx[PL], vx[PL], qx[RW][PL];
+    float kx[PL], vx[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
         const int d = lane + 64 * i;
-        kx[i] = d < D ? load_elem<DT>(a.k_new, kn + d) : 0.f;
-        vx[i] = d < D ? load_elem<DT>(a.v_new, kn + d) : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < RW; ++k) {
-        const int row = w + k * (kNT / 64);
-        const int j = row / a.G, hh = row - (row / a.G) * a.G;
-        const size_t qo = (((size_t)r * a.NQ + j) * a.Hq + (size_t)g * a.G + hh) * D;
-#pragma unroll
-        for (int i = 0; i < PL; ++i) {
-            const int d = lane + 64 * i;
-            qx[k][i] = (row < a.NR && d < D) ? load_elem<DT>(a.q, qo + d) : 0.f;
-        }
+        kx[i] = d < D ? load_elem<DT>(ts.k, d) : 0.f;
+        vx[i] = d < D ? load_elem<DT>(ts.v, d) : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < RW; ++k) {
@@ -1507,7 +1574,10 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
         if (row >= a.NR) break;
         float part = 0.f;
 #pragma unroll
-        for (int i = 0; i < PL; ++i) part = fmaf(qx[k][i], kx[i], part);
+        for (int i = 0; i < PL; ++i) {
+            const int d = lane + 64 * i;
+            if (d < D) part = fmaf(load_elem<DT>(ts.q, (size_t)row * D + d), kx[i], part);
+        }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off, 64);
         const float z = part * a.scale_log2;
@@ -1527,31 +1597,23 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F) {
     }
     lds_barrier();
     for (int d = threadIdx.x; d < D; d += kNT) {
+        const float knew = load_elem<DT>(ts.k, d);
         reinterpret_cast<E*>(a.kt_w)[tile + (size_t)t * D + d] =
             reinterpret_cast<const E*>(a.k_new)[kn + d];
         reinterpret_cast<E*>(a.vt_w)[tile + (size_t)d * a.B + t] =
             reinterpret_cast<const E*>(a.v_new)[kn + d];
-    }
-    if (summ) {
-        const int d = threadIdx.x;
-        float lo = load_elem<DT>(a.k_new, kn + d), hi = lo;
-        if (a.B <= 17) {
-#pragma unroll
-            for (int k = 0; k < 16; ++k)
-                if (k < a.B - 1) {
-                    lo = fminf(lo, sx[k]);
-                    hi = fmaxf(hi, sx[k]);
-                }
-        } else {
+        if (ts.summ) {
+            float lo = knew, hi = knew;
             for (int j = 0; j < a.B - 1; ++j) {
-                const float x = load_elem<DT>(a.kt, tile + (size_t)j * D + d);
+                const float x = ts.summ == 1 ? load_elem<DT>(ts.rows, (size_t)j * D + d)
+                                             : load_elem<DT>(a.kt, tile + (size_t)j * D + d);
                 lo = fminf(lo, x);
                 hi = fmaxf(hi, x);
             }
+            const size_t so = ((size_t)u * a.n_blk_max + b) * 2 * D + d;
+            store_elem<DT>(a.summ_w, so, lo);
+            store_elem<DT>(a.summ_w, so + D, hi);
         }
-        const size_t so = ((size_t)u * a.n_blk_max + b) * 2 * D + d;
-        store_elem<DT>(a.summ_w, so, lo);
-        store_elem<DT>(a.summ_w, so + D, hi);
     }
 }
 
@@ -1564,18 +1626,19 @@ __device__ void attn_item(const StepArgs& a, int u, int sp, int grp, unsigned ch
     F.m = cur.take<float>(win.nr);
     F.l = cur.take<float>(win.nr);
     F.acc = cur.take<float>((size_t)win.nr * D);
+    TokStage ts{};
     if constexpr (ATT == kAttnMfma) {
-        attn_item_mfma<D, NRG, TOK>(a, u, sp, win, cur, F, tbl);  // stages the table after loading q
+        // stages the table (and the token) after loading q
+        ts = attn_item_mfma<D, NRG, TOK>(a, u, sp, win, cur, F, tbl);
     } else {
+        if constexpr (TOK) ts = tok_prefetch<DT, D>(a, u, sp, cur);
         const SplitRange sr = split_range<TOK>(a, u, sp);
         for (int i = threadIdx.x; i < sr.e1 - sr.e0; i += kNT)
             tbl[i] = a.table[(size_t)u * a.n_sel + sr.e0 + i];
         __syncthreads();
         attn_item_valu<DT, D, TOK>(a, u, sp, cur, F, tbl);
     }
-    if constexpr (TOK) {
-        if (sp == a.S - 1) attn_new_token<DT, D>(a, u, F);
-    }
+    if constexpr (TOK) attn_new_token<DT, D>(a, u, F, ts);
     attn_emit<DT, D>(a, u, sp, win, F);
 }
 

@@ -615,7 +615,9 @@ class PreparedStep:
     the kernel."""
 
     _Q, _STEP, _BI, _SI, _BO, _SO, _INS, _TBL = 1, 13, 9, 10, 11, 12, 16, 23
+    _NBLK = 4
     _KNEW, _VNEW, _POS = 26, 27, 28  # oasis_lookahead_step_append only
+    _TT, _TL = 26, 27                # tail_tile, tail_len of oasis_lookahead_step
 
     def __init__(self, args, res, lib, append=False, no_alloc=False):
         self.args = args
@@ -625,8 +627,13 @@ class PreparedStep:
                       "oasis_lookahead_step_noalloc" if no_alloc else "oasis_lookahead_step")
         self._fn = getattr(lib, self._name)
 
-    def __call__(self, step: int, q: torch.Tensor | None = None, token=None) -> dict:
-        """token: (k_new, v_new, pos) of this step (append form only)."""
+    def __call__(self, step: int, q: torch.Tensor | None = None, token=None,
+                 n_blk: torch.Tensor | None = None, ins_blk: torch.Tensor | None = None,
+                 tail=None) -> dict:
+        """token: (k_new, v_new, pos) of this step (append form only).  n_blk,
+        ins_blk and tail = (tail_tile, tail_len) replace the prepared tensors
+        of those arguments (same shapes and dtypes; each was given at
+        preparation, so its pointer slot exists)."""
         a = self.args
         a[self._STEP] = int(step)
         if q is not None:
@@ -636,6 +643,16 @@ class PreparedStep:
                 raise ValueError("this step was prepared without a new token")
             for i, t in zip((self._KNEW, self._VNEW, self._POS), token):
                 a[i] = ctypes.c_void_p(t.data_ptr())
+        for i, t in ((self._NBLK, n_blk), (self._INS, ins_blk)):
+            if t is not None:
+                if a[i] is None or t.dtype != torch.int32 or not t.is_contiguous():
+                    raise ValueError("prepare the step with this argument first (int32, contiguous)")
+                a[i] = ctypes.c_void_p(t.data_ptr())
+        if tail is not None:
+            if self.append or a[self._TT] is None:
+                raise ValueError("this step was prepared without tail_tile / tail_len")
+            a[self._TT] = ctypes.c_void_p(tail[0].data_ptr())
+            a[self._TL] = ctypes.c_void_p(tail[1].data_ptr())
         st = self._fn(*a)
         if st != 0:
             check(self._name, st)

@@ -35,9 +35,7 @@ plan_kernel(int H, int NQ, int pred_row, int K, const int32_t* __restrict__ topk
 }
 
 static size_t plan_lds_bytes(int K) {
-    const size_t k4 = (size_t)pad4(K);
-    auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
-    return a16(k4 * 4) * 10 + a16(k4 * 8) + a16(64) + a16(48);
+    return ((size_t)pad4(K) * 4 + 15) / 16 * 16 + plan_lds_size(K);  // P, then the plan state
 }
 
 // ------------------------------------------------------------ launching

@@ -199,6 +199,13 @@ struct LdsCursor {
 
 __host__ __device__ inline int pad4(int k) { return (k + 3) & ~3; }
 
+// LDS bytes carve_plan takes.
+__host__ __device__ inline size_t plan_lds_size(int K) {
+    const size_t k4 = (size_t)pad4(K);
+    auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+    return a16(k4 * 4) * 9 + a16(k4 * 8) + a16(24 * 4) + a16(48);
+}
+
 // LDS bytes of a scan item (P/N rows, top-K, plan, and the unit's scores when
 // they stay in LDS), mirrored by the carving in scan_item / finish_kernel.
 __host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_scores) {
@@ -207,7 +214,7 @@ __host__ __device__ inline size_t scan_lds_bytes(int NQ, int D, int K, int n_sco
     size_t b = a16(NQ * 2 * D * 4);                                     // pn
     b += a16(NQ * 512 * 4) + a16(4 * 2 * 4) + a16(16 * 4);             // hist, scan, sh
     b += a16(NQ * kp * 4) * 2 + a16(kp * 4);                            // sel key/idx, P
-    b += a16(kp * 4) * 4 + a16(kp * 8) + a16(kp * 4) * 5 + a16(64) + a16(48);  // plan
+    b += plan_lds_size(K);                                              // plan
     b += a16((size_t)n_scores * 4);                                     // scores
     return b;
 }
@@ -649,6 +656,186 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
     lds_barrier();
 }
 
+// ------------------------------------------------------------ one long row
+// Top-K of one score row of up to kSelKPT * kNT entries in global memory, by
+// one workgroup (the selection launch of split units).  Thread t holds the
+// keys of blocks t, t + 256, ... in registers, loaded straight from memory
+// (coalesced, all in flight).  Each block's key is 64-bit: the order-preserving
+// uint32 of its score above the complement of its block index (13 bits), so
+// every key is distinct and larger means (higher score, then lower block).
+// Radix passes of 8 bits below the bits every key shares narrow the bin of the
+// K-th key until that bin and the bins above hold at most `cmax` keys (one
+// pass on score rows of the measured shapes: ~140-170 keys); those are
+// compacted to LDS and ranked by counting.  Integer work only: exact for the
+// fp32 scores given, ties by ascending block.
+constexpr int kSelKPT = 32;
+constexpr int kSelIdxBits = 13;
+constexpr uint32_t kSelIdxMax = (1u << kSelIdxBits) - 1u;
+static_assert(kSelKPT * kNT == (1 << kSelIdxBits), "one index field per held key");
+constexpr int kSelCandMax = kMaxTopK + 128;  // largest candidate list
+
+struct SelLds {
+    int* hist;                 // [2][256]
+    uint32_t* red;             // [16]
+    int* sh;                   // [4]
+    unsigned long long* cand;  // [kSelCandMax + 2]
+};
+
+__device__ __forceinline__ SelLds carve_sel(LdsCursor& cur) {
+    SelLds L;
+    L.hist = cur.take<int>(512);
+    L.red = cur.take<uint32_t>(16);
+    L.sh = cur.take<int>(4);
+    L.cand = cur.take<unsigned long long>(kSelCandMax + 2);
+    return L;
+}
+__host__ __device__ inline size_t sel_lds_bytes() {
+    return 512 * 4 + 16 * 4 + 16 + (size_t)(kSelCandMax + 2) * 8 + 48;
+}
+
+// Issue the loads of a row's scores (raw bits; no use, so nothing waits yet).
+__device__ __forceinline__ void sel_load(const float* row, int n, uint32_t (&key)[kSelKPT]) {
+    const int last = n > 0 ? n - 1 : 0;
+#pragma unroll
+    for (int q = 0; q < kSelKPT; ++q)
+        key[q] = __float_as_uint(row[min(q * kNT + (int)threadIdx.x, last)]);
+}
+
+// Ranked top-K of the row whose score bits sel_load put in `key`: block
+// indices to orow[0..K) (-1 past n), scores to srow (if any), and the ranked
+// blocks to P (LDS, -1 padded to pad4(K); if any) for the plan.
+__device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int K, int32_t* orow, float* srow,
+                           int* P, const SelLds& L) {
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int Kp = min(K, n);
+    for (int a = max(Kp, 0) + t; a < K; a += kNT) {
+        orow[a] = -1;
+        if (srow) srow[a] = -__builtin_inff();
+    }
+    if (P)
+        for (int a = max(Kp, 0) + t; a < pad4(K); a += kNT) P[a] = -1;
+    if (Kp <= 0) {
+        lds_barrier();
+        return;
+    }
+    const int nv = n > t ? (n - t + kNT - 1) / kNT : 0;  // keys q < nv are blocks < n
+    const uint32_t low0 = kSelIdxMax - (uint32_t)t;     // index field of key 0
+    auto comp = [&](int q) {
+        return ((unsigned long long)key[q] << kSelIdxBits) | (unsigned long long)(low0 - kNT * q);
+    };
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int q = 0; q < kSelKPT; ++q) {
+        key[q] = float_key(__uint_as_float(key[q]));
+        const bool v = q < nv;
+        lo = v && key[q] < lo ? key[q] : lo;
+        hi = v && key[q] > hi ? key[q] : hi;
+    }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+        L.red[wv * 2] = lo;
+        L.red[wv * 2 + 1] = hi;
+    }
+    L.hist[t] = 0;
+    L.hist[kNT + t] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int w = 0; w < kNT / 64; ++w) {
+        lo = L.red[w * 2] < lo ? L.red[w * 2] : lo;
+        hi = L.red[w * 2 + 1] > hi ? L.red[w * 2 + 1] : hi;
+    }
+    const int cmax = min(Kp + 128, kSelCandMax);
+    // Bits below hb are not shared by every key (the index field never is).
+    int hb = (lo == hi ? 0 : 32 - __clz(lo ^ hi)) + kSelIdxBits;
+    unsigned long long mask = ~((1ull << hb) - 1ull);
+    unsigned long long prefix = ((unsigned long long)hi << kSelIdxBits) & mask;
+    int above = 0, remaining = Kp, cnt = n;
+    if (n <= cmax) {
+        prefix = 0ull;  // every block is a candidate
+    } else {
+        int buf = 0;
+        for (;;) {
+            const int w8 = hb < 8 ? hb : 8;
+            const int shift = hb - w8;
+            const uint32_t dm = (1u << w8) - 1u;
+            int* hist = L.hist + buf * kNT;
+#pragma unroll
+            for (int q = 0; q < kSelKPT; ++q) {
+                const unsigned long long c = comp(q);
+                if (q < nv && (c & mask) == prefix) atomicAdd(&hist[(uint32_t)(c >> shift) & dm], 1);
+            }
+            lds_barrier();
+            if (wv == 0) {
+                // lane l holds digits 255-4l .. 252-4l: a prefix over lanes is
+                // a suffix (largest digits first) over digits
+                int c[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) c[e] = hist[255 - (4 * lane + e)];
+                const int local = c[0] + c[1] + c[2] + c[3];
+                int before = (int)wave_incl_sum((uint32_t)local) - local;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (before < remaining && before + c[e] >= remaining) {
+                        L.sh[0] = 255 - (4 * lane + e);
+                        L.sh[1] = before;
+                        L.sh[2] = c[e];
+                    }
+                    before += c[e];
+                }
+            }
+            L.hist[(buf ^ 1) * kNT + t] = 0;  // the next pass's buffer
+            lds_barrier();
+            const int d = L.sh[0], before = L.sh[1];
+            cnt = L.sh[2];
+            prefix |= (unsigned long long)d << shift;
+            mask |= (unsigned long long)dm << shift;
+            hb = shift;
+            above += before;
+            remaining -= before;
+            if (above + cnt <= cmax || hb == 0) break;
+            buf ^= 1;
+        }
+    }
+    // Candidates: every key at or above the bin's lower edge, compacted in
+    // thread order.
+    const int C = n <= cmax ? n : above + cnt;
+    uint32_t cm = 0;
+#pragma unroll
+    for (int q = 0; q < kSelKPT; ++q) cm |= uint32_t(q < nv && comp(q) >= prefix) << q;
+    const uint32_t mine = (uint32_t)__builtin_popcount(cm);
+    const uint32_t inc = wave_incl_sum(mine);
+    if (lane == 63) L.red[8 + wv] = inc;
+    lds_barrier();
+    uint32_t pos = inc - mine;
+#pragma unroll
+    for (int w = 0; w < kNT / 64; ++w) pos += w < wv ? L.red[8 + w] : 0u;
+#pragma unroll
+    for (int q = 0; q < kSelKPT; ++q)
+        if ((cm >> q) & 1u) L.cand[pos++] = comp(q);
+    if (t == 0) L.cand[C] = 0ull;  // pairs are read two at a time; 0 is below every key
+    lds_barrier();
+    // Counting rank among the candidates.
+    const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(L.cand);
+    const int C2 = (C + 1) >> 1;
+    for (int a = t; a < C; a += kNT) {
+        const unsigned long long e = L.cand[a];
+        int rank = 0;
+#pragma unroll 8
+        for (int i = 0; i < C2; ++i) {
+            const ulonglong2 x = c2[i];
+            rank += (x.x > e) + (x.y > e);
+        }
+        if (rank < Kp) {
+            const int bi = (int)(kSelIdxMax - (uint32_t)(e & kSelIdxMax));
+            orow[rank] = bi;
+            if (srow) srow[rank] = key_float((uint32_t)(e >> kSelIdxBits));
+            if (P) P[rank] = bi;
+        }
+    }
+    lds_barrier();
+}
+
 // ============================================================ plan
 struct PlanLds {
     int* blk;      // [K4]
@@ -661,7 +848,10 @@ struct PlanLds {
     int* new_blk;          // [K4]
     int* new_stamp;        // [K4]
     int* rank_of_slot;     // [K4] victim rank of a slot (K for hits)
-    uint32_t* scanbuf;     // [4][2]
+    uint32_t* scanbuf;     // [24]: block scans [0, 12), inserted count [12], empty flags [16, 20)
+    int* order;            // [K4] slots by (stamp, slot) (plan_order; FAST plans only)
+    uint16_t* mark_p;      // [n_blk] rank of a predicted block (FAST plans only; unchecked garbage elsewhere)
+    uint16_t* mark_b;      // [n_blk] slot of a resident block (likewise)
     unsigned long long* ins_key;  // [6]: oldest (stamp, slot) key; slot holding the new block;
                                   // [2..5] each wave's oldest key
 };
@@ -678,9 +868,22 @@ __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
     L.new_blk = cur.take<int>(K4);
     L.new_stamp = cur.take<int>(K4);
     L.rank_of_slot = cur.take<int>(K4);
-    L.scanbuf = cur.take<uint32_t>(16);
+    L.scanbuf = cur.take<uint32_t>(24);
     L.ins_key = cur.take<unsigned long long>(6);
+    L.order = nullptr;
+    L.mark_p = L.mark_b = nullptr;
     return L;
+}
+
+// The FAST plan's extra state: the slot order and the block marks of n_blk blocks.
+__device__ __forceinline__ void carve_plan_fast(LdsCursor& cur, int K4, int n_blk, PlanLds& L) {
+    L.order = cur.take<int>(K4);
+    L.mark_p = cur.take<uint16_t>(n_blk);
+    L.mark_b = cur.take<uint16_t>(n_blk);
+}
+__host__ __device__ inline size_t plan_fast_lds_size(int K, int n_blk) {
+    auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
+    return a16((size_t)pad4(K) * 4) + 2 * a16((size_t)n_blk * 2);
 }
 
 // Stage one unit's slot tables in LDS (no barrier: plan_unit's callers pass
@@ -695,83 +898,176 @@ __device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* 
     }
 }
 
+// Slots in (stamp, slot) order, oldest first (L.order[rank] = slot), and
+// whether any slot is empty (the seeding plan): both depend on the slot tables
+// only, so a FAST plan has them before its predicted list exists.  Needs the
+// staged tables visible (a barrier after plan_load) and leaves a barrier to
+// plan_unit.
+__device__ __forceinline__ void plan_order(int K, const PlanLds& L) {
+    const int tid = threadIdx.x;
+    const int K4 = pad4(K);
+    int empty = 0;
+    for (int s = tid; s < K4; s += kNT) {
+        L.ekey[s] = s < K ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
+                          : 0x7fffffffffffffffLL;
+        empty |= s < K && L.blk[s] == -1;
+    }
+    const bool wave_empty = __ballot(empty) != 0;
+    if ((tid & 63) == 0) L.scanbuf[16 + (tid >> 6)] = wave_empty;
+    lds_barrier();
+    const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
+    for (int s = tid; s < K; s += kNT) {
+        const long long e = L.ekey[s];
+        int r = 0;
+#pragma unroll 8
+        for (int i = 0; i < K4 / 2; ++i) {
+            const longlong2 x = E2[i];
+            r += (x.x < e) + (x.y < e);
+        }
+        L.order[r] = s;
+    }
+}
+
 // Capped least-recently-selected plan of one unit from the ranked predicted
 // list P (LDS, -1 padded) and the staged slot tables, then the insertion of
 // the request's newly completed block `ins` (-1 = none): outside the cap it
 // refreshes its slot if resident, else takes the slot with the smallest
 // (stamp, slot) after the admissions, taking over that slot's admission if it
 // had one.  The outputs may alias the slot tables the stage was loaded from.
+// FAST (after plan_order, block ids below n_blk): membership through marks
+// indexed by block (each list writes its index at its blocks' marks, then a
+// block is in a list iff the entry its mark names holds it, so stale marks
+// are harmless and no atomics are needed), and the victims' order from the
+// slot order by the same block scan as the missing blocks.  Otherwise
+// membership compares every pair and the victims are ranked by counting.
+template <bool FAST = false>
 __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_out, int step,
                           int cap, int ins, int32_t* cnt_out, int32_t* src_out, int32_t* dst_out,
-                          int32_t* ev_out, const PlanLds& L) {
+                          int32_t* ev_out, const PlanLds& L, int n_blk = 0) {
     const int tid = threadIdx.x;
     const int K4 = pad4(K);
-    int empty = 0;
-    for (int s = tid; s < K; s += kNT) empty |= L.blk[s] == -1;
-    const bool wave_empty = __ballot(empty) != 0;
-    if ((tid & 63) == 0) L.scanbuf[8 + (tid >> 6)] = wave_empty;
-    lds_barrier();
-    const int seeding = (L.scanbuf[8] | L.scanbuf[9] | L.scanbuf[10] | L.scanbuf[11]) != 0;
-    // Membership both ways: slot s is a hit if its block is predicted; rank i
-    // is missing if its block is not resident.  Items [0, K) are slots,
-    // [K, 2K) predicted ranks.
-    const int4* P4 = reinterpret_cast<const int4*>(P);
-    const int4* B4 = reinterpret_cast<const int4*>(L.blk);
-    for (int it = tid; it < 2 * K; it += kNT) {
-        const bool slot = it < K;
-        const int idx = slot ? it : it - K;
-        const int v = slot ? L.blk[idx] : P[idx];
-        const int4* other = slot ? P4 : B4;
-        int found = 0;
-        if (v >= 0) {
-#pragma unroll 8
-            for (int i = 0; i < K4 / 4; ++i) {
-                const int4 x = other[i];
-                found |= (x.x == v) | (x.y == v) | (x.z == v) | (x.w == v);
-            }
+    int seeding;
+    if constexpr (FAST) {
+        // Membership both ways through the marks (16-bit stores, one writer
+        // per mark except for blocks held twice, which then agree).
+        for (int it = tid; it < K; it += kNT) {
+            const int pb = P[it], bb = L.blk[it];
+            if (pb >= 0 && pb < n_blk) L.mark_p[pb] = (uint16_t)it;
+            if (bb >= 0 && bb < n_blk) L.mark_b[bb] = (uint16_t)it;
         }
-        if (slot)
-            L.hit[idx] = found;
-        else
-            L.miss[idx] = v >= 0 && !found;
+        lds_barrier();
+        seeding = (L.scanbuf[16] | L.scanbuf[17] | L.scanbuf[18] | L.scanbuf[19]) != 0;
+        for (int it = tid; it < K; it += kNT) {
+            const int bb = L.blk[it];
+            int hit = 0;
+            if (bb >= 0 && bb < n_blk) {
+                const int i = L.mark_p[bb];
+                hit = i < K && P[i] == bb;
+            }
+            L.hit[it] = hit;
+            const int pb = P[it];
+            int found = 0;
+            if (pb >= 0 && pb < n_blk) {
+                const int sl = L.mark_b[pb];
+                found = sl < K && L.blk[sl] == pb;
+            }
+            L.miss[it] = pb >= 0 && !found;
+        }
+        lds_barrier();
+    } else {
+        int empty = 0;
+        for (int s = tid; s < K; s += kNT) empty |= L.blk[s] == -1;
+        const bool wave_empty = __ballot(empty) != 0;
+        if ((tid & 63) == 0) L.scanbuf[16 + (tid >> 6)] = wave_empty;
+        lds_barrier();
+        seeding = (L.scanbuf[16] | L.scanbuf[17] | L.scanbuf[18] | L.scanbuf[19]) != 0;
+        // Membership both ways: slot s is a hit if its block is predicted; rank i
+        // is missing if its block is not resident.  Items [0, K) are slots,
+        // [K, 2K) predicted ranks.
+        const int4* P4 = reinterpret_cast<const int4*>(P);
+        const int4* B4 = reinterpret_cast<const int4*>(L.blk);
+        for (int it = tid; it < 2 * K; it += kNT) {
+            const bool slot = it < K;
+            const int idx = slot ? it : it - K;
+            const int v = slot ? L.blk[idx] : P[idx];
+            const int4* other = slot ? P4 : B4;
+            int found = 0;
+            if (v >= 0) {
+#pragma unroll 8
+                for (int i = 0; i < K4 / 4; ++i) {
+                    const int4 x = other[i];
+                    found |= (x.x == v) | (x.y == v) | (x.z == v) | (x.w == v);
+                }
+            }
+            if (slot)
+                L.hit[idx] = found;
+            else
+                L.miss[idx] = v >= 0 && !found;
+        }
+        lds_barrier();
     }
-    lds_barrier();
-    // Missing blocks in rank order, victims counted.
+    // Missing blocks in rank order, victims counted (FAST: victims in slot
+    // order, so the scan also gives each non-hit slot its victim rank).
     uint32_t n_missing = 0, n_hits = 0;
-    for (int base = 0; base < K; base += kNT) {
-        const int i = base + tid;
-        uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
-        uint32_t ex[2], tot[2];
-        block_scan<2>(v, ex, tot, L.scanbuf);
-        if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
-        n_missing += tot[0];
-        n_hits += tot[1];
-    }
-    for (int s = tid; s < K4; s += kNT)
-        L.ekey[s] = (s < K && !L.hit[s])
-                        ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
-                        : 0x7fffffffffffffffLL;
-    lds_barrier();
-    // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
-    for (int s = tid; s < K; s += kNT) {
-        if (!L.hit[s]) {
-            const long long e = L.ekey[s];
-            int r = 0;
-            const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
-#pragma unroll 8
-            for (int i = 0; i < K4 / 2; ++i) {
-                const longlong2 x = E2[i];
-                r += (x.x < e) + (x.y < e);
+    if constexpr (FAST) {
+        uint32_t n_vict = 0;
+        for (int base = 0; base < K; base += kNT) {
+            const int i = base + tid;
+            const int so = i < K ? L.order[i] : 0;
+            uint32_t v[3] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u,
+                             i < K ? (uint32_t)(L.hit[so] == 0) : 0u};
+            uint32_t ex[3], tot[3];
+            block_scan<3>(v, ex, tot, L.scanbuf);
+            if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
+            if (i < K) {
+                if (v[2]) L.victim_of_rank[n_vict + ex[2]] = so;
+                L.rank_of_slot[so] = v[2] ? (int)(n_vict + ex[2]) : K;
             }
-            L.victim_of_rank[r] = s;
-            L.rank_of_slot[s] = r;
-        } else {
-            L.rank_of_slot[s] = K;
+            n_missing += tot[0];
+            n_hits += tot[1];
+            n_vict += tot[2];
         }
-        L.new_blk[s] = L.blk[s];
-        L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+        for (int s = tid; s < K; s += kNT) {
+            L.new_blk[s] = L.blk[s];
+            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+        }
+        lds_barrier();
+    } else {
+        for (int base = 0; base < K; base += kNT) {
+            const int i = base + tid;
+            uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
+            uint32_t ex[2], tot[2];
+            block_scan<2>(v, ex, tot, L.scanbuf);
+            if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
+            n_missing += tot[0];
+            n_hits += tot[1];
+        }
+        for (int s = tid; s < K4; s += kNT)
+            L.ekey[s] = (s < K && !L.hit[s])
+                            ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
+                            : 0x7fffffffffffffffLL;
+        lds_barrier();
+        // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
+        for (int s = tid; s < K; s += kNT) {
+            if (!L.hit[s]) {
+                const long long e = L.ekey[s];
+                int r = 0;
+                const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
+#pragma unroll 8
+                for (int i = 0; i < K4 / 2; ++i) {
+                    const longlong2 x = E2[i];
+                    r += (x.x < e) + (x.y < e);
+                }
+                L.victim_of_rank[r] = s;
+                L.rank_of_slot[s] = r;
+            } else {
+                L.rank_of_slot[s] = K;
+            }
+            L.new_blk[s] = L.blk[s];
+            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+        }
+        lds_barrier();
     }
-    lds_barrier();
     const int n_victims = K - (int)n_hits;
     int n = min((int)n_missing, n_victims);
     if (!seeding) n = min(n, cap);
@@ -1466,25 +1762,40 @@ __device__ void attn_emit(const StepArgs& a, int u, int sp, const RowWin& win, c
     }
 }
 
-// LSE merge of the S partials of unit u, all loads issued side by side (the
-// partials come from another launch, so each round trip reaches the L2 of
-// another XCD or HBM).  (m, l) pairs lie [s][row], so thread t reads row t % NR
-// of the splits t / NR, t / NR + 256 / NR, ...: coalesced, one round trip.  The
-// per-thread maxima, then the per-thread sums of exp2(m - M) * l, are reduced
-// per row through LDS.  Each output element then sums its splits' weighted
-// accumulators, kMergeBatch splits' loads in flight at a time.
-constexpr int kMergeBatch = 8;  // splits whose partial loads a merge thread keeps in flight
+// LSE merge of the S partials of unit u.  The partials come from another
+// launch, so every round trip reaches the L2 of another XCD or HBM; the merge
+// keeps them few.  Thread t owns 16-byte output pieces t, t + 256, ...; the
+// accumulator loads of its first piece (kMergeBatch splits) are issued before
+// anything else, since they do not depend on the row maxima.  (m, l) pairs lie
+// [s][row], so thread t reads row t % NR of the splits t / NR, t / NR + 256 / NR,
+// ...: coalesced, one round trip; the row maxima, then the sums of
+// exp2(m - M) * l, are reduced per row through LDS, and the weights
+// exp2(m - M) of every (split, row) kept in LDS when they fit (kMergeW).  Each
+// output then sums its splits' weighted accumulators in split order and
+// divides by the row's sum.
+constexpr int kMergeBatch = 16;  // 16-byte accumulator loads a merge thread keeps in flight
+constexpr int kMergeW = 4096;    // (split, row) weights kept in LDS
 
 template <int DT, int D>
 __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, float* Mr, float* Lr,
-                                float* red) {
+                                float* red, float* W) {
     const int tid = threadIdx.x;
     const int NR = win.nr, S = a.S;
+    constexpr int D4 = D / 4;
+    const int n4 = NR * D4;
     const int nsub = kNT / NR;                // threads per row
     const int row_t = tid % NR, sub = tid / NR;
     const size_t ub = (size_t)win.grp * a.U + u;  // this item's partials: [S][NR]
     const float* ml = a.part_ml + ub * S * NR * 2;
+    const float4* pa = reinterpret_cast<const float4*>(a.part_acc + ub * S * NR * D);
     const float ninf = -__builtin_inff();
+    const bool keep_w = S * NR <= kMergeW;
+    float4 v[kMergeBatch];
+    auto load_batch = [&](int o4, int s0) {
+#pragma unroll
+        for (int e = 0; e < kMergeBatch; ++e) v[e] = pa[(size_t)min(s0 + e, S - 1) * n4 + o4];
+    };
+    if (tid < n4) load_batch(tid, 0);
     float mx = ninf;
     if (sub < nsub)
         for (int s = sub; s < S; s += nsub) mx = fmaxf(mx, ml[((size_t)s * NR + row_t) * 2]);
@@ -1499,12 +1810,13 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
     float sm = 0.f;
     if (sub < nsub) {
         const float M = Mr[row_t];
-        if (M != ninf)
-            for (int s = sub; s < S; s += nsub) {
-                const size_t pr = ((size_t)s * NR + row_t) * 2;
-                const float ms = ml[pr];
-                if (ms != ninf) sm += exp2f(ms - M) * ml[pr + 1];
-            }
+        for (int s = sub; s < S; s += nsub) {
+            const size_t pr = ((size_t)s * NR + row_t) * 2;
+            const float ms = ml[pr];
+            const float w = (M != ninf && ms != ninf) ? exp2f(ms - M) : 0.f;
+            if (keep_w) W[s * NR + row_t] = w;
+            if (w != 0.f) sm += w * ml[pr + 1];
+        }
     }
     red[tid] = sm;
     __syncthreads();
@@ -1515,28 +1827,36 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
         const float M = Mr[tid];
         if (a.lse) a.lse[attn_out_row(a, u, win.row0 + tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
     }
-    __syncthreads();  // Mr / Lr ready
-    const int nout = NR * D;
-    const float* pa = a.part_acc + ub * S * NR * D;
-    for (int o = tid; o < nout; o += kNT) {
-        const int row = o / D, d = o - (o / D) * D;
+    __syncthreads();  // Mr / Lr / W ready
+    for (int o4 = tid; o4 < n4; o4 += kNT) {
+        const int row = o4 / D4, d = (o4 - row * D4) * 4;
         const float M = Mr[row], L = Lr[row];
-        float acc = 0.f;
-        if (L > 0.f) {
-            for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
-                float m[kMergeBatch], v[kMergeBatch];
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+            if (s0 > 0 || o4 != tid) load_batch(o4, s0);
 #pragma unroll
-                for (int e = 0; e < kMergeBatch; ++e) {
-                    const bool ok = s0 + e < S;
-                    m[e] = ok ? ml[((size_t)(s0 + e) * NR + row) * 2] : ninf;
-                    v[e] = ok ? pa[(size_t)(s0 + e) * NR * D + o] : 0.f;
+            for (int e = 0; e < kMergeBatch; ++e) {
+                const int sp = s0 + e;
+                float w = 0.f;
+                if (sp < S) {
+                    if (keep_w) {
+                        w = W[sp * NR + row];
+                    } else {
+                        const float ms = ml[((size_t)sp * NR + row) * 2];
+                        w = (M != ninf && ms != ninf) ? exp2f(ms - M) : 0.f;
+                    }
                 }
-#pragma unroll
-                for (int e = 0; e < kMergeBatch; ++e)
-                    if (m[e] != ninf) acc = fmaf(exp2f(m[e] - M), v[e], acc);
+                if (w != 0.f) {
+                    acc[0] = fmaf(w, v[e].x, acc[0]);
+                    acc[1] = fmaf(w, v[e].y, acc[1]);
+                    acc[2] = fmaf(w, v[e].z, acc[2]);
+                    acc[3] = fmaf(w, v[e].w, acc[3]);
+                }
             }
         }
-        store_elem<DT>(a.out, attn_out_row(a, u, win.row0 + row) * D + d, L > 0.f ? acc / L : 0.f);
+        const size_t ob = attn_out_row(a, u, win.row0 + row) * D + d;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) store_elem<DT>(a.out, ob + c, L > 0.f ? acc[c] / L : 0.f);
     }
 }
 
@@ -1699,68 +2019,94 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
         if (k < nu * NQ) {
             const int u = x + 8 * (k / NQ), j = k - (k / NQ) * NQ;
             const int K4 = pad4(a.K);
-            TopkLds T = carve_topk(cur, 1, K4);
-            const PlanLds Pl = carve_plan(cur, K4);
-            T.ek = cur.take<unsigned long long>(K4);
             const bool plan = a.do_plan && j == a.pred_row;
-            if (plan)
-                plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
             const int r = u / a.H, g = u - (u / a.H) * a.H;
             const float* gsc = a.scores + (((size_t)r * NQ + j) * a.H + g) * a.n_blk_max;
             const int n_r = a.n_blk ? min(max(a.n_blk[r], 0), a.n_blk_max) : a.n_blk_max;
-            const float* lsc_row = nullptr;
-            bool padded = false;
-            if (finish_scores_in_lds(a.n_blk_max)) {
-                // The row goes to LDS in coalesced loads, padded for the
-                // selection's conflict-free loads of every key into registers.
-                const int per = max(1, (n_r + kNT - 1) / kNT);
-                float* lsc = cur.take<float>((size_t)a.n_blk_max + kNT);
-                if ((a.n_blk_max & 3) == 0 && (reinterpret_cast<uintptr_t>(gsc) & 15) == 0) {
-                    // 16-byte loads, kStageVec of them in flight per thread
-                    const int n4 = (n_r + 3) >> 2;
-                    const float4* g4 = reinterpret_cast<const float4*>(gsc);
-                    for (int i0 = 0; i0 < n4; i0 += kStageVec * kNT) {
-                        float4 v[kStageVec];
+            const size_t ors = (size_t)a.H * a.K;
+            const size_t ob = (((size_t)r * NQ + j) * a.H + g) * a.K;
+            int* P = cur.take<int>(K4);
+            PlanLds Pl = carve_plan(cur, K4);
+            const bool held = a.n_blk_max <= kSelKPT * kNT;  // the row fits in registers
+            if (held) {
+                // The slot tables' loads, then the scores' (all in flight); the
+                // slot order is formed while the scores arrive.
+                carve_plan_fast(cur, K4, a.n_blk_max, Pl);
+                const SelLds S = carve_sel(cur);
+                if (plan)
+                    plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K,
+                              a.K, Pl);
+                uint32_t key[kSelKPT];
+                sel_load(gsc, n_r, key);
+                if (plan) {
+                    lds_barrier();
+                    plan_order(a.K, Pl);
+                }
+                select_row(key, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
+                           plan ? P : nullptr, S);
+                if (plan) {
+                    const size_t so = (size_t)u * a.K;
+                    plan_unit<true>(P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
+                                    a.ins_blk ? a.ins_blk[r] : -1, a.plan_count + u, a.plan_src + so,
+                                    a.plan_dst + so, a.plan_evicted ? a.plan_evicted + so : nullptr,
+                                    Pl, a.n_blk_max);
+                }
+                return;
+            }
+            if (plan)
+                plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
+            {
+                TopkLds T = carve_topk(cur, 1, K4);
+                T.P = P;
+                T.ek = cur.take<unsigned long long>(K4);
+                const float* lsc_row = nullptr;
+                bool padded = false;
+                if (finish_scores_in_lds(a.n_blk_max)) {
+                    // The row goes to LDS in coalesced loads, padded for the
+                    // selection's conflict-free loads of every key into registers.
+                    const int per = max(1, (n_r + kNT - 1) / kNT);
+                    float* lsc = cur.take<float>((size_t)a.n_blk_max + kNT);
+                    if ((a.n_blk_max & 3) == 0 && (reinterpret_cast<uintptr_t>(gsc) & 15) == 0) {
+                        // 16-byte loads, kStageVec of them in flight per thread
+                        const int n4 = (n_r + 3) >> 2;
+                        const float4* g4 = reinterpret_cast<const float4*>(gsc);
+                        for (int i0 = 0; i0 < n4; i0 += kStageVec * kNT) {
+                            float4 v[kStageVec];
 #pragma unroll
-                        for (int e = 0; e < kStageVec; ++e) {
-                            const int i = i0 + e * kNT + threadIdx.x;
-                            if (i < n4) v[e] = g4[i];
-                        }
+                            for (int e = 0; e < kStageVec; ++e) {
+                                const int i = i0 + e * kNT + threadIdx.x;
+                                if (i < n4) v[e] = g4[i];
+                            }
 #pragma unroll
-                        for (int e = 0; e < kStageVec; ++e) {
-                            const int i = i0 + e * kNT + threadIdx.x;
-                            if (i < n4) {
-                                const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+                            for (int e = 0; e < kStageVec; ++e) {
+                                const int i = i0 + e * kNT + threadIdx.x;
+                                if (i < n4) {
+                                    const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
 #pragma unroll
-                                for (int c = 0; c < 4; ++c) {
-                                    const int bb = 4 * i + c;
-                                    if (bb < n_r) lsc[bb + bb / per] = f[c];
+                                    for (int c = 0; c < 4; ++c) {
+                                        const int bb = 4 * i + c;
+                                        if (bb < n_r) lsc[bb + bb / per] = f[c];
+                                    }
                                 }
                             }
                         }
-                    }
-                } else {
+                    } else {
 #pragma unroll 8
-                    for (int i = threadIdx.x; i < n_r; i += kNT) lsc[i + i / per] = gsc[i];
+                        for (int i = threadIdx.x; i < n_r; i += kNT) lsc[i + i / per] = gsc[i];
+                    }
+                    __syncthreads();
+                    lsc_row = lsc;
+                    padded = true;
                 }
-                __syncthreads();
-                lsc_row = lsc;
-                padded = true;
+                // one call site (rows this long are rare): the row is read
+                // through generic addresses, LDS or global
+                topk_rows<1, kFinishKPT, true>(padded ? lsc_row : gsc, 0, n_r, a.K, a.topk_idx + ob,
+                                               a.topk_score ? a.topk_score + ob : nullptr, ors,
+                                               plan ? 0 : -1, T, padded);
             }
-            const size_t ors = (size_t)a.H * a.K;
-            const size_t ob = (((size_t)r * NQ + j) * a.H + g) * a.K;
-            // two call sites, so the staged row is read with LDS instructions
-            if (padded)
-                topk_rows<1, kFinishKPT, true>(lsc_row, 0, n_r, a.K, a.topk_idx + ob,
-                                               a.topk_score ? a.topk_score + ob : nullptr, ors,
-                                               plan ? 0 : -1, T, true);
-            else
-                topk_rows<1, kFinishKPT, true>(gsc, 0, n_r, a.K, a.topk_idx + ob,
-                                               a.topk_score ? a.topk_score + ob : nullptr, ors,
-                                               plan ? 0 : -1, T, false);
             if (plan) {
                 const size_t so = (size_t)u * a.K;
-                plan_unit(T.P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
+                plan_unit(P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
                           a.ins_blk ? a.ins_blk[r] : -1, a.plan_count + u, a.plan_src + so,
                           a.plan_dst + so, a.plan_evicted ? a.plan_evicted + so : nullptr, Pl);
             }
@@ -1772,18 +2118,22 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
         float* Mr = cur.take<float>(kMaxRows);
         float* Lr = cur.take<float>(kMaxRows);
         float* red = cur.take<float>(kNT);
+        float* W = cur.take<float>(kMergeW);
         const int i = k / a.RGN, grp = k - (k / a.RGN) * a.RGN;
-        attn_merge_unit<DT, D>(a, x + 8 * i, row_win(a, grp), Mr, Lr, red);
+        attn_merge_unit<DT, D>(a, x + 8 * i, row_win(a, grp), Mr, Lr, red, W);
     }
 }
 
 // LDS of finish_kernel: a select item's top-K and plan state (+ its score row
 // when finish_scores_in_lds), a merge item's reduction buffers.
 __host__ __device__ inline size_t finish_lds_bytes(int K, int n_blk_max, bool sel) {
-    const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4;
+    const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4 + kMergeW * 4;
     if (!sel) return m;
-    const size_t s = scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max)) +
-                     ((size_t)pad4(K) * 8 + 15) / 16 * 16;  // rank keys
+    const size_t p = ((size_t)pad4(K) * 4 + 15) / 16 * 16 + plan_lds_size(K);  // P, plan
+    const size_t s = p + (n_blk_max <= kSelKPT * kNT
+                              ? plan_fast_lds_size(K, n_blk_max) + sel_lds_bytes()
+                              : scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max)) +
+                                    ((size_t)pad4(K) * 8 + 15) / 16 * 16);  // top-K state, rank keys
     return s > m ? s : m;
 }
 

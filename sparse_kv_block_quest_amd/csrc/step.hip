@@ -74,11 +74,15 @@ static int launch_finish(const StepArgs& a, hipStream_t st) {
     if (!sel && !mrg) return OASIS_OK;
     const long long grid = 8LL * ((a.U + 7) / 8) * (sel * NQ + mrg * a.RGN);
     if (grid > 0x7fffffffLL) return OASIS_EUNSUPPORTED;
-    const size_t lds = finish_lds_bytes(a.K, a.n_blk_max, sel != 0);
-    auto kern = finish_kernel<DT, D, NQ>;
+    // rows held in registers: wide workgroups (more waves per SIMD for the
+    // latency-bound selection, plan and merge); otherwise kNT threads
+    const bool wide = !sel || a.n_blk_max <= kSelRowMax;
+    const int nt = wide ? kFinishNT : kNT;
+    const size_t lds = finish_lds_bytes(a.K, a.n_blk_max, sel != 0, nt);
+    auto kern = wide ? finish_kernel<DT, D, NQ, kFinishNT> : finish_kernel<DT, D, NQ, kNT>;
     int rc = set_lds(reinterpret_cast<const void*>(kern), lds);
     if (rc != OASIS_OK) return rc;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kNT), lds, st, a, sel, mrg);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(nt), lds, st, a, sel, mrg);
     return launch_status();
 }
 

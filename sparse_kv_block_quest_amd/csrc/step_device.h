@@ -159,9 +159,9 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 }
 
 // Exclusive prefix sums over the workgroup of N values per thread.
-template <int N>
+template <int N, int NT = kNT>
 __device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&excl)[N],
-                                           uint32_t (&total)[N], uint32_t* buf /*[4][N]*/) {
+                                           uint32_t (&total)[N], uint32_t* buf /*[NT / 64][N]*/) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     uint32_t inc[N];
 #pragma unroll
@@ -175,7 +175,7 @@ __device__ __forceinline__ void block_scan(const uint32_t (&v)[N], uint32_t (&ex
     for (int i = 0; i < N; ++i) {
         uint32_t base = 0, tot = 0;
 #pragma unroll
-        for (int ww = 0; ww < kNT / 64; ++ww) {
+        for (int ww = 0; ww < NT / 64; ++ww) {
             const uint32_t x = buf[ww * N + i];
             base += ww < w ? x : 0u;
             tot += x;
@@ -203,7 +203,7 @@ __host__ __device__ inline int pad4(int k) { return (k + 3) & ~3; }
 __host__ __device__ inline size_t plan_lds_size(int K) {
     const size_t k4 = (size_t)pad4(K);
     auto a16 = [](size_t x) { return (x + 15) & ~size_t(15); };
-    return a16(k4 * 4) * 9 + a16(k4 * 8) + a16(24 * 4) + a16(48);
+    return a16(k4 * 4) * 9 + a16(k4 * 8) + a16(80 * 4) + a16(18 * 8);
 }
 
 // LDS bytes of a scan item (P/N rows, top-K, plan, and the unit's scores when
@@ -657,26 +657,27 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
 }
 
 // ------------------------------------------------------------ one long row
-// Top-K of one score row of up to kSelKPT * kNT entries in global memory, by
-// one workgroup (the selection launch of split units).  Thread t holds the
-// keys of blocks t, t + 256, ... in registers, loaded straight from memory
-// (coalesced, all in flight).  Each block's key is 64-bit: the order-preserving
-// uint32 of its score above the complement of its block index (13 bits), so
-// every key is distinct and larger means (higher score, then lower block).
-// Radix passes of 8 bits below the bits every key shares narrow the bin of the
-// K-th key until that bin and the bins above hold at most `cmax` keys (one
-// pass on score rows of the measured shapes: ~140-170 keys); those are
-// compacted to LDS and ranked by counting.  Integer work only: exact for the
-// fp32 scores given, ties by ascending block.
-constexpr int kSelKPT = 32;
+// Top-K of one score row of up to kSelRowMax entries in global memory, by one
+// workgroup of NT threads (the selection launch of split units).  Thread t
+// holds the keys of blocks t, t + NT, ... in registers, loaded straight from
+// memory (coalesced, all in flight).  Each block's key is 64-bit: the
+// order-preserving uint32 of its score above the complement of its block
+// index (13 bits), so every key is distinct and larger means (higher score,
+// then lower block).  Radix passes of 8 bits below the bits every key shares
+// narrow the bin of the K-th key until that bin and the bins above hold at
+// most `cmax` keys (one pass on score rows of the measured shapes: ~140-170
+// keys); those are compacted to LDS and ranked by counting, four adjacent
+// lanes per candidate when the workgroup has them.  Integer work only: exact
+// for the fp32 scores given, ties by ascending block.
 constexpr int kSelIdxBits = 13;
+constexpr int kSelRowMax = 1 << kSelIdxBits;  // longest row held in registers
 constexpr uint32_t kSelIdxMax = (1u << kSelIdxBits) - 1u;
-static_assert(kSelKPT * kNT == (1 << kSelIdxBits), "one index field per held key");
 constexpr int kSelCandMax = kMaxTopK + 128;  // largest candidate list
+constexpr int kFinishNT = 1024;              // threads of a selection-launch workgroup
 
 struct SelLds {
     int* hist;                 // [2][256]
-    uint32_t* red;             // [16]
+    uint32_t* red;             // [64]: per wave (min, max) [0, 32), candidate counts [32, 48)
     int* sh;                   // [4]
     unsigned long long* cand;  // [kSelCandMax + 2]
 };
@@ -684,48 +685,53 @@ struct SelLds {
 __device__ __forceinline__ SelLds carve_sel(LdsCursor& cur) {
     SelLds L;
     L.hist = cur.take<int>(512);
-    L.red = cur.take<uint32_t>(16);
+    L.red = cur.take<uint32_t>(64);
     L.sh = cur.take<int>(4);
     L.cand = cur.take<unsigned long long>(kSelCandMax + 2);
     return L;
 }
 __host__ __device__ inline size_t sel_lds_bytes() {
-    return 512 * 4 + 16 * 4 + 16 + (size_t)(kSelCandMax + 2) * 8 + 48;
+    return 512 * 4 + 64 * 4 + 16 + (size_t)(kSelCandMax + 2) * 8 + 48;
 }
 
 // Issue the loads of a row's scores (raw bits; no use, so nothing waits yet).
-__device__ __forceinline__ void sel_load(const float* row, int n, uint32_t (&key)[kSelKPT]) {
+template <int NT>
+__device__ __forceinline__ void sel_load(const float* row, int n, uint32_t (&key)[kSelRowMax / NT]) {
     const int last = n > 0 ? n - 1 : 0;
 #pragma unroll
-    for (int q = 0; q < kSelKPT; ++q)
-        key[q] = __float_as_uint(row[min(q * kNT + (int)threadIdx.x, last)]);
+    for (int q = 0; q < kSelRowMax / NT; ++q)
+        key[q] = __float_as_uint(row[min(q * NT + (int)threadIdx.x, last)]);
 }
 
 // Ranked top-K of the row whose score bits sel_load put in `key`: block
 // indices to orow[0..K) (-1 past n), scores to srow (if any), and the ranked
 // blocks to P (LDS, -1 padded to pad4(K); if any) for the plan.
-__device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int K, int32_t* orow, float* srow,
-                           int* P, const SelLds& L) {
+template <int NT>
+__device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int n, int K,
+                                           int32_t* orow, float* srow, int* P, const SelLds& L) {
+    constexpr int KPT = kSelRowMax / NT;
+    constexpr int NW = NT / 64;
+    static_assert(KPT * NT == kSelRowMax && NT >= 256, "one index field per held key");
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int Kp = min(K, n);
-    for (int a = max(Kp, 0) + t; a < K; a += kNT) {
+    for (int a = max(Kp, 0) + t; a < K; a += NT) {
         orow[a] = -1;
         if (srow) srow[a] = -__builtin_inff();
     }
     if (P)
-        for (int a = max(Kp, 0) + t; a < pad4(K); a += kNT) P[a] = -1;
+        for (int a = max(Kp, 0) + t; a < pad4(K); a += NT) P[a] = -1;
     if (Kp <= 0) {
         lds_barrier();
         return;
     }
-    const int nv = n > t ? (n - t + kNT - 1) / kNT : 0;  // keys q < nv are blocks < n
-    const uint32_t low0 = kSelIdxMax - (uint32_t)t;     // index field of key 0
+    const int nv = n > t ? (n - t + NT - 1) / NT : 0;  // keys q < nv are blocks < n
+    const uint32_t low0 = kSelIdxMax - (uint32_t)t;   // index field of key 0
     auto comp = [&](int q) {
-        return ((unsigned long long)key[q] << kSelIdxBits) | (unsigned long long)(low0 - kNT * q);
+        return ((unsigned long long)key[q] << kSelIdxBits) | (unsigned long long)(low0 - NT * q);
     };
     uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int q = 0; q < kSelKPT; ++q) {
+    for (int q = 0; q < KPT; ++q) {
         key[q] = float_key(__uint_as_float(key[q]));
         const bool v = q < nv;
         lo = v && key[q] < lo ? key[q] : lo;
@@ -737,11 +743,10 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int 
         L.red[wv * 2] = lo;
         L.red[wv * 2 + 1] = hi;
     }
-    L.hist[t] = 0;
-    L.hist[kNT + t] = 0;
+    for (int i = t; i < 512; i += NT) L.hist[i] = 0;
     lds_barrier();
 #pragma unroll
-    for (int w = 0; w < kNT / 64; ++w) {
+    for (int w = 0; w < NW; ++w) {
         lo = L.red[w * 2] < lo ? L.red[w * 2] : lo;
         hi = L.red[w * 2 + 1] > hi ? L.red[w * 2 + 1] : hi;
     }
@@ -759,11 +764,21 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int 
             const int w8 = hb < 8 ? hb : 8;
             const int shift = hb - w8;
             const uint32_t dm = (1u << w8) - 1u;
-            int* hist = L.hist + buf * kNT;
+            int* hist = L.hist + buf * 256;
+            if (shift >= kSelIdxBits) {
+                // digits and prefix in the score bits: 32-bit work
+                const int ks = shift - kSelIdxBits;
+                const uint32_t m32 = (uint32_t)(mask >> kSelIdxBits);
+                const uint32_t p32 = (uint32_t)(prefix >> kSelIdxBits);
 #pragma unroll
-            for (int q = 0; q < kSelKPT; ++q) {
-                const unsigned long long c = comp(q);
-                if (q < nv && (c & mask) == prefix) atomicAdd(&hist[(uint32_t)(c >> shift) & dm], 1);
+                for (int q = 0; q < KPT; ++q)
+                    if (q < nv && (key[q] & m32) == p32) atomicAdd(&hist[(key[q] >> ks) & dm], 1);
+            } else {
+#pragma unroll
+                for (int q = 0; q < KPT; ++q) {
+                    const unsigned long long c = comp(q);
+                    if (q < nv && (c & mask) == prefix) atomicAdd(&hist[(uint32_t)(c >> shift) & dm], 1);
+                }
             }
             lds_barrier();
             if (wv == 0) {
@@ -784,7 +799,7 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int 
                     before += c[e];
                 }
             }
-            L.hist[(buf ^ 1) * kNT + t] = 0;  // the next pass's buffer
+            for (int i = t; i < 256; i += NT) L.hist[(buf ^ 1) * 256 + i] = 0;  // next pass's buffer
             lds_barrier();
             const int d = L.sh[0], before = L.sh[1];
             cnt = L.sh[2];
@@ -801,36 +816,59 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelKPT], int n, int 
     // thread order.
     const int C = n <= cmax ? n : above + cnt;
     uint32_t cm = 0;
+    if ((prefix & kSelIdxMax) == 0) {  // the edge has no index bits: compare scores only
+        const uint32_t p32 = (uint32_t)(prefix >> kSelIdxBits);
 #pragma unroll
-    for (int q = 0; q < kSelKPT; ++q) cm |= uint32_t(q < nv && comp(q) >= prefix) << q;
+        for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && key[q] >= p32) << q;
+    } else {
+#pragma unroll
+        for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && comp(q) >= prefix) << q;
+    }
     const uint32_t mine = (uint32_t)__builtin_popcount(cm);
     const uint32_t inc = wave_incl_sum(mine);
-    if (lane == 63) L.red[8 + wv] = inc;
+    if (lane == 63) L.red[32 + wv] = inc;
     lds_barrier();
     uint32_t pos = inc - mine;
 #pragma unroll
-    for (int w = 0; w < kNT / 64; ++w) pos += w < wv ? L.red[8 + w] : 0u;
+    for (int w = 0; w < NW; ++w) pos += w < wv ? L.red[32 + w] : 0u;
 #pragma unroll
-    for (int q = 0; q < kSelKPT; ++q)
+    for (int q = 0; q < KPT; ++q)
         if ((cm >> q) & 1u) L.cand[pos++] = comp(q);
     if (t == 0) L.cand[C] = 0ull;  // pairs are read two at a time; 0 is below every key
     lds_barrier();
     // Counting rank among the candidates.
     const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(L.cand);
     const int C2 = (C + 1) >> 1;
-    for (int a = t; a < C; a += kNT) {
-        const unsigned long long e = L.cand[a];
-        int rank = 0;
-#pragma unroll 8
-        for (int i = 0; i < C2; ++i) {
-            const ulonglong2 x = c2[i];
-            rank += (x.x > e) + (x.y > e);
-        }
+    auto emit = [&](unsigned long long e, int rank) {
         if (rank < Kp) {
             const int bi = (int)(kSelIdxMax - (uint32_t)(e & kSelIdxMax));
             orow[rank] = bi;
             if (srow) srow[rank] = key_float((uint32_t)(e >> kSelIdxBits));
             if (P) P[rank] = bi;
+        }
+    };
+    if (4 * C <= NT) {
+        // lanes 4a .. 4a+3 rank candidate a, each over every fourth pair
+        const int a = t >> 2, part = t & 3;
+        const unsigned long long e = L.cand[a < C ? a : 0];
+        int rank = 0;
+        for (int i = part; i < C2; i += 4) {
+            const ulonglong2 x = c2[i];
+            rank += (x.x > e) + (x.y > e);
+        }
+        rank += __shfl_xor(rank, 1, 64);
+        rank += __shfl_xor(rank, 2, 64);
+        if (a < C && part == 0) emit(e, rank);
+    } else {
+        for (int a = t; a < C; a += NT) {
+            const unsigned long long e = L.cand[a];
+            int rank = 0;
+#pragma unroll 8
+            for (int i = 0; i < C2; ++i) {
+                const ulonglong2 x = c2[i];
+                rank += (x.x > e) + (x.y > e);
+            }
+            emit(e, rank);
         }
     }
     lds_barrier();
@@ -848,12 +886,12 @@ struct PlanLds {
     int* new_blk;          // [K4]
     int* new_stamp;        // [K4]
     int* rank_of_slot;     // [K4] victim rank of a slot (K for hits)
-    uint32_t* scanbuf;     // [24]: block scans [0, 12), inserted count [12], empty flags [16, 20)
+    uint32_t* scanbuf;     // [80]: block scans [0, 48), inserted count [48], empty flags [56, 72)
     int* order;            // [K4] slots by (stamp, slot) (plan_order; FAST plans only)
     uint16_t* mark_p;      // [n_blk] rank of a predicted block (FAST plans only; unchecked garbage elsewhere)
     uint16_t* mark_b;      // [n_blk] slot of a resident block (likewise)
-    unsigned long long* ins_key;  // [6]: oldest (stamp, slot) key; slot holding the new block;
-                                  // [2..5] each wave's oldest key
+    unsigned long long* ins_key;  // [18]: oldest (stamp, slot) key; slot holding the new block;
+                                  // [2, 2 + waves) each wave's oldest key
 };
 
 __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
@@ -868,8 +906,8 @@ __device__ __forceinline__ PlanLds carve_plan(LdsCursor& cur, int K4) {
     L.new_blk = cur.take<int>(K4);
     L.new_stamp = cur.take<int>(K4);
     L.rank_of_slot = cur.take<int>(K4);
-    L.scanbuf = cur.take<uint32_t>(24);
-    L.ins_key = cur.take<unsigned long long>(6);
+    L.scanbuf = cur.take<uint32_t>(80);
+    L.ins_key = cur.take<unsigned long long>(18);
     L.order = nullptr;
     L.mark_p = L.mark_b = nullptr;
     return L;
@@ -889,10 +927,11 @@ __host__ __device__ inline size_t plan_fast_lds_size(int K, int n_blk) {
 // Stage one unit's slot tables in LDS (no barrier: plan_unit's callers pass
 // at least one before plan_unit reads them).  Issued early, so the loads
 // overlap other work.
+template <int NT = kNT>
 __device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* stamp_in, int K,
                                           const PlanLds& L) {
     const int K4 = pad4(K);
-    for (int s = threadIdx.x; s < K4; s += kNT) {
+    for (int s = threadIdx.x; s < K4; s += NT) {
         L.blk[s] = s < K ? blk_in[s] : -1;
         L.stamp[s] = s < K ? stamp_in[s] : 0;
     }
@@ -902,21 +941,40 @@ __device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* 
 // whether any slot is empty (the seeding plan): both depend on the slot tables
 // only, so a FAST plan has them before its predicted list exists.  Needs the
 // staged tables visible (a barrier after plan_load) and leaves a barrier to
-// plan_unit.
+// plan_unit.  With NT >= 4 * K, four adjacent lanes count one slot's rank,
+// each over a quarter of the keys.
+template <int NT = kNT>
 __device__ __forceinline__ void plan_order(int K, const PlanLds& L) {
     const int tid = threadIdx.x;
     const int K4 = pad4(K);
     int empty = 0;
-    for (int s = tid; s < K4; s += kNT) {
+    for (int s = tid; s < K4; s += NT) {
         L.ekey[s] = s < K ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
                           : 0x7fffffffffffffffLL;
         empty |= s < K && L.blk[s] == -1;
     }
     const bool wave_empty = __ballot(empty) != 0;
-    if ((tid & 63) == 0) L.scanbuf[16 + (tid >> 6)] = wave_empty;
+    if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
     lds_barrier();
     const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
-    for (int s = tid; s < K; s += kNT) {
+    if (NT >= 4 * K4) {
+        const int s = tid >> 2, part = tid & 3;
+        const int q = K4 / 8;  // pairs per quarter; the last quarter takes the rest
+        const int i0 = part * q, i1 = part == 3 ? K4 / 2 : i0 + q;
+        int r = 0;
+        if (s < K) {
+            const long long e = L.ekey[s];
+            for (int i = i0; i < i1; ++i) {
+                const longlong2 x = E2[i];
+                r += (x.x < e) + (x.y < e);
+            }
+        }
+        r += __shfl_xor(r, 1, 64);
+        r += __shfl_xor(r, 2, 64);
+        if (s < K && part == 0) L.order[r] = s;
+        return;
+    }
+    for (int s = tid; s < K; s += NT) {
         const long long e = L.ekey[s];
         int r = 0;
 #pragma unroll 8
@@ -940,24 +998,24 @@ __device__ __forceinline__ void plan_order(int K, const PlanLds& L) {
 // are harmless and no atomics are needed), and the victims' order from the
 // slot order by the same block scan as the missing blocks.  Otherwise
 // membership compares every pair and the victims are ranked by counting.
-template <bool FAST = false>
+template <bool FAST = false, int NT = kNT>
 __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_out, int step,
                           int cap, int ins, int32_t* cnt_out, int32_t* src_out, int32_t* dst_out,
                           int32_t* ev_out, const PlanLds& L, int n_blk = 0) {
     const int tid = threadIdx.x;
     const int K4 = pad4(K);
-    int seeding;
+    int seeding = 0;
     if constexpr (FAST) {
         // Membership both ways through the marks (16-bit stores, one writer
         // per mark except for blocks held twice, which then agree).
-        for (int it = tid; it < K; it += kNT) {
+        for (int it = tid; it < K; it += NT) {
             const int pb = P[it], bb = L.blk[it];
             if (pb >= 0 && pb < n_blk) L.mark_p[pb] = (uint16_t)it;
             if (bb >= 0 && bb < n_blk) L.mark_b[bb] = (uint16_t)it;
         }
         lds_barrier();
-        seeding = (L.scanbuf[16] | L.scanbuf[17] | L.scanbuf[18] | L.scanbuf[19]) != 0;
-        for (int it = tid; it < K; it += kNT) {
+        for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
+        for (int it = tid; it < K; it += NT) {
             const int bb = L.blk[it];
             int hit = 0;
             if (bb >= 0 && bb < n_blk) {
@@ -976,17 +1034,17 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
         lds_barrier();
     } else {
         int empty = 0;
-        for (int s = tid; s < K; s += kNT) empty |= L.blk[s] == -1;
+        for (int s = tid; s < K; s += NT) empty |= L.blk[s] == -1;
         const bool wave_empty = __ballot(empty) != 0;
-        if ((tid & 63) == 0) L.scanbuf[16 + (tid >> 6)] = wave_empty;
+        if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
         lds_barrier();
-        seeding = (L.scanbuf[16] | L.scanbuf[17] | L.scanbuf[18] | L.scanbuf[19]) != 0;
+        for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
         // Membership both ways: slot s is a hit if its block is predicted; rank i
         // is missing if its block is not resident.  Items [0, K) are slots,
         // [K, 2K) predicted ranks.
         const int4* P4 = reinterpret_cast<const int4*>(P);
         const int4* B4 = reinterpret_cast<const int4*>(L.blk);
-        for (int it = tid; it < 2 * K; it += kNT) {
+        for (int it = tid; it < 2 * K; it += NT) {
             const bool slot = it < K;
             const int idx = slot ? it : it - K;
             const int v = slot ? L.blk[idx] : P[idx];
@@ -1010,14 +1068,58 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     // order, so the scan also gives each non-hit slot its victim rank).
     uint32_t n_missing = 0, n_hits = 0;
     if constexpr (FAST) {
+      if (K <= 256) {
+        // One wave: lane l takes items 4l .. 4l+3 (predicted ranks, slots,
+        // slots in (stamp, slot) order); the others wait at the barrier.
+        if (tid < 64) {
+            uint32_t f0[4], f1[4], f2[4];
+            int so[4];
+            uint32_t c0 = 0, c1 = 0, c2 = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * tid + e;
+                const bool ok = i < K;
+                so[e] = ok ? L.order[i] : 0;
+                f0[e] = ok ? (uint32_t)L.miss[i] : 0u;
+                f1[e] = ok ? (uint32_t)L.hit[i] : 0u;
+                f2[e] = ok ? (uint32_t)(L.hit[so[e]] == 0) : 0u;
+                c0 += f0[e];
+                c1 += f1[e];
+                c2 += f2[e];
+            }
+            const uint32_t i0 = wave_incl_sum(c0), i1 = wave_incl_sum(c1), i2 = wave_incl_sum(c2);
+            uint32_t e0 = i0 - c0, e2 = i2 - c2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * tid + e;
+                if (f0[e]) L.missing_of_rank[e0++] = P[i];
+                if (i < K) {
+                    if (f2[e]) L.victim_of_rank[e2] = so[e];
+                    L.rank_of_slot[so[e]] = f2[e] ? (int)e2 : K;
+                    e2 += f2[e];
+                }
+            }
+            if (tid == 63) {
+                L.scanbuf[0] = i0;
+                L.scanbuf[1] = i1;
+            }
+        }
+        for (int s = tid; s < K; s += NT) {
+            L.new_blk[s] = L.blk[s];
+            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+        }
+        lds_barrier();
+        n_missing = L.scanbuf[0];
+        n_hits = L.scanbuf[1];
+      } else {
         uint32_t n_vict = 0;
-        for (int base = 0; base < K; base += kNT) {
+        for (int base = 0; base < K; base += NT) {
             const int i = base + tid;
             const int so = i < K ? L.order[i] : 0;
             uint32_t v[3] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u,
                              i < K ? (uint32_t)(L.hit[so] == 0) : 0u};
             uint32_t ex[3], tot[3];
-            block_scan<3>(v, ex, tot, L.scanbuf);
+            block_scan<3, NT>(v, ex, tot, L.scanbuf);
             if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
             if (i < K) {
                 if (v[2]) L.victim_of_rank[n_vict + ex[2]] = so;
@@ -1027,28 +1129,29 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
             n_hits += tot[1];
             n_vict += tot[2];
         }
-        for (int s = tid; s < K; s += kNT) {
+        for (int s = tid; s < K; s += NT) {
             L.new_blk[s] = L.blk[s];
             L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
         }
         lds_barrier();
+      }
     } else {
-        for (int base = 0; base < K; base += kNT) {
+        for (int base = 0; base < K; base += NT) {
             const int i = base + tid;
             uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
             uint32_t ex[2], tot[2];
-            block_scan<2>(v, ex, tot, L.scanbuf);
+            block_scan<2, NT>(v, ex, tot, L.scanbuf);
             if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
             n_missing += tot[0];
             n_hits += tot[1];
         }
-        for (int s = tid; s < K4; s += kNT)
+        for (int s = tid; s < K4; s += NT)
             L.ekey[s] = (s < K && !L.hit[s])
                             ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
                             : 0x7fffffffffffffffLL;
         lds_barrier();
         // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
-        for (int s = tid; s < K; s += kNT) {
+        for (int s = tid; s < K; s += NT) {
             if (!L.hit[s]) {
                 const long long e = L.ekey[s];
                 int r = 0;
@@ -1071,7 +1174,7 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     const int n_victims = K - (int)n_hits;
     int n = min((int)n_missing, n_victims);
     if (!seeding) n = min(n, cap);
-    for (int i = tid; i < n; i += kNT) {
+    for (int i = tid; i < n; i += NT) {
         const int dst = L.victim_of_rank[i];
         L.new_blk[dst] = L.missing_of_rank[i];
         L.new_stamp[dst] = step;
@@ -1081,9 +1184,9 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     if (ins >= 0) {  // uniform: one value per request
         // The oldest (stamp, slot) after the admissions: a minimum per thread,
         // per wave (DPP, high words first, then the low words of the lanes
-        // holding the smallest high word), then over the 4 waves.
+        // holding the smallest high word), then over the waves.
         unsigned long long best = ~0ull;
-        for (int s = tid; s < K; s += kNT) {
+        for (int s = tid; s < K; s += NT) {
             // Stamps are >= -1: the offset keeps the unsigned order of (stamp, slot).
             const unsigned long long key =
                 ((unsigned long long)((long long)L.new_stamp[s] + 0x80000000LL) << 32) | (unsigned)s;
@@ -1098,7 +1201,7 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
         if (tid == 0) {
             unsigned long long oldest = L.ins_key[2];
 #pragma unroll
-            for (int ww = 1; ww < kNT / 64; ++ww)
+            for (int ww = 1; ww < NT / 64; ++ww)
                 oldest = L.ins_key[2 + ww] < oldest ? L.ins_key[2 + ww] : oldest;
             L.ins_key[0] = oldest;
             const unsigned long long at = L.ins_key[1];
@@ -1117,12 +1220,12 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
                 L.new_blk[v] = ins;
                 L.new_stamp[v] = step;
             }
-            L.scanbuf[12] = (uint32_t)n;
+            L.scanbuf[48] = (uint32_t)n;
         }
         lds_barrier();
-        n = (int)L.scanbuf[12];
+        n = (int)L.scanbuf[48];
     }
-    for (int i = tid; i < K; i += kNT) {
+    for (int i = tid; i < K; i += NT) {
         if (i < n) {
             const int dst = L.victim_of_rank[i];
             src_out[i] = L.missing_of_rank[i];
@@ -1134,7 +1237,7 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
             if (ev_out) ev_out[i] = -1;
         }
     }
-    for (int s = tid; s < K; s += kNT) {
+    for (int s = tid; s < K; s += NT) {
         blk_out[s] = L.new_blk[s];
         stamp_out[s] = L.new_stamp[s];
     }
@@ -1764,38 +1867,49 @@ __device__ void attn_emit(const StepArgs& a, int u, int sp, const RowWin& win, c
 
 // LSE merge of the S partials of unit u.  The partials come from another
 // launch, so every round trip reaches the L2 of another XCD or HBM; the merge
-// keeps them few.  Thread t owns 16-byte output pieces t, t + 256, ...; the
-// accumulator loads of its first piece (kMergeBatch splits) are issued before
-// anything else, since they do not depend on the row maxima.  (m, l) pairs lie
-// [s][row], so thread t reads row t % NR of the splits t / NR, t / NR + 256 / NR,
-// ...: coalesced, one round trip; the row maxima, then the sums of
-// exp2(m - M) * l, are reduced per row through LDS, and the weights
-// exp2(m - M) of every (split, row) kept in LDS when they fit (kMergeW).  Each
-// output then sums its splits' weighted accumulators in split order and
-// divides by the row's sum.
+// keeps them few.  Four adjacent threads own a 16-byte output piece, each a
+// quarter of the splits; the accumulator loads of their first piece are
+// issued before anything else, since they do not depend on the row maxima.
+// (m, l) pairs lie [s][row], so thread t reads row t % NR of the splits
+// t / NR, t / NR + NT / NR, ...: coalesced, one round trip; the row maxima,
+// then the sums of exp2(m - M) * l, are reduced per row through LDS, and the
+// weights exp2(m - M) of every (split, row) kept in LDS when they fit
+// (kMergeW).  Each output then sums its splits' weighted accumulators (in
+// split order within a quarter, the quarters as (0 + 1) + (2 + 3)) and divides
+// by the row's sum.
 constexpr int kMergeBatch = 16;  // 16-byte accumulator loads a merge thread keeps in flight
 constexpr int kMergeW = 4096;    // (split, row) weights kept in LDS
 
-template <int DT, int D>
+template <int DT, int D, int NT = kNT>
 __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, float* Mr, float* Lr,
                                 float* red, float* W) {
     const int tid = threadIdx.x;
     const int NR = win.nr, S = a.S;
     constexpr int D4 = D / 4;
     const int n4 = NR * D4;
-    const int nsub = kNT / NR;                // threads per row
+    const int nsub = NT / NR;                 // threads per row
+    const int nred = min(nsub, S);            // of those, the ones holding a split
     const int row_t = tid % NR, sub = tid / NR;
     const size_t ub = (size_t)win.grp * a.U + u;  // this item's partials: [S][NR]
     const float* ml = a.part_ml + ub * S * NR * 2;
     const float4* pa = reinterpret_cast<const float4*>(a.part_acc + ub * S * NR * D);
     const float ninf = -__builtin_inff();
     const bool keep_w = S * NR <= kMergeW;
-    float4 v[kMergeBatch];
+    // Four adjacent threads share an output piece, each summing a contiguous
+    // range of `per` splits; the ranges are then added in a fixed tree.  The
+    // order depends on S only, so stacked rows merge exactly as single rows.
+    constexpr int tpo = 4;
+    const int per = (S + tpo - 1) / tpo;
+    const int part = tid % tpo;
+    const int s_lo = min(part * per, S), s_hi = min(s_lo + per, S);
+    constexpr int MB = NT >= 1024 ? kMergeBatch / 2 : kMergeBatch;  // within 128 VGPRs at 1024
+    float4 v[MB];
     auto load_batch = [&](int o4, int s0) {
 #pragma unroll
-        for (int e = 0; e < kMergeBatch; ++e) v[e] = pa[(size_t)min(s0 + e, S - 1) * n4 + o4];
+        for (int e = 0; e < MB; ++e)
+            v[e] = pa[(size_t)max(min(s0 + e, s_hi - 1), 0) * n4 + o4];
     };
-    if (tid < n4) load_batch(tid, 0);
+    if (tid / tpo < n4) load_batch(tid / tpo, s_lo);
     float mx = ninf;
     if (sub < nsub)
         for (int s = sub; s < S; s += nsub) mx = fmaxf(mx, ml[((size_t)s * NR + row_t) * 2]);
@@ -1803,7 +1917,7 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
     __syncthreads();
     if (tid < NR) {
         float M = ninf;
-        for (int k = 0; k < nsub; ++k) M = fmaxf(M, red[tid + k * NR]);
+        for (int k = 0; k < nred; ++k) M = fmaxf(M, red[tid + k * NR]);
         Mr[tid] = M;
     }
     __syncthreads();
@@ -1822,23 +1936,24 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
     __syncthreads();
     if (tid < NR) {
         float L = 0.f;
-        for (int k = 0; k < nsub; ++k) L += red[tid + k * NR];
+        for (int k = 0; k < nred; ++k) L += red[tid + k * NR];
         Lr[tid] = L;
         const float M = Mr[tid];
         if (a.lse) a.lse[attn_out_row(a, u, win.row0 + tid)] = L > 0.f ? (M + log2f(L)) * kLn2 : ninf;
     }
     __syncthreads();  // Mr / Lr / W ready
-    for (int o4 = tid; o4 < n4; o4 += kNT) {
+    // Every thread of a group runs the same iterations (the shuffles below).
+    for (int o4 = tid / tpo; o4 < n4; o4 += NT / tpo) {
         const int row = o4 / D4, d = (o4 - row * D4) * 4;
         const float M = Mr[row], L = Lr[row];
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
-            if (s0 > 0 || o4 != tid) load_batch(o4, s0);
+        for (int s0 = s_lo; s0 < s_hi; s0 += MB) {
+            if (s0 > s_lo || o4 != tid / tpo) load_batch(o4, s0);
 #pragma unroll
-            for (int e = 0; e < kMergeBatch; ++e) {
+            for (int e = 0; e < MB; ++e) {
                 const int sp = s0 + e;
                 float w = 0.f;
-                if (sp < S) {
+                if (sp < s_hi) {
                     if (keep_w) {
                         w = W[sp * NR + row];
                     } else {
@@ -1854,9 +1969,19 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
                 }
             }
         }
-        const size_t ob = attn_out_row(a, u, win.row0 + row) * D + d;
+        // ranges in order: (0 + 1) + (2 + 3)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) store_elem<DT>(a.out, ob + c, L > 0.f ? acc[c] / L : 0.f);
+        for (int c = 0; c < 4; ++c) {
+            float o = __shfl_xor(acc[c], 1, 64);
+            acc[c] = (part & 1) ? o + acc[c] : acc[c] + o;
+            o = __shfl_xor(acc[c], 2, 64);
+            acc[c] = (part & 2) ? o + acc[c] : acc[c] + o;
+        }
+        if (part == 0) {
+            const size_t ob = attn_out_row(a, u, win.row0 + row) * D + d;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) store_elem<DT>(a.out, ob + c, L > 0.f ? acc[c] / L : 0.f);
+        }
     }
 }
 
@@ -2004,9 +2129,10 @@ __host__ __device__ inline size_t finish_scores_lds(int n_blk_max) {
 // Second launch for split units: top-K (+ plan) from the global scores when
 // NC > 1 (`select` items, one per unit and scored row), LSE merge of the
 // attention partials when S > 1 (`merge` items, one per unit and row group).
-// Same XCD mapping as the main launch.
-template <int DT, int D, int NQ>
-__global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_items, int merge_items) {
+// Same XCD mapping as the main launch.  NT = kFinishNT when every row fits
+// in registers (n_blk_max <= kSelRowMax), else kNT (rows staged or re-read).
+template <int DT, int D, int NQ, int NT>
+__global__ void __launch_bounds__(NT) finish_kernel(StepArgs a, int select_items, int merge_items) {
     extern __shared__ __align__(16) unsigned char lds[];
     const int w = blockIdx.x;
     const int x = w & 7;
@@ -2014,7 +2140,7 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
     const int nu = a.U > x ? (a.U - x + 7) / 8 : 0;
     LdsCursor cur{lds};
     if (select_items) {
-        // One item per (unit, scored row): the row's 256 threads hold its keys;
+        // One item per (unit, scored row): the row's NT threads hold its keys;
         // the item of row pred_row also plans the unit.
         if (k < nu * NQ) {
             const int u = x + 8 * (k / NQ), j = k - (k / NQ) * NQ;
@@ -2027,32 +2153,31 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
             const size_t ob = (((size_t)r * NQ + j) * a.H + g) * a.K;
             int* P = cur.take<int>(K4);
             PlanLds Pl = carve_plan(cur, K4);
-            const bool held = a.n_blk_max <= kSelKPT * kNT;  // the row fits in registers
-            if (held) {
+            if constexpr (NT != kNT) {
                 // The slot tables' loads, then the scores' (all in flight); the
                 // slot order is formed while the scores arrive.
                 carve_plan_fast(cur, K4, a.n_blk_max, Pl);
                 const SelLds S = carve_sel(cur);
                 if (plan)
-                    plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K,
-                              a.K, Pl);
-                uint32_t key[kSelKPT];
-                sel_load(gsc, n_r, key);
+                    plan_load<NT>(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K,
+                                  a.K, Pl);
+                uint32_t key[kSelRowMax / NT];
+                sel_load<NT>(gsc, n_r, key);
                 if (plan) {
                     lds_barrier();
-                    plan_order(a.K, Pl);
+                    plan_order<NT>(a.K, Pl);
                 }
-                select_row(key, n_r, a.K, a.topk_idx + ob, a.topk_score ? a.topk_score + ob : nullptr,
-                           plan ? P : nullptr, S);
+                select_row<NT>(key, n_r, a.K, a.topk_idx + ob,
+                               a.topk_score ? a.topk_score + ob : nullptr, plan ? P : nullptr, S);
                 if (plan) {
                     const size_t so = (size_t)u * a.K;
-                    plan_unit<true>(P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
+                    plan_unit<true, NT>(P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,
                                     a.ins_blk ? a.ins_blk[r] : -1, a.plan_count + u, a.plan_src + so,
                                     a.plan_dst + so, a.plan_evicted ? a.plan_evicted + so : nullptr,
                                     Pl, a.n_blk_max);
                 }
                 return;
-            }
+            } else {
             if (plan)
                 plan_load(a.slot_blk_in + (size_t)u * a.K, a.slot_stamp_in + (size_t)u * a.K, a.K, Pl);
             {
@@ -2111,26 +2236,27 @@ __global__ void __launch_bounds__(kNT) finish_kernel(StepArgs a, int select_item
                           a.plan_dst + so, a.plan_evicted ? a.plan_evicted + so : nullptr, Pl);
             }
             return;
+            }
         }
         k -= nu * NQ;
     }
     if (merge_items && k < nu * a.RGN) {
         float* Mr = cur.take<float>(kMaxRows);
         float* Lr = cur.take<float>(kMaxRows);
-        float* red = cur.take<float>(kNT);
+        float* red = cur.take<float>(NT);
         float* W = cur.take<float>(kMergeW);
         const int i = k / a.RGN, grp = k - (k / a.RGN) * a.RGN;
-        attn_merge_unit<DT, D>(a, x + 8 * i, row_win(a, grp), Mr, Lr, red, W);
+        attn_merge_unit<DT, D, NT>(a, x + 8 * i, row_win(a, grp), Mr, Lr, red, W);
     }
 }
 
 // LDS of finish_kernel: a select item's top-K and plan state (+ its score row
 // when finish_scores_in_lds), a merge item's reduction buffers.
-__host__ __device__ inline size_t finish_lds_bytes(int K, int n_blk_max, bool sel) {
-    const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + kNT * 4 + kMergeW * 4;
+__host__ __device__ inline size_t finish_lds_bytes(int K, int n_blk_max, bool sel, int nt) {
+    const size_t m = 2 * 16 * ((kMaxRows * 4 + 15) / 16) + (size_t)nt * 4 + kMergeW * 4;
     if (!sel) return m;
     const size_t p = ((size_t)pad4(K) * 4 + 15) / 16 * 16 + plan_lds_size(K);  // P, plan
-    const size_t s = p + (n_blk_max <= kSelKPT * kNT
+    const size_t s = p + (n_blk_max <= kSelRowMax
                               ? plan_fast_lds_size(K, n_blk_max) + sel_lds_bytes()
                               : scan_lds_bytes(1, 0, K, (int)finish_scores_lds(n_blk_max)) +
                                     ((size_t)pad4(K) * 8 + 15) / 16 * 16);  // top-K state, rank keys

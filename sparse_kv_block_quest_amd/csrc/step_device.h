@@ -2268,12 +2268,16 @@ struct StepPlan {
     int NC, chunk, S, per_split;
 };
 
+constexpr int kMinSplitTiles = 8;     // automatic split: tiles per attention item at least
+constexpr int kMinChunkBlocks = 256;  // automatic split: blocks per scan item at least
+
 // Items per unit.  With at least 256 units (one per CU) every unit gets one
 // scan item and one attention item: no partials, one launch.  Smaller batches
 // split units until about 512 main workgroups (two per CU) are in flight:
-// the attention takes its share of the items by bytes (at least 4 tiles per
-// split), the scan the items left (at least 64 blocks each); the split units
-// then take a second, small launch.
+// the attention takes its share of the items by bytes (at least kMinSplitTiles
+// tiles per split), the scan the items left (at least kMinChunkBlocks blocks
+// each; below these an item's fixed costs outweigh its share of the stream);
+// the split units then take a second, small launch.
 // With rgn row groups every split is rgn items, each reading the split's tiles.
 inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb, bool scan,
                            bool attn, int want_nc, int want_s, int rgn = 1) {
@@ -2284,7 +2288,8 @@ inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb
     const double tot = scan_b + attn_b > 0 ? scan_b + attn_b : 1.0;
     if (attn) {
         int s = want_s > 0 ? want_s : (U >= 256 ? 1 : (int)(items * attn_b / tot / rgn + 0.5));
-        if (want_s <= 0 && s > (n_sel + 3) / 4) s = (n_sel + 3) / 4;
+        if (want_s <= 0 && s > (n_sel + kMinSplitTiles - 1) / kMinSplitTiles)
+            s = (n_sel + kMinSplitTiles - 1) / kMinSplitTiles;
         const int min_s = (n_sel + kMaxSplitEntries - 1) / kMaxSplitEntries;
         if (s < min_s) s = min_s;
         if (n_sel > 0 && s > n_sel) s = n_sel;
@@ -2298,7 +2303,7 @@ inline StepPlan plan_items(int U, int n_blk_max, int n_sel, int D, int B, int eb
         const int left = items - (attn ? p.S * rgn : 0);
         int nc = want_nc > 0 ? want_nc
                              : (U >= 256 ? 1 : (attn ? left : (int)(items * scan_b / tot + 0.5)));
-        const int max_nc = want_nc > 0 ? n_blk_max : (n_blk_max + 63) / 64;
+        const int max_nc = want_nc > 0 ? n_blk_max : (n_blk_max + kMinChunkBlocks - 1) / kMinChunkBlocks;
         if (nc > max_nc) nc = max_nc;
         if (nc < 1) nc = 1;
         const int chunk = (n_blk_max + nc - 1) / nc;

@@ -90,6 +90,29 @@ __device__ __forceinline__ void store_elem(void* base, size_t i, float f) {
     }
 }
 
+// Four consecutive elements from element i (i a multiple of 4): one vector
+// store when the address allows it, else four.
+template <int DT>
+__device__ __forceinline__ void store4(void* base, size_t i, const float (&f)[4]) {
+    if constexpr (DT == OASIS_F32) {
+        float* p = reinterpret_cast<float*>(base) + i;
+        if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+            *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+            return;
+        }
+    } else {
+        uint16_t* p = reinterpret_cast<uint16_t*>(base) + i;
+        if ((reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+            const uint32_t lo = f32_to_bf16_bits(f[0]) | (f32_to_bf16_bits(f[1]) << 16);
+            const uint32_t hi = f32_to_bf16_bits(f[2]) | (f32_to_bf16_bits(f[3]) << 16);
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+            return;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) store_elem<DT>(base, i + c, f[c]);
+}
+
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t float_key(float f) {
     uint32_t u = __float_as_uint(f);

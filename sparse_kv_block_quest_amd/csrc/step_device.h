@@ -706,9 +706,19 @@ __device__ __forceinline__ void sel_load(const float* row, int n, uint32_t (&key
 // Ranked top-K of the row whose score bits sel_load put in `key`: block
 // indices to orow[0..K) (-1 past n), scores to srow (if any), and the ranked
 // blocks to P (LDS, -1 padded to pad4(K); if any) for the plan.
-template <int NT>
+// `hook` runs work of the caller's that needs no selection result inside the
+// selection's first LDS phase: before() ahead of its first barrier, after()
+// right after it (another barrier follows before the selection returns).
+// With P, each ranked block's rank also goes to mark_p[block] (if mark_p).
+struct NoHook {
+    __device__ void before() const {}
+    __device__ void after() const {}
+};
+
+template <int NT, class Hook = NoHook>
 __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int n, int K,
-                                           int32_t* orow, float* srow, int* P, const SelLds& L) {
+                                           int32_t* orow, float* srow, int* P, const SelLds& L,
+                                           const Hook& hook = Hook(), uint16_t* mark_p = nullptr) {
     constexpr int KPT = kSelRowMax / NT;
     constexpr int NW = NT / 64;
     static_assert(KPT * NT == kSelRowMax && NT >= 256, "one index field per held key");
@@ -721,6 +731,9 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
     if (P)
         for (int a = max(Kp, 0) + t; a < pad4(K); a += NT) P[a] = -1;
     if (Kp <= 0) {
+        hook.before();
+        lds_barrier();
+        hook.after();
         lds_barrier();
         return;
     }
@@ -744,7 +757,9 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
         L.red[wv * 2 + 1] = hi;
     }
     for (int i = t; i < 512; i += NT) L.hist[i] = 0;
+    hook.before();
     lds_barrier();
+    hook.after();
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
         lo = L.red[w * 2] < lo ? L.red[w * 2] : lo;
@@ -844,7 +859,10 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
             const int bi = (int)(kSelIdxMax - (uint32_t)(e & kSelIdxMax));
             orow[rank] = bi;
             if (srow) srow[rank] = key_float((uint32_t)(e >> kSelIdxBits));
-            if (P) P[rank] = bi;
+            if (P) {
+                P[rank] = bi;
+                if (mark_p) mark_p[bi] = (uint16_t)rank;
+            }
         }
     };
     if (4 * C <= NT) {
@@ -937,54 +955,64 @@ __device__ __forceinline__ void plan_load(const int32_t* blk_in, const int32_t* 
     }
 }
 
-// Slots in (stamp, slot) order, oldest first (L.order[rank] = slot), and
-// whether any slot is empty (the seeding plan): both depend on the slot tables
-// only, so a FAST plan has them before its predicted list exists.  Needs the
-// staged tables visible (a barrier after plan_load) and leaves a barrier to
-// plan_unit.  With NT >= 4 * K, four adjacent lanes count one slot's rank,
-// each over a quarter of the keys.
-template <int NT = kNT>
-__device__ __forceinline__ void plan_order(int K, const PlanLds& L) {
-    const int tid = threadIdx.x;
-    const int K4 = pad4(K);
-    int empty = 0;
-    for (int s = tid; s < K4; s += NT) {
-        L.ekey[s] = s < K ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
-                          : 0x7fffffffffffffffLL;
-        empty |= s < K && L.blk[s] == -1;
+// Slots in (stamp, slot) order, oldest first (L.order[rank] = slot), whether
+// any slot is empty (the seeding plan), and each resident block's slot in
+// L.mark_b: all depend on the slot tables only, so a FAST plan has them
+// before its predicted list exists.  Run as a selection hook: before() needs
+// the staged tables (plan_load, its loads waited for) and a barrier after it,
+// after() counts each slot's rank (four adjacent lanes per slot when the
+// workgroup has them, each over a quarter of the keys).
+template <int NT>
+struct PlanOrderHook {
+    const PlanLds& L;
+    int K, n_blk;
+    __device__ void before() const {
+        const int tid = threadIdx.x;
+        const int K4 = pad4(K);
+        int empty = 0;
+        for (int s = tid; s < K4; s += NT) {
+            const int bb = s < K ? L.blk[s] : -1;
+            L.ekey[s] = s < K ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
+                              : 0x7fffffffffffffffLL;
+            empty |= s < K && bb == -1;
+            if (bb >= 0 && bb < n_blk) L.mark_b[bb] = (uint16_t)s;
+        }
+        const bool wave_empty = __ballot(empty) != 0;
+        if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
     }
-    const bool wave_empty = __ballot(empty) != 0;
-    if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
-    lds_barrier();
-    const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
-    if (NT >= 4 * K4) {
-        const int s = tid >> 2, part = tid & 3;
-        const int q = K4 / 8;  // pairs per quarter; the last quarter takes the rest
-        const int i0 = part * q, i1 = part == 3 ? K4 / 2 : i0 + q;
-        int r = 0;
-        if (s < K) {
+    __device__ void after() const {
+        const int tid = threadIdx.x;
+        const int K4 = pad4(K);
+        const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
+        if (NT >= 4 * K4) {
+            const int s = tid >> 2, part = tid & 3;
+            const int q = K4 / 8;  // pairs per quarter; the last quarter takes the rest
+            const int i0 = part * q, i1 = part == 3 ? K4 / 2 : i0 + q;
+            int r = 0;
+            if (s < K) {
+                const long long e = L.ekey[s];
+                for (int i = i0; i < i1; ++i) {
+                    const longlong2 x = E2[i];
+                    r += (x.x < e) + (x.y < e);
+                }
+            }
+            r += __shfl_xor(r, 1, 64);
+            r += __shfl_xor(r, 2, 64);
+            if (s < K && part == 0) L.order[r] = s;
+            return;
+        }
+        for (int s = tid; s < K; s += NT) {
             const long long e = L.ekey[s];
-            for (int i = i0; i < i1; ++i) {
+            int r = 0;
+#pragma unroll 8
+            for (int i = 0; i < K4 / 2; ++i) {
                 const longlong2 x = E2[i];
                 r += (x.x < e) + (x.y < e);
             }
+            L.order[r] = s;
         }
-        r += __shfl_xor(r, 1, 64);
-        r += __shfl_xor(r, 2, 64);
-        if (s < K && part == 0) L.order[r] = s;
-        return;
     }
-    for (int s = tid; s < K; s += NT) {
-        const long long e = L.ekey[s];
-        int r = 0;
-#pragma unroll 8
-        for (int i = 0; i < K4 / 2; ++i) {
-            const longlong2 x = E2[i];
-            r += (x.x < e) + (x.y < e);
-        }
-        L.order[r] = s;
-    }
-}
+};
 
 // Capped least-recently-selected plan of one unit from the ranked predicted
 // list P (LDS, -1 padded) and the staged slot tables, then the insertion of
@@ -1005,15 +1033,12 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     const int tid = threadIdx.x;
     const int K4 = pad4(K);
     int seeding = 0;
-    if constexpr (FAST) {
-        // Membership both ways through the marks (16-bit stores, one writer
-        // per mark except for blocks held twice, which then agree).
-        for (int it = tid; it < K; it += NT) {
-            const int pb = P[it], bb = L.blk[it];
-            if (pb >= 0 && pb < n_blk) L.mark_p[pb] = (uint16_t)it;
-            if (bb >= 0 && bb < n_blk) L.mark_b[bb] = (uint16_t)it;
-        }
-        lds_barrier();
+    uint32_t n_missing = 0, n_hits = 0;
+    if (FAST && K <= 256) {
+        // The marks are in place (mark_b from the slot-order hook, mark_p from
+        // the ranking): every thread tests membership, then one wave scans
+        // (lane l takes items 4l .. 4l+3: predicted ranks, slots, slots in
+        // (stamp, slot) order).
         for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
         for (int it = tid; it < K; it += NT) {
             const int bb = L.blk[it];
@@ -1023,6 +1048,8 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
                 hit = i < K && P[i] == bb;
             }
             L.hit[it] = hit;
+            L.new_blk[it] = bb;
+            L.new_stamp[it] = hit ? step : L.stamp[it];
             const int pb = P[it];
             int found = 0;
             if (pb >= 0 && pb < n_blk) {
@@ -1032,45 +1059,6 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
             L.miss[it] = pb >= 0 && !found;
         }
         lds_barrier();
-    } else {
-        int empty = 0;
-        for (int s = tid; s < K; s += NT) empty |= L.blk[s] == -1;
-        const bool wave_empty = __ballot(empty) != 0;
-        if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
-        lds_barrier();
-        for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
-        // Membership both ways: slot s is a hit if its block is predicted; rank i
-        // is missing if its block is not resident.  Items [0, K) are slots,
-        // [K, 2K) predicted ranks.
-        const int4* P4 = reinterpret_cast<const int4*>(P);
-        const int4* B4 = reinterpret_cast<const int4*>(L.blk);
-        for (int it = tid; it < 2 * K; it += NT) {
-            const bool slot = it < K;
-            const int idx = slot ? it : it - K;
-            const int v = slot ? L.blk[idx] : P[idx];
-            const int4* other = slot ? P4 : B4;
-            int found = 0;
-            if (v >= 0) {
-#pragma unroll 8
-                for (int i = 0; i < K4 / 4; ++i) {
-                    const int4 x = other[i];
-                    found |= (x.x == v) | (x.y == v) | (x.z == v) | (x.w == v);
-                }
-            }
-            if (slot)
-                L.hit[idx] = found;
-            else
-                L.miss[idx] = v >= 0 && !found;
-        }
-        lds_barrier();
-    }
-    // Missing blocks in rank order, victims counted (FAST: victims in slot
-    // order, so the scan also gives each non-hit slot its victim rank).
-    uint32_t n_missing = 0, n_hits = 0;
-    if constexpr (FAST) {
-      if (K <= 256) {
-        // One wave: lane l takes items 4l .. 4l+3 (predicted ranks, slots,
-        // slots in (stamp, slot) order); the others wait at the barrier.
         if (tid < 64) {
             uint32_t f0[4], f1[4], f2[4];
             int so[4];
@@ -1104,72 +1092,130 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
                 L.scanbuf[1] = i1;
             }
         }
-        for (int s = tid; s < K; s += NT) {
-            L.new_blk[s] = L.blk[s];
-            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
-        }
         lds_barrier();
         n_missing = L.scanbuf[0];
         n_hits = L.scanbuf[1];
-      } else {
-        uint32_t n_vict = 0;
-        for (int base = 0; base < K; base += NT) {
-            const int i = base + tid;
-            const int so = i < K ? L.order[i] : 0;
-            uint32_t v[3] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u,
-                             i < K ? (uint32_t)(L.hit[so] == 0) : 0u};
-            uint32_t ex[3], tot[3];
-            block_scan<3, NT>(v, ex, tot, L.scanbuf);
-            if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
-            if (i < K) {
-                if (v[2]) L.victim_of_rank[n_vict + ex[2]] = so;
-                L.rank_of_slot[so] = v[2] ? (int)(n_vict + ex[2]) : K;
-            }
-            n_missing += tot[0];
-            n_hits += tot[1];
-            n_vict += tot[2];
-        }
-        for (int s = tid; s < K; s += NT) {
-            L.new_blk[s] = L.blk[s];
-            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
-        }
-        lds_barrier();
-      }
     } else {
-        for (int base = 0; base < K; base += NT) {
-            const int i = base + tid;
-            uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
-            uint32_t ex[2], tot[2];
-            block_scan<2, NT>(v, ex, tot, L.scanbuf);
-            if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
-            n_missing += tot[0];
-            n_hits += tot[1];
-        }
-        for (int s = tid; s < K4; s += NT)
-            L.ekey[s] = (s < K && !L.hit[s])
-                            ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
-                            : 0x7fffffffffffffffLL;
-        lds_barrier();
-        // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
-        for (int s = tid; s < K; s += NT) {
-            if (!L.hit[s]) {
-                const long long e = L.ekey[s];
-                int r = 0;
-                const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
-#pragma unroll 8
-                for (int i = 0; i < K4 / 2; ++i) {
-                    const longlong2 x = E2[i];
-                    r += (x.x < e) + (x.y < e);
-                }
-                L.victim_of_rank[r] = s;
-                L.rank_of_slot[s] = r;
-            } else {
-                L.rank_of_slot[s] = K;
+        if constexpr (FAST) {
+            // Membership both ways through the marks (16-bit stores, one writer
+            // per mark except for blocks held twice, which then agree).
+            for (int it = tid; it < K; it += NT) {
+                const int pb = P[it], bb = L.blk[it];
+                if (pb >= 0 && pb < n_blk) L.mark_p[pb] = (uint16_t)it;
+                if (bb >= 0 && bb < n_blk) L.mark_b[bb] = (uint16_t)it;
             }
-            L.new_blk[s] = L.blk[s];
-            L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+            lds_barrier();
+            for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
+            for (int it = tid; it < K; it += NT) {
+                const int bb = L.blk[it];
+                int hit = 0;
+                if (bb >= 0 && bb < n_blk) {
+                    const int i = L.mark_p[bb];
+                    hit = i < K && P[i] == bb;
+                }
+                L.hit[it] = hit;
+                const int pb = P[it];
+                int found = 0;
+                if (pb >= 0 && pb < n_blk) {
+                    const int sl = L.mark_b[pb];
+                    found = sl < K && L.blk[sl] == pb;
+                }
+                L.miss[it] = pb >= 0 && !found;
+            }
+            lds_barrier();
+        } else {
+            int empty = 0;
+            for (int s = tid; s < K; s += NT) empty |= L.blk[s] == -1;
+            const bool wave_empty = __ballot(empty) != 0;
+            if ((tid & 63) == 0) L.scanbuf[56 + (tid >> 6)] = wave_empty;
+            lds_barrier();
+            for (int w = 0; w < NT / 64; ++w) seeding |= L.scanbuf[56 + w] != 0;
+            // Membership both ways: slot s is a hit if its block is predicted; rank i
+            // is missing if its block is not resident.  Items [0, K) are slots,
+            // [K, 2K) predicted ranks.
+            const int4* P4 = reinterpret_cast<const int4*>(P);
+            const int4* B4 = reinterpret_cast<const int4*>(L.blk);
+            for (int it = tid; it < 2 * K; it += NT) {
+                const bool slot = it < K;
+                const int idx = slot ? it : it - K;
+                const int v = slot ? L.blk[idx] : P[idx];
+                const int4* other = slot ? P4 : B4;
+                int found = 0;
+                if (v >= 0) {
+#pragma unroll 8
+                    for (int i = 0; i < K4 / 4; ++i) {
+                        const int4 x = other[i];
+                        found |= (x.x == v) | (x.y == v) | (x.z == v) | (x.w == v);
+                    }
+                }
+                if (slot)
+                    L.hit[idx] = found;
+                else
+                    L.miss[idx] = v >= 0 && !found;
+            }
+            lds_barrier();
         }
-        lds_barrier();
+        // Missing blocks in rank order, victims counted (FAST: victims in slot
+        // order, so the scan also gives each non-hit slot its victim rank).
+        if constexpr (FAST) {
+            uint32_t n_vict = 0;
+            for (int base = 0; base < K; base += NT) {
+                const int i = base + tid;
+                const int so = i < K ? L.order[i] : 0;
+                uint32_t v[3] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u,
+                                 i < K ? (uint32_t)(L.hit[so] == 0) : 0u};
+                uint32_t ex[3], tot[3];
+                block_scan<3, NT>(v, ex, tot, L.scanbuf);
+                if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
+                if (i < K) {
+                    if (v[2]) L.victim_of_rank[n_vict + ex[2]] = so;
+                    L.rank_of_slot[so] = v[2] ? (int)(n_vict + ex[2]) : K;
+                }
+                n_missing += tot[0];
+                n_hits += tot[1];
+                n_vict += tot[2];
+            }
+            for (int s = tid; s < K; s += NT) {
+                L.new_blk[s] = L.blk[s];
+                L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+            }
+            lds_barrier();
+        } else {
+            for (int base = 0; base < K; base += NT) {
+                const int i = base + tid;
+                uint32_t v[2] = {i < K ? (uint32_t)L.miss[i] : 0u, i < K ? (uint32_t)L.hit[i] : 0u};
+                uint32_t ex[2], tot[2];
+                block_scan<2, NT>(v, ex, tot, L.scanbuf);
+                if (v[0]) L.missing_of_rank[n_missing + ex[0]] = P[i];
+                n_missing += tot[0];
+                n_hits += tot[1];
+            }
+            for (int s = tid; s < K4; s += NT)
+                L.ekey[s] = (s < K && !L.hit[s])
+                                ? (long long)(((unsigned long long)(long long)L.stamp[s] << 32) | (unsigned)s)
+                                : 0x7fffffffffffffffLL;
+            lds_barrier();
+            // Victims ordered by (stamp, slot): counting rank over the 64-bit keys.
+            for (int s = tid; s < K; s += NT) {
+                if (!L.hit[s]) {
+                    const long long e = L.ekey[s];
+                    int r = 0;
+                    const longlong2* E2 = reinterpret_cast<const longlong2*>(L.ekey);
+#pragma unroll 8
+                    for (int i = 0; i < K4 / 2; ++i) {
+                        const longlong2 x = E2[i];
+                        r += (x.x < e) + (x.y < e);
+                    }
+                    L.victim_of_rank[r] = s;
+                    L.rank_of_slot[s] = r;
+                } else {
+                    L.rank_of_slot[s] = K;
+                }
+                L.new_blk[s] = L.blk[s];
+                L.new_stamp[s] = L.hit[s] ? step : L.stamp[s];
+            }
+            lds_barrier();
+        }
     }
     const int n_victims = K - (int)n_hits;
     int n = min((int)n_missing, n_victims);
@@ -1895,10 +1941,11 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
     const float4* pa = reinterpret_cast<const float4*>(a.part_acc + ub * S * NR * D);
     const float ninf = -__builtin_inff();
     const bool keep_w = S * NR <= kMergeW;
-    // Four adjacent threads share an output piece, each summing a contiguous
-    // range of `per` splits; the ranges are then added in a fixed tree.  The
-    // order depends on S only, so stacked rows merge exactly as single rows.
-    constexpr int tpo = 4;
+    // tpo adjacent threads (4, or 2 when S < 4) share an output piece, each
+    // summing a contiguous range of `per` splits; the ranges are then added in
+    // a fixed tree.  The order depends on S only, so stacked rows merge exactly
+    // as single rows.
+    const int tpo = S >= 4 ? 4 : 2;
     const int per = (S + tpo - 1) / tpo;
     const int part = tid % tpo;
     const int s_lo = min(part * per, S), s_hi = min(s_lo + per, S);
@@ -1910,8 +1957,12 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
             v[e] = pa[(size_t)max(min(s0 + e, s_hi - 1), 0) * n4 + o4];
     };
     if (tid / tpo < n4) load_batch(tid / tpo, s_lo);
-    float mx = ninf;
-    if (sub < nsub)
+    // With S <= nsub a thread holds at most one (m, l) pair: read it once.
+    const bool one = S <= nsub;
+    float2 pr1 = make_float2(ninf, 0.f);
+    if (one && sub < S) pr1 = reinterpret_cast<const float2*>(ml)[(size_t)sub * NR + row_t];
+    float mx = pr1.x;
+    if (!one)
         for (int s = sub; s < S; s += nsub) mx = fmaxf(mx, ml[((size_t)s * NR + row_t) * 2]);
     red[tid] = mx;
     __syncthreads();
@@ -1922,7 +1973,14 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
     }
     __syncthreads();
     float sm = 0.f;
-    if (sub < nsub) {
+    if (one) {
+        if (sub < S) {
+            const float M = Mr[row_t];
+            const float w = (M != ninf && pr1.x != ninf) ? exp2f(pr1.x - M) : 0.f;
+            if (keep_w) W[sub * NR + row_t] = w;
+            if (w != 0.f) sm += w * pr1.y;
+        }
+    } else if (sub < nsub) {
         const float M = Mr[row_t];
         for (int s = sub; s < S; s += nsub) {
             const size_t pr = ((size_t)s * NR + row_t) * 2;
@@ -1974,13 +2032,17 @@ __device__ void attn_merge_unit(const StepArgs& a, int u, const RowWin& win, flo
         for (int c = 0; c < 4; ++c) {
             float o = __shfl_xor(acc[c], 1, 64);
             acc[c] = (part & 1) ? o + acc[c] : acc[c] + o;
-            o = __shfl_xor(acc[c], 2, 64);
-            acc[c] = (part & 2) ? o + acc[c] : acc[c] + o;
+            if (tpo == 4) {
+                o = __shfl_xor(acc[c], 2, 64);
+                acc[c] = (part & 2) ? o + acc[c] : acc[c] + o;
+            }
         }
         if (part == 0) {
             const size_t ob = attn_out_row(a, u, win.row0 + row) * D + d;
+            float r[4];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) store_elem<DT>(a.out, ob + c, L > 0.f ? acc[c] / L : 0.f);
+            for (int c = 0; c < 4; ++c) r[c] = L > 0.f ? acc[c] / L : 0.f;
+            store4<DT>(a.out, ob, r);
         }
     }
 }
@@ -2154,8 +2216,7 @@ __global__ void __launch_bounds__(NT) finish_kernel(StepArgs a, int select_items
             int* P = cur.take<int>(K4);
             PlanLds Pl = carve_plan(cur, K4);
             if constexpr (NT != kNT) {
-                // The slot tables' loads, then the scores' (all in flight); the
-                // slot order is formed while the scores arrive.
+                // The slot tables' loads, then the scores' (all in flight).
                 carve_plan_fast(cur, K4, a.n_blk_max, Pl);
                 const SelLds S = carve_sel(cur);
                 if (plan)
@@ -2163,12 +2224,13 @@ __global__ void __launch_bounds__(NT) finish_kernel(StepArgs a, int select_items
                                   a.K, Pl);
                 uint32_t key[kSelRowMax / NT];
                 sel_load<NT>(gsc, n_r, key);
-                if (plan) {
-                    lds_barrier();
-                    plan_order<NT>(a.K, Pl);
-                }
-                select_row<NT>(key, n_r, a.K, a.topk_idx + ob,
-                               a.topk_score ? a.topk_score + ob : nullptr, plan ? P : nullptr, S);
+                int32_t* oi = a.topk_idx + ob;
+                float* os = a.topk_score ? a.topk_score + ob : nullptr;
+                if (plan)  // the slot order and resident marks ride in the selection's first phase
+                    select_row<NT>(key, n_r, a.K, oi, os, P, S, PlanOrderHook<NT>{Pl, a.K, a.n_blk_max},
+                                   Pl.mark_p);
+                else
+                    select_row<NT>(key, n_r, a.K, oi, os, nullptr, S);
                 if (plan) {
                     const size_t so = (size_t)u * a.K;
                     plan_unit<true, NT>(P, a.K, a.slot_blk_out + so, a.slot_stamp_out + so, a.step, a.cap,

@@ -114,8 +114,9 @@ __device__ __forceinline__ void store4(void* base, size_t i, const float (&f)[4]
 }
 
 // Order-preserving map of fp32 onto uint32 (larger float -> larger key).
+// -0 and +0 compare equal, so they get one key (adding +0 turns -0 into +0).
 __device__ __forceinline__ uint32_t float_key(float f) {
-    uint32_t u = __float_as_uint(f);
+    uint32_t u = __float_as_uint(f + 0.0f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 

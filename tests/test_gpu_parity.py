@@ -185,6 +185,47 @@ def test_score_topk_ties_and_short_contexts(cuda):
     assert torch.all(idx[2] == -1)
 
 
+def edge_summaries(case, R, H, nb, D, gen, dev):
+    """Summaries whose scores stress the selection: all equal, a few distinct
+    values (radix passes run into the block-index bits), or random."""
+    x = synth.normal((R, H, nb, D), gen, dev).abs()
+    if case == "equal":
+        x = torch.zeros_like(x)
+    elif case in ("two_values", "few"):
+        n_pat = 2 if case == "two_values" else 5
+        pats = synth.normal((R, H, n_pat, D), gen, dev).abs()
+        pick = torch.randint(0, n_pat, (R, H, nb), generator=gen, device=dev)
+        x = torch.gather(pats, 2, pick[..., None].expand(R, H, nb, D))
+    return torch.stack([-x, x], dim=3).contiguous()  # [R][H][nb][2][D]: min, max
+
+
+@pytest.mark.parametrize("case,nb,K,n_blk", [
+    ("random", 8192, 128, None), ("equal", 8192, 128, None), ("two_values", 8192, 128, None),
+    ("few", 3000, 64, None), ("random", 8192, 1024, None), ("random", 8192, 1, None),
+    ("two_values", 8192, 1024, None), ("random", 2048, 128, [2048, 100, 7, 0]),
+    ("equal", 1500, 16, [1500, 1499, 16, 15]),
+])
+def test_score_topk_split_selection_edges(cuda, case, nb, K, n_blk):
+    """The second launch's selection of split units (scan chunks forced), on
+    rows held in registers: ties everywhere, a few distinct scores (several
+    radix passes, the last ones into the block-index bits), K up to 1024 (more
+    candidates than four lanes each can rank), K = 1, rows no longer than the
+    candidate bound (no pass), shorter than K, and empty."""
+    say(f"split selection {case} nb={nb} K={K} n_blk={n_blk}")
+    R, H, G, D = 4, 2, 2, 64
+    gen = synth.generator(11, synth.S_MISC, cuda)
+    summ = edge_summaries(case, R, H, nb, D, gen, cuda)
+    q = synth.normal((R, 2, H * G, D), gen, cuda)
+    wl = synth.replace(synth.workload("tiny-fp32"), R=R, H=H, Hq=H * G, D=D, B=16, L=nb * 16, K=K)
+    nbt = None if n_blk is None else torch.tensor(n_blk, dtype=torch.int32, device=cuda)
+    for chunks in (2, 5):
+        idx, val, sc = ops.score_topk(q, summ, K, n_blk=nbt, want_scores=True,
+                                      opts=ops.step_opts(scan_chunks=chunks))
+        torch.cuda.synchronize()
+        nbn = np.full(R, nb, dtype=np.int32) if n_blk is None else np.array(n_blk, dtype=np.int32)
+        check_score_topk_against_oracle(wl, summ, q, idx, val, sc, nbn, K)
+
+
 @pytest.mark.parametrize("name,units", [("qwen3-8b-1layer", None), ("qwen3-235b-1layer", [(0, 1), (7, 3)]),
                                         ("llama3.1-8b-32layer", [(0, 0), (13, 5), (31, 7)])])
 def test_score_topk_full_size(cuda, name, units):

@@ -1034,6 +1034,7 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     const int K4 = pad4(K);
     int seeding = 0;
     uint32_t n_missing = 0, n_hits = 0;
+    bool admitted = false;  // the FAST one-wave path admits the missing blocks itself
     if (FAST && K <= 256) {
         // The marks are in place (mark_b from the slot-order hook, mark_p from
         // the ranking): every thread tests membership, then one wave scans
@@ -1091,7 +1092,24 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
                 L.scanbuf[0] = i0;
                 L.scanbuf[1] = i1;
             }
+            if (tid == 0) L.ins_key[1] = ~0ull;  // for the insertion below
+            // The same wave admits the missing blocks: its lanes' LDS writes
+            // above are seen by its reads below (one wave's LDS operations
+            // complete in order), so no workgroup barrier sits in between.
+            const int nm = (int)__builtin_amdgcn_readlane((int)i0, 63);
+            const int nh = (int)__builtin_amdgcn_readlane((int)i1, 63);
+            int na = min(nm, K - nh);
+            bool seed_w = false;
+            for (int w = 0; w < NT / 64; ++w) seed_w |= L.scanbuf[56 + w] != 0;
+            if (!seed_w) na = min(na, cap);
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            for (int i = tid; i < na; i += 64) {
+                const int dst = L.victim_of_rank[i];
+                L.new_blk[dst] = L.missing_of_rank[i];
+                L.new_stamp[dst] = step;
+            }
         }
+        admitted = true;
         lds_barrier();
         n_missing = L.scanbuf[0];
         n_hits = L.scanbuf[1];
@@ -1220,13 +1238,15 @@ __device__ void plan_unit(const int* P, int K, int32_t* blk_out, int32_t* stamp_
     const int n_victims = K - (int)n_hits;
     int n = min((int)n_missing, n_victims);
     if (!seeding) n = min(n, cap);
-    for (int i = tid; i < n; i += NT) {
-        const int dst = L.victim_of_rank[i];
-        L.new_blk[dst] = L.missing_of_rank[i];
-        L.new_stamp[dst] = step;
+    if (!admitted) {
+        for (int i = tid; i < n; i += NT) {
+            const int dst = L.victim_of_rank[i];
+            L.new_blk[dst] = L.missing_of_rank[i];
+            L.new_stamp[dst] = step;
+        }
+        if (ins >= 0 && tid == 0) L.ins_key[1] = ~0ull;
+        lds_barrier();
     }
-    if (ins >= 0 && tid == 0) L.ins_key[1] = ~0ull;
-    lds_barrier();
     if (ins >= 0) {  // uniform: one value per request
         // The oldest (stamp, slot) after the admissions: a minimum per thread,
         // per wave (DPP, high words first, then the low words of the lanes

@@ -677,6 +677,7 @@ constexpr int kFinishNT = 1024;              // threads of a selection-launch wo
 
 struct SelLds {
     int* hist;                 // [2][256]
+    int* pos;                  // [256]: first candidate slot of each digit of the first pass
     uint32_t* red;             // [64]: per wave (min, max) [0, 32), candidate counts [32, 48)
     int* sh;                   // [4]
     unsigned long long* cand;  // [kSelCandMax + 2]
@@ -685,13 +686,14 @@ struct SelLds {
 __device__ __forceinline__ SelLds carve_sel(LdsCursor& cur) {
     SelLds L;
     L.hist = cur.take<int>(512);
+    L.pos = cur.take<int>(256);
     L.red = cur.take<uint32_t>(64);
     L.sh = cur.take<int>(4);
     L.cand = cur.take<unsigned long long>(kSelCandMax + 2);
     return L;
 }
 __host__ __device__ inline size_t sel_lds_bytes() {
-    return 512 * 4 + 64 * 4 + 16 + (size_t)(kSelCandMax + 2) * 8 + 48;
+    return 512 * 4 + 256 * 4 + 64 * 4 + 16 + (size_t)(kSelCandMax + 2) * 8 + 64;
 }
 
 // Issue the loads of a row's scores (raw bits; no use, so nothing waits yet).
@@ -771,6 +773,7 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
     unsigned long long mask = ~((1ull << hb) - 1ull);
     unsigned long long prefix = ((unsigned long long)hi << kSelIdxBits) & mask;
     int above = 0, remaining = Kp, cnt = n;
+    int npass = 0, d1 = 0, shift1 = 0;  // passes run; the first pass's digit and shift
     if (n <= cmax) {
         prefix = 0ull;  // every block is a candidate
     } else {
@@ -811,6 +814,7 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
                         L.sh[1] = before;
                         L.sh[2] = c[e];
                     }
+                    if (npass == 0) L.pos[255 - (4 * lane + e)] = before;  // keys of larger digits
                     before += c[e];
                 }
             }
@@ -818,6 +822,11 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
             lds_barrier();
             const int d = L.sh[0], before = L.sh[1];
             cnt = L.sh[2];
+            if (npass == 0) {
+                d1 = d;
+                shift1 = shift;
+            }
+            ++npass;
             prefix |= (unsigned long long)d << shift;
             mask |= (unsigned long long)dm << shift;
             hb = shift;
@@ -827,30 +836,47 @@ __device__ __forceinline__ void select_row(uint32_t (&key)[kSelRowMax / NT], int
             buf ^= 1;
         }
     }
-    // Candidates: every key at or above the bin's lower edge, compacted in
-    // thread order.
+    // Candidates: every key at or above the bin's lower edge.
     const int C = n <= cmax ? n : above + cnt;
-    uint32_t cm = 0;
-    if ((prefix & kSelIdxMax) == 0) {  // the edge has no index bits: compare scores only
-        const uint32_t p32 = (uint32_t)(prefix >> kSelIdxBits);
+    if (npass == 1) {
+        // One pass: every key shares the first pass's region, so the candidates
+        // are the keys of digits >= d1, and the digit's exclusive suffix count
+        // is where its keys start (their order within a digit does not matter:
+        // the ranking below orders them).
+        // (the first pass always takes 8 bits: hb >= the index field's 13)
 #pragma unroll
-        for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && key[q] >= p32) << q;
+        for (int q = 0; q < KPT; ++q) {
+            const int dg = shift1 >= kSelIdxBits
+                               ? (int)((key[q] >> (shift1 - kSelIdxBits)) & 255u)
+                               : (int)((uint32_t)(comp(q) >> shift1) & 255u);
+            if (q < nv && dg >= d1) L.cand[atomicAdd(&L.pos[dg], 1)] = comp(q);
+        }
+        if (t == 0) L.cand[C] = 0ull;  // pairs are read two at a time; 0 is below every key
+        lds_barrier();
     } else {
+        // Otherwise compacted in thread order.
+        uint32_t cm = 0;
+        if ((prefix & kSelIdxMax) == 0) {  // the edge has no index bits: compare scores only
+            const uint32_t p32 = (uint32_t)(prefix >> kSelIdxBits);
 #pragma unroll
-        for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && comp(q) >= prefix) << q;
+            for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && key[q] >= p32) << q;
+        } else {
+#pragma unroll
+            for (int q = 0; q < KPT; ++q) cm |= uint32_t(q < nv && comp(q) >= prefix) << q;
+        }
+        const uint32_t mine = (uint32_t)__builtin_popcount(cm);
+        const uint32_t inc = wave_incl_sum(mine);
+        if (lane == 63) L.red[32 + wv] = inc;
+        lds_barrier();
+        uint32_t pos = inc - mine;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) pos += w < wv ? L.red[32 + w] : 0u;
+#pragma unroll
+        for (int q = 0; q < KPT; ++q)
+            if ((cm >> q) & 1u) L.cand[pos++] = comp(q);
+        if (t == 0) L.cand[C] = 0ull;  // pairs are read two at a time; 0 is below every key
+        lds_barrier();
     }
-    const uint32_t mine = (uint32_t)__builtin_popcount(cm);
-    const uint32_t inc = wave_incl_sum(mine);
-    if (lane == 63) L.red[32 + wv] = inc;
-    lds_barrier();
-    uint32_t pos = inc - mine;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) pos += w < wv ? L.red[32 + w] : 0u;
-#pragma unroll
-    for (int q = 0; q < KPT; ++q)
-        if ((cm >> q) & 1u) L.cand[pos++] = comp(q);
-    if (t == 0) L.cand[C] = 0ull;  // pairs are read two at a time; 0 is below every key
-    lds_barrier();
     // Counting rank among the candidates.
     const ulonglong2* c2 = reinterpret_cast<const ulonglong2*>(L.cand);
     const int C2 = (C + 1) >> 1;

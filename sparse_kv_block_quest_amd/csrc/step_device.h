@@ -1488,6 +1488,7 @@ struct TokStage {
     const uint8_t* rows;  // [B-1][D] stored keys of the active block
     int active;           // this item appends a token (uniform)
     int summ;             // the token completes its block: 0 no, 1 rows staged, 2 load them
+    int blk, slot;        // the token's block and its row in the block
 };
 
 template <int DT, int D>
@@ -1507,9 +1508,12 @@ __device__ __forceinline__ TokStage tok_prefetch(const StepArgs& a, int u, int s
     const int p = a.pos[r];
     ts.active = sp == a.S - 1 && p >= 0 && p / a.B < a.unit_stride;
     ts.summ = 0;
+    ts.blk = ts.slot = 0;
     if (!ts.active) return ts;
     const int tid = threadIdx.x;
     const int b = p / a.B, t = p - (p / a.B) * a.B;
+    ts.blk = b;
+    ts.slot = t;
     if (t == a.B - 1) ts.summ = a.B - 1 <= kSummRows ? 1 : 2;
     // query rows: for each query row group j the G heads' rows are contiguous
     constexpr int QPT = (kMaxRows * D * 4 / 16 + kNT - 1) / kNT;  // q vectors per thread at most
@@ -2107,12 +2111,9 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F, const
     using E = typename Elem<DT>::type;
     if (!ts.active) return;
     constexpr int PL = (D + 63) / 64;  // dims per lane
-    const int r = u / a.H;
-    const int p = a.pos[r];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const size_t kn = (size_t)u * D;
     constexpr int RW = kMaxRows / (kNT / 64);  // rows per wave at most
-    const int b = p / a.B, t = p - (p / a.B) * a.B;
+    const int b = ts.blk, t = ts.slot;
     const size_t tile = ((size_t)u * a.unit_stride + b) * (size_t)a.tile_stride;
     float kx[PL], vx[PL];
 #pragma unroll
@@ -2149,12 +2150,12 @@ __device__ void attn_new_token(const StepArgs& a, int u, const AttnFin& F, const
         }
     }
     lds_barrier();
+    // The token's K row and V column go into its tile from the staged copies
+    // (the same elements as k_new / v_new; no load after the loop).
     for (int d = threadIdx.x; d < D; d += kNT) {
         const float knew = load_elem<DT>(ts.k, d);
-        reinterpret_cast<E*>(a.kt_w)[tile + (size_t)t * D + d] =
-            reinterpret_cast<const E*>(a.k_new)[kn + d];
-        reinterpret_cast<E*>(a.vt_w)[tile + (size_t)d * a.B + t] =
-            reinterpret_cast<const E*>(a.v_new)[kn + d];
+        reinterpret_cast<E*>(a.kt_w)[tile + (size_t)t * D + d] = reinterpret_cast<const E*>(ts.k)[d];
+        reinterpret_cast<E*>(a.vt_w)[tile + (size_t)d * a.B + t] = reinterpret_cast<const E*>(ts.v)[d];
         if (ts.summ) {
             float lo = knew, hi = knew;
             for (int j = 0; j < a.B - 1; ++j) {

@@ -230,6 +230,19 @@ def test_step_interleaved_store(cuda, name, G, D, B, L, K, opts):
               interleaved=True)
 
 
+@pytest.mark.parametrize("L,K,cap,opts", [
+    (16 * 1024, 258, 40, (4, 2, 0)),   # K > 256: the plan's block-scan branch, K not a multiple of 4
+    (16 * 1024, 18, 6, (3, 2, 0)),     # K < 64, not a multiple of 4: the one-wave branch
+    (16 * 9000, 64, 16, (2, 2, 0)),    # rows over 8,192 blocks: 256-thread selection and plan
+])
+def test_step_split_plan_branches(cuda, L, K, cap, opts):
+    """The second launch's plan on each of its branches, over a chain of steps
+    with forced scan chunks (so the selection and plan run in finish_kernel)."""
+    wl = small("qwen3-8b-1layer", R=2, H=2, Hq=8, L=L, K=K, cap=cap)
+    say(f"fused step split plan L={L} K={K} cap={cap} opts={opts}")
+    run_chain(cuda, wl, 3, opts=ops.step_opts(*opts))
+
+
 def test_step_short_contexts(cuda):
     """Requests with fewer full blocks than K, and an empty one."""
     wl = small("qwen3-8b-1layer", R=3, H=2, Hq=8, L=1024, K=32, cap=4)

@@ -17,7 +17,9 @@
 //    also attends its active local block).
 //
 // Work decomposition.  A unit is one (request r, KV head g) pair, u = r*H + g.
-// A launch is a 1-D grid of 256-thread workgroups.  Consecutive workgroup ids
+// The main launch is a 1-D grid of 256-thread workgroups (the second launch of
+// split units uses 1,024 threads when the score rows fit in registers).
+// Consecutive workgroup ids
 // go round robin over the 8 XCDs, so id w runs on XCD w % 8; every item of
 // unit u gets an id on XCD u % 8, which keeps a unit's partial results in one
 // L2.  Per XCD, scan items come first.
@@ -29,7 +31,7 @@
 //  - attention item (u, s): online softmax over split s of the unit's tile
 //    table (the last split also takes the active block).  With one split the
 //    item writes the outputs; with S > 1 it writes a partial (max, sum, acc)
-//    that finish_kernel merges in split order.
+//    that finish_kernel merges (in an order fixed by S).
 // Workgroups of one launch never exchange data: on this multi-XCD part every
 // device-scope release writes back a whole L2, which costs more than a second
 // launch, so the kernel boundary is the only synchronisation.
@@ -48,7 +50,7 @@ constexpr int kMaxTopK = 1024;  // largest K (resident slots per KV head)
 constexpr int kMaxRows = 32;    // n_q * G rows one attention item handles
 constexpr int kScanUnroll = 8;  // block passes in flight per scan thread
 constexpr int kTopkKPT = 16;    // top-K keys per thread held in registers
-constexpr int kFinishKPT = 32;  // the same in the selection launch of split units
+constexpr int kFinishKPT = 32;  // the same in the selection launch, rows over kSelRowMax blocks
 constexpr int kTopkGroup = 8;   // keys re-read per group beyond the register-held ones
 constexpr int kStageVec = 8;    // 16-byte score loads in flight per thread when staging
 constexpr int kMaxSplitEntries = 1024;  // tile-table entries of one attention item
@@ -658,7 +660,8 @@ __device__ void topk_rows(const float* sc, size_t rs, int n, int K, int32_t* oid
 
 // ------------------------------------------------------------ one long row
 // Top-K of one score row of up to kSelRowMax entries in global memory, by one
-// workgroup of NT threads (the selection launch of split units).  Thread t
+// workgroup of NT threads (the selection launch of split units; the ranked
+// list is the pages' per-head block set, v2 §3.3.1).  Thread t
 // holds the keys of blocks t, t + NT, ... in registers, loaded straight from
 // memory (coalesced, all in flight).  Each block's key is 64-bit: the
 // order-preserving uint32 of its score above the complement of its block

@@ -243,6 +243,15 @@ def test_step_split_plan_branches(cuda, L, K, cap, opts):
     run_chain(cuda, wl, 3, opts=ops.step_opts(*opts))
 
 
+def test_step_merge_weights_from_memory(cuda):
+    """More (split, row) pairs than the merge keeps in LDS (160 splits x 32 rows
+    of the VALU attention at G = 16): the merge reads its weights' inputs from
+    memory instead."""
+    wl = small("qwen3-8b-1layer", R=1, H=1, Hq=16, L=16 * 2048, K=160, cap=8)
+    say("fused step, 160 attention splits x 32 rows")
+    run_chain(cuda, wl, 2, opts=ops.step_opts(2, 160, 1))
+
+
 def test_step_short_contexts(cuda):
     """Requests with fewer full blocks than K, and an empty one."""
     wl = small("qwen3-8b-1layer", R=3, H=2, Hq=8, L=1024, K=32, cap=4)

@@ -250,8 +250,8 @@ __device__ __forceinline__ void scan_blocks(const StepArgs& a, int u, int c, flo
 #pragma unroll
         for (int k = 0; k < UNR; ++k) {
             const int b = min(b0 + k * BPP + lb, b_end - 1);
-            mn[k] = base[(size_t)b * 2 * LPR];
-            mx[k] = base[(size_t)b * 2 * LPR + LPR];
+            mn[k] = load_stream(base + (size_t)b * 2 * LPR);
+            mx[k] = load_stream(base + (size_t)b * 2 * LPR + LPR);
         }
     };
     // The first summaries do not depend on q: they are in flight while the
@@ -1648,11 +1648,12 @@ __device__ TokStage attn_item_mfma(const StepArgs& a, int u, int sp, const RowWi
         const uint8_t* vbase = a.vt + (t64 * tile_elems + (real ? (size_t)sub * 16 : 0)) * 2;
 #pragma unroll
         for (int j = 0; j < KB; ++j)
-            kv[j] = *reinterpret_cast<const bf16x8_t*>(kbase + (real ? ((size_t)j * 64 + lane) * 16 : 0));
+            kv[j] = load_stream(
+                reinterpret_cast<const bf16x8_t*>(kbase + (real ? ((size_t)j * 64 + lane) * 16 : 0)));
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-            vv[db] = *reinterpret_cast<const bf16x4_t*>(
-                vbase + (real ? ((size_t)(db * 16 + l16) * B + lg * 4) * 2 : 0));
+            vv[db] = load_stream(reinterpret_cast<const bf16x4_t*>(
+                vbase + (real ? ((size_t)(db * 16 + l16) * B + lg * 4) * 2 : 0)));
         return ntok;
     };
 

@@ -40,7 +40,7 @@ build_summaries_kernel(const uint8_t* __restrict__ keys, uint8_t* __restrict__ s
     float lo[VEC], hi[VEC];
     {
         float v[VEC];
-        unpack16<DT>(src[0], v);
+        unpack16<DT>(load_stream(src), v);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) lo[e] = hi[e] = v[e];
     }
@@ -49,7 +49,7 @@ build_summaries_kernel(const uint8_t* __restrict__ keys, uint8_t* __restrict__ s
     for (int i0 = 0; i0 < B; i0 += CH) {
         uint4 raw[CH];
 #pragma unroll
-        for (int i = 0; i < CH; ++i) raw[i] = src[(long long)(i0 + i) * ROW_U4];
+        for (int i = 0; i < CH; ++i) raw[i] = load_stream(src + (long long)(i0 + i) * ROW_U4);
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             float v[VEC];
